@@ -1,0 +1,473 @@
+// zf_codec.hip - block codec kernels for gfx950: full-cache encode, per-step append, decode.
+//
+// Codec: ZipFusion video summary ("Run AI Faster With Lossless Compressed Memory", chapter
+// "Twelve Bits and One Addition").  Paged cache: essay "Open weights as an optimization
+// surface" (KV memory handed out in fixed-size pages).
+//
+// Work split.  A raw page u16[H][2][T][D] is one contiguous 64 KB run (H = 8, T = 16,
+// D = 128), so one workgroup owns one (sequence, logical page) and streams it with 16-byte
+// loads: 8 lanes cover one 64-value block, a 256-thread group covers 32 blocks per sweep.
+// Spill slots follow an exclusive scan of raw-block counts in (sequence, token) order, so
+// encode runs as pack -> scan -> spill: the pack pass writes sm/nib/base/row_flags and a
+// per-page raw count; one workgroup scans the page counts; the spill pass turns them into
+// row_spill and writes the 32-byte spill slots of the raw blocks.
+#include "zf_internal.h"
+
+namespace zf {
+
+struct SeqView {
+  int32_t B, maxp, max_seq_len;
+  const int32_t* pt;
+  int32_t* lens;
+};
+
+// Rows of logical page p of sequence b that hold tokens, or -1 when the length is invalid.
+__device__ __forceinline__ int rows_in_page(const SeqView& s, const Geom& g, int b, int p,
+                                            int32_t* len_out) {
+  int32_t L = s.lens[b];
+  *len_out = L;
+  if (L < 0 || (int64_t)L > (int64_t)s.maxp * g.T) return -1;
+  int64_t r = (int64_t)L - (int64_t)p * g.T;
+  return r <= 0 ? 0 : (r > g.T ? g.T : (int)r);
+}
+
+// ------------------------------------------------------------------------------ encode: pack
+
+__global__ __launch_bounds__(256) void enc_pack_k(Geom g, SeqView s, const uint16_t* __restrict__ raw,
+                                                  uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
+                                                  uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags,
+                                                  uint32_t* __restrict__ page_count, uint32_t* status) {
+  const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int32_t L;
+  const int rows = rows_in_page(s, g, b, p, &L);
+  if (rows < 0) {
+    if (p == 0 && tid == 0) set_status(status, ZF_DEV_ELEN);
+    return;
+  }
+  if (rows == 0) return;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
+  if (pid < 0 || pid >= g.P) {
+    if (tid == 0) {
+      set_status(status, ZF_DEV_EPAGE);
+      page_count[(int64_t)b * s.maxp + p] = 0u;
+    }
+    return;
+  }
+  __shared__ uint32_t s_flags[64];
+  if (tid < g.T) s_flags[tid] = 0u;
+  __syncthreads();
+
+  const int nb = g.nb();
+  const int blocks = 2 * g.H * g.T * nb;
+  const int64_t page_vals = g.vals_per_page();
+  const int lane8 = tid & 7;
+  for (int m = tid >> 3; m < blocks; m += blockDim.x >> 3) {
+    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+    if (slot >= rows) continue;  // uniform over the 8 lanes of the block
+    const int64_t v0 = (int64_t)pid * page_vals + (int64_t)m * kBlock + lane8 * 8;
+    uint4 in = *reinterpret_cast<const uint4*>(raw + v0);
+    uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    Window win = window8(w);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
+      win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
+      win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
+    }
+    const uint32_t raw_blk = win.special | (uint32_t)(win.emax - win.emin > 15u);
+    const uint32_t bexp = raw_blk ? 0u : win.emin;
+    uint32_t smw[2], nibw, hiw;
+    pack8(w, bexp, raw_blk, smw, nibw, hiw);
+    *reinterpret_cast<uint2*>(sm + v0) = make_uint2(smw[0], smw[1]);
+    *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = nibw;
+    if (lane8 == 0) {
+      base[v0 / kBlock] = (uint8_t)bexp;
+      if (raw_blk) atomicOr(&s_flags[slot], 1u << (hk * nb + half));
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    uint32_t f = tid < rows ? s_flags[tid] : 0u;
+    if (tid < rows) row_flags[(int64_t)pid * g.T + tid] = f;
+    uint32_t c = __popc(f);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) c += __shfl_xor((int)c, o, 64);
+    if (tid == 0) page_count[(int64_t)b * s.maxp + p] = c;
+  }
+}
+
+// ------------------------------------------------------------------------------ encode: scan
+
+// One workgroup.  Turns per-page raw counts into exclusive prefixes (offset by *spill_top) in
+// (sequence, page) order; flags the call as failed when the pool is too small.
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 8;
+
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  // Hillis-Steele over kScanThreads values in LDS (one value per thread).
+  const int tid = threadIdx.x;
+  s_tmp[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    uint32_t add = tid >= o ? s_tmp[tid - o] : 0u;
+    __syncthreads();
+    s_tmp[tid] += add;
+    __syncthreads();
+  }
+  uint32_t incl = s_tmp[tid];
+  *total = s_tmp[kScanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void enc_scan_k(Geom g, SeqView s,
+                                                           uint32_t* __restrict__ page_count,
+                                                           uint64_t* spill_top, uint64_t spill_slots,
+                                                           uint32_t* ws_flag, uint32_t* status) {
+  extern __shared__ uint32_t s_off[];  // [B + 1] page offsets, then kScanThreads scratch
+  uint32_t* s_tmp = s_off + s.B + 1;
+  __shared__ uint32_t s_total;
+  const int tid = threadIdx.x;
+  // pages per sequence -> exclusive offsets (chunked over the batch)
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < s.B; b0 += kScanThreads) {
+    int b = b0 + tid;
+    uint32_t np = 0;
+    if (b < s.B) {
+      int32_t L = s.lens[b];
+      if (L > 0 && (int64_t)L <= (int64_t)s.maxp * g.T) np = (uint32_t)((L + g.T - 1) / g.T);
+    }
+    uint32_t tot;
+    uint32_t ex = block_exclusive_scan(np, s_tmp, &tot);
+    if (b < s.B) s_off[b] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) s_off[s.B] = carry;
+  __syncthreads();
+  const uint32_t nchunks = s_off[s.B];
+  const uint64_t top = *spill_top;
+
+  // two passes: total, then prefixes (only if the pool holds them)
+  for (int pass = 0; pass < 2; ++pass) {
+    uint64_t run = 0;
+    for (uint32_t c0 = 0; c0 < nchunks; c0 += kScanThreads * kScanItems) {
+      uint32_t vals[kScanItems];
+      int64_t where[kScanItems];
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < kScanItems; ++i) {
+        uint32_t c = c0 + (uint32_t)tid * kScanItems + i;
+        vals[i] = 0;
+        where[i] = -1;
+        if (c < nchunks) {
+          int lo = 0, hi = s.B - 1;  // last b with s_off[b] <= c
+          while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= c) lo = mid; else hi = mid - 1;
+          }
+          where[i] = (int64_t)lo * s.maxp + (c - s_off[lo]);
+          vals[i] = page_count[where[i]];
+        }
+        mine += vals[i];
+      }
+      uint32_t tot;
+      uint32_t ex = block_exclusive_scan(mine, s_tmp, &tot);
+      if (pass == 1) {
+        uint64_t acc = top + run + ex;
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+          if (where[i] >= 0) page_count[where[i]] = (uint32_t)acc;
+          acc += vals[i];
+        }
+      }
+      run += tot;
+    }
+    if (pass == 0) {
+      if (tid == 0) s_total = (run > spill_slots - top) ? 1u : 0u;
+      __syncthreads();
+      if (s_total) {
+        if (tid == 0) {
+          *ws_flag = ZF_DEV_ESPILL;
+          set_status(status, ZF_DEV_ESPILL);
+        }
+        return;
+      }
+      if (tid == 0) {
+        *ws_flag = 0u;
+        *spill_top = top + run;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ encode: spill
+
+__global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint16_t* __restrict__ raw,
+                                                   const uint32_t* __restrict__ row_flags,
+                                                   uint32_t* __restrict__ row_spill, uint8_t* __restrict__ spill,
+                                                   const uint32_t* __restrict__ page_prefix,
+                                                   const uint32_t* ws_flag, uint64_t spill_slots) {
+  if (*ws_flag != 0u) return;
+  const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int32_t L;
+  const int rows = rows_in_page(s, g, b, p, &L);
+  if (rows <= 0) return;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
+  if (pid < 0 || pid >= g.P) return;
+  __shared__ uint32_t s_flags[64], s_first[64];
+  if (tid < 64) {
+    uint32_t f = tid < rows ? row_flags[(int64_t)pid * g.T + tid] : 0u;
+    uint32_t c = __popc(f), incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t up = __shfl_up((int)incl, o, 64);
+      if (tid >= o) incl += up;
+    }
+    uint32_t first = page_prefix[(int64_t)b * s.maxp + p] + (incl - c);
+    s_flags[tid] = f;
+    s_first[tid] = first;
+    if (tid < rows) row_spill[(int64_t)pid * g.T + tid] = first;
+  }
+  __syncthreads();
+  const int nb = g.nb();
+  const int blocks = 2 * g.H * g.T * nb;
+  const int lane8 = tid & 7;
+  for (int m = tid >> 3; m < blocks; m += blockDim.x >> 3) {
+    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+    if (slot >= rows) continue;
+    const int j = hk * nb + half;
+    const uint32_t f = s_flags[slot];
+    if (!((f >> j) & 1u)) continue;
+    const uint64_t idx = (uint64_t)s_first[slot] + __popc(f & ((1u << j) - 1u));
+    if (idx >= spill_slots) continue;  // only reachable when two sequences share a page
+    const int64_t v0 = (int64_t)pid * g.vals_per_page() + (int64_t)m * kBlock + lane8 * 8;
+    uint4 in = *reinterpret_cast<const uint4*>(raw + v0);
+    uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t hi = 0u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
+    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
+  }
+}
+
+// ------------------------------------------------------------------------------ append
+
+// One workgroup: classify the B new rows, scan their raw counts in batch order, then write.
+// All or nothing: any device-detected problem leaves the cache and seq_lens untouched.
+constexpr int kAppendThreads = 1024;
+constexpr int kAppendMaxBatch = 4096;  // two u32 per row in LDS
+
+__global__ __launch_bounds__(kAppendThreads) void append_k(Geom g, SeqView s,
+                                                           const uint16_t* __restrict__ k_new,
+                                                           const uint16_t* __restrict__ v_new, uint8_t* sm,
+                                                           uint8_t* nib, uint8_t* base, uint32_t* row_flags,
+                                                           uint32_t* row_spill, uint8_t* spill,
+                                                           uint64_t* spill_top, uint64_t spill_slots,
+                                                           uint32_t* status) {
+  extern __shared__ uint32_t s_flags[];  // [B] row flags, then [B] exclusive prefixes
+  uint32_t* s_pref = s_flags + s.B;
+  __shared__ uint32_t s_err, s_tmp[kAppendThreads];
+  const int tid = threadIdx.x;
+  if (tid == 0) s_err = 0u;
+  for (int b = tid; b < s.B; b += kAppendThreads) s_flags[b] = 0u;
+  __syncthreads();
+  // phase 0: validate every row position and page
+  for (int b = tid; b < s.B; b += kAppendThreads) {
+    int32_t L = s.lens[b];
+    uint32_t e = 0;
+    if (L < 0 || (int64_t)L + 1 > (int64_t)s.maxp * g.T || L + 1 > s.max_seq_len) {
+      e = ZF_DEV_ELEN;
+    } else {
+      int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
+      if (pid < 0 || pid >= g.P) e = ZF_DEV_EPAGE;
+    }
+    if (e) atomicOr(&s_err, e);
+  }
+  __syncthreads();
+  if (s_err) {
+    if (tid == 0) set_status(status, s_err);
+    return;
+  }
+  const int nb = g.nb(), D = g.D, H = g.H;
+  const int rb = 2 * H * nb;  // blocks per row
+  const int lane8 = tid & 7;
+  const int64_t nblk = (int64_t)s.B * rb;
+  // phase 1: raw flags of the new rows
+  for (int64_t m = tid >> 3; m < nblk; m += kAppendThreads >> 3) {
+    const int b = (int)(m / rb), j = (int)(m % rb);
+    const int half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
+    const uint16_t* src = (kv ? v_new : k_new) + ((int64_t)b * H + h) * D + half * kBlock + lane8 * 8;
+    uint4 in = *reinterpret_cast<const uint4*>(src);
+    uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    Window win = window8(w);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
+      win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
+      win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
+    }
+    if (lane8 == 0 && (win.special | (uint32_t)(win.emax - win.emin > 15u)))
+      atomicOr(&s_flags[b], 1u << j);
+  }
+  __syncthreads();
+  // phase 2: exclusive scan of raw counts in batch order
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < s.B; b0 += kAppendThreads) {
+    int b = b0 + tid;
+    uint32_t c = b < s.B ? __popc(s_flags[b]) : 0u;
+    s_tmp[tid] = c;
+    __syncthreads();
+    for (int o = 1; o < kAppendThreads; o <<= 1) {
+      uint32_t add = tid >= o ? s_tmp[tid - o] : 0u;
+      __syncthreads();
+      s_tmp[tid] += add;
+      __syncthreads();
+    }
+    if (b < s.B) s_pref[b] = carry + s_tmp[tid] - c;
+    carry += s_tmp[kAppendThreads - 1];
+    __syncthreads();
+  }
+  const uint64_t top = *spill_top;
+  if ((uint64_t)carry > spill_slots - top) {
+    if (tid == 0) set_status(status, ZF_DEV_ESPILL);
+    return;
+  }
+  // phase 3: write the rows
+  for (int64_t m = tid >> 3; m < nblk; m += kAppendThreads >> 3) {
+    const int b = (int)(m / rb), j = (int)(m % rb);
+    const int half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
+    const int32_t L = s.lens[b];
+    const int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
+    const int slot = L % g.T;
+    const uint16_t* src = (kv ? v_new : k_new) + ((int64_t)b * H + h) * D + half * kBlock + lane8 * 8;
+    uint4 in = *reinterpret_cast<const uint4*>(src);
+    uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    const uint32_t f = s_flags[b];
+    const uint32_t raw_blk = (f >> j) & 1u;
+    Window win = window8(w);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
+    const uint32_t bexp = raw_blk ? 0u : win.emin;
+    uint32_t smw[2], nibw, hiw;
+    pack8(w, bexp, raw_blk, smw, nibw, hiw);
+    const int64_t v0 = (((int64_t)pid * H + h) * 2 + kv) * g.T * D + (int64_t)slot * D + half * kBlock + lane8 * 8;
+    *reinterpret_cast<uint2*>(sm + v0) = make_uint2(smw[0], smw[1]);
+    *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = nibw;
+    if (lane8 == 0) base[v0 / kBlock] = (uint8_t)bexp;
+    if (raw_blk) {
+      const uint64_t idx = top + s_pref[b] + __popc(f & ((1u << j) - 1u));
+      *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hiw;
+    }
+  }
+  for (int b = tid; b < s.B; b += kAppendThreads) {
+    const int32_t L = s.lens[b];
+    const int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
+    row_flags[(int64_t)pid * g.T + L % g.T] = s_flags[b];
+    row_spill[(int64_t)pid * g.T + L % g.T] = (uint32_t)(top + s_pref[b]);
+  }
+  __syncthreads();  // every lane has read its length before any is advanced
+  for (int b = tid; b < s.B; b += kAppendThreads) s.lens[b] += 1;
+  if (tid == 0) *spill_top = top + carry;
+}
+
+// ------------------------------------------------------------------------------ decode
+
+__global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t* __restrict__ sm,
+                                                const uint8_t* __restrict__ nib, const uint8_t* __restrict__ base,
+                                                const uint32_t* __restrict__ row_flags,
+                                                const uint32_t* __restrict__ row_spill,
+                                                const uint8_t* __restrict__ spill, uint64_t spill_slots,
+                                                uint16_t* __restrict__ out, uint32_t* status) {
+  const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int32_t L;
+  const int rows = rows_in_page(s, g, b, p, &L);
+  if (rows < 0) {
+    if (p == 0 && tid == 0) set_status(status, ZF_DEV_ELEN);
+    return;
+  }
+  if (rows == 0) return;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
+  if (pid < 0 || pid >= g.P) {
+    if (tid == 0) set_status(status, ZF_DEV_EPAGE);
+    return;
+  }
+  const int nb = g.nb();
+  const int blocks = 2 * g.H * g.T * nb;
+  const int lane8 = tid & 7;
+  uint32_t err = 0;
+  for (int m = tid >> 3; m < blocks; m += blockDim.x >> 3) {
+    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+    if (slot >= rows) continue;
+    const int64_t v0 = (int64_t)pid * g.vals_per_page() + (int64_t)m * kBlock + lane8 * 8;
+    const uint2 smw = *reinterpret_cast<const uint2*>(sm + v0);
+    const uint32_t nibw = *reinterpret_cast<const uint32_t*>(nib + (v0 >> 1));
+    const uint32_t f = row_flags[(int64_t)pid * g.T + slot];
+    const int j = hk * nb + half;
+    uint32_t base_pair = 0u, hi = 0u;
+    if ((f >> j) & 1u) {
+      const uint64_t idx = (uint64_t)row_spill[(int64_t)pid * g.T + slot] + __popc(f & ((1u << j) - 1u));
+      if (idx < spill_slots) hi = *reinterpret_cast<const uint32_t*>(spill + idx * 32u + lane8 * 4);
+      else err = ZF_DEV_ESPILL;
+    } else {
+      base_pair = (uint32_t)base[v0 / kBlock] * 0x00800080u;
+    }
+    uint32_t pr[4], w[4];
+    rebuild8(smw.x, smw.y, nibw, hi, base_pair, pr);
+    pairs_to_natural(pr, w);
+    *reinterpret_cast<uint4*>(out + v0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (err) set_status(status, err);
+}
+
+// ------------------------------------------------------------------------------ host launchers
+
+static SeqView view(const zf_seqs* q) {
+  return SeqView{q->batch, q->max_pages_per_seq, q->max_seq_len, q->page_table, q->seq_lens};
+}
+
+hipError_t launch_encode(const Geom& g, const zf_cache* c, const zf_seqs* q, const uint16_t* raw,
+                         uint32_t* ws, hipStream_t st) {
+  SeqView s = view(q);
+  uint32_t* ws_flag = ws;
+  uint32_t* page_count = ws + 64;  // 256-byte header
+  dim3 grid(q->max_pages_per_seq, q->batch);
+  hipLaunchKernelGGL(enc_pack_k, grid, dim3(256), 0, st, g, s, raw, c->sm, c->nib, c->base,
+                     c->row_flags, page_count, c->status);
+  size_t lds = ((size_t)q->batch + 1 + kScanThreads) * sizeof(uint32_t);
+  hipLaunchKernelGGL(enc_scan_k, dim3(1), dim3(kScanThreads), lds, st, g, s, page_count,
+                     c->spill_top, c->spill_slots, ws_flag, c->status);
+  hipLaunchKernelGGL(enc_spill_k, grid, dim3(256), 0, st, g, s, raw, c->row_flags, c->row_spill,
+                     c->spill, page_count, ws_flag, c->spill_slots);
+  return hipGetLastError();
+}
+
+size_t encode_workspace_bytes(const zf_seqs* q) {
+  return 256 + (size_t)q->batch * (size_t)q->max_pages_per_seq * sizeof(uint32_t);
+}
+
+size_t encode_lds_bytes(int32_t batch) {
+  return ((size_t)batch + 1 + kScanThreads) * sizeof(uint32_t);
+}
+
+int append_max_batch() { return kAppendMaxBatch; }
+
+hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, const uint16_t* k_new,
+                         const uint16_t* v_new, hipStream_t st) {
+  SeqView s = view(q);
+  size_t lds = 2 * (size_t)q->batch * sizeof(uint32_t);
+  hipLaunchKernelGGL(append_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, k_new, v_new, c->sm,
+                     c->nib, c->base, c->row_flags, c->row_spill, c->spill, c->spill_top,
+                     c->spill_slots, c->status);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const Geom& g, const zf_cache* c, const zf_seqs* q, uint16_t* out,
+                         hipStream_t st) {
+  SeqView s = view(q);
+  dim3 grid(q->max_pages_per_seq, q->batch);
+  hipLaunchKernelGGL(decode_k, grid, dim3(256), 0, st, g, s, c->sm, c->nib, c->base, c->row_flags,
+                     c->row_spill, c->spill, c->spill_slots, out, c->status);
+  return hipGetLastError();
+}
+
+}  // namespace zf

@@ -1,0 +1,155 @@
+/*
+ * zf.h - lossless compressed-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method (ZipFusion video summary, "Run AI Faster With Lossless Compressed Memory"):
+ * the KV cache stays compressed in GPU memory; a block of BF16 values keeps one shared base
+ * exponent and a 4-bit exponent offset per value next to each value's sign and mantissa
+ * (12 bits per value, 75 % of BF16, chapter "Twelve Bits and One Addition"); blocks whose
+ * exponents are too spread out stay raw; attention rebuilds every value in registers with a
+ * single integer addition instead of unpacking the cache to a buffer inside the decode loop.
+ * The cache is paged (essay "Open weights as an optimization surface": KV memory allocated in
+ * fixed-size blocks, decode phase reading the cache every step).
+ *
+ * ---------------------------------------------------------------------------------- format
+ * Geometry: num_pages pages of page_size tokens; num_kv_heads heads; head_dim a multiple of
+ * 64 with 2 * num_kv_heads * head_dim / 64 <= 32.  A block is 64 consecutive head_dim values
+ * of one (token, kv head, K or V).  A token row is all blocks of one token; block j of a row
+ * is j = (h * 2 + kv) * (head_dim / 64) + half  (kv = 0 for K, 1 for V).
+ * For every value x (bf16 bits s|eeeeeeee|mmmmmmm):
+ *   sm  byte  = s << 7 | m
+ *   nibble    = e - base            (compressed block; base = smallest exponent of the block)
+ *             = e & 15              (raw block)
+ * A block is raw iff one of its exponents is 0 (zero, subnormal) or 255 (Inf, NaN), or its
+ * exponents span more than 16 values.  A raw block has base 0, its bit set in the row's flag
+ * word, and 32 spill bytes holding e >> 4 of each value (packed like the nibbles).
+ * Rebuild: x = (s << 15 | nibble << 7 | m) + (base << 7)   or   + ((e >> 4) << 11) when raw.
+ * Spill slots: a row's raw blocks occupy consecutive slots in block order starting at
+ * row_spill[row]; zf_encode_kv takes slots for rows in (sequence, token) order, zf_append_kv
+ * in batch order, both starting at *spill_top, which they advance.  Slots are never freed.
+ *
+ * Arrays (device memory, 256-byte aligned, caller-owned; the library allocates nothing):
+ *   sm        u8 [num_pages][H][2][page_size][D]
+ *   nib       u8 [num_pages][H][2][page_size][D/2]   two values per byte, low nibble first
+ *   base      u8 [num_pages][H][2][page_size][D/64]  0 = raw
+ *   row_flags u32[num_pages][page_size]              bit j = block j raw
+ *   row_spill u32[num_pages][page_size]              slot of the row's first raw block
+ *   spill     u8 [spill_slots][32]
+ *   spill_top u64 (one counter)   status u32 (sticky device error bits, ZF_DEV_*)
+ * Raw (uncompressed) pages use u16[num_pages][H][2][page_size][D], the same page ids.
+ *
+ * ---------------------------------------------------------------------------------- errors
+ * Calls validate their host-side arguments and return ZF_EINVAL / ZF_EUNSUPPORTED without
+ * enqueuing anything.  Otherwise they enqueue on `stream` and return at once (ZF_OK), or
+ * ZF_EHIP if the launch failed.  Problems found on the device (a page id outside
+ * [0, num_pages), a length beyond the page table or the host bound, an exhausted spill pool)
+ * set ZF_DEV_* bits in *status, which stay set until the caller clears them; rows with a bad
+ * page id are skipped.  zf_get_status reads the word (it synchronizes the stream).
+ * Only rows t < seq_lens[b] are defined; other slots are never read as data.
+ */
+#ifndef ZF_H
+#define ZF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* zf_stream_t; /* a hipStream_t; NULL = the default stream */
+
+typedef enum {
+  ZF_OK = 0,
+  ZF_EINVAL = 1,        /* bad argument (null or misaligned pointer, bad sizes)        */
+  ZF_EUNSUPPORTED = 2,  /* valid but outside what the kernels implement                */
+  ZF_EHIP = 3,          /* a HIP runtime call failed                                   */
+  ZF_EWORKSPACE = 4     /* workspace missing or smaller than the matching _bytes query */
+} zf_status;
+
+#define ZF_DEV_ESPILL 1u  /* spill pool exhausted: the call wrote no spill, kept spill_top */
+#define ZF_DEV_EPAGE 2u   /* a page-table entry the call needed is out of range           */
+#define ZF_DEV_ELEN 4u    /* a length is negative or beyond the page table / host bound   */
+
+typedef struct {
+  int32_t num_pages, page_size, num_kv_heads, head_dim;
+  uint8_t* sm;
+  uint8_t* nib;
+  uint8_t* base;
+  uint32_t* row_flags;
+  uint32_t* row_spill;
+  uint8_t* spill;
+  uint64_t spill_slots;
+  uint64_t* spill_top;
+  uint32_t* status;
+} zf_cache;
+
+typedef struct {
+  int32_t batch, max_pages_per_seq;
+  const int32_t* page_table; /* device [batch][max_pages_per_seq], physical page ids        */
+  int32_t* seq_lens;         /* device [batch], tokens present                               */
+  int32_t max_seq_len;       /* HOST bound on every seq_lens[b] when the call runs (after an
+                                append: on the grown lengths); sizes grids and workspaces   */
+} zf_seqs;
+
+/* Bytes of one cache's arrays except spill, for sizing a pool. */
+size_t zf_cache_bytes(int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                      int32_t head_dim);
+
+/* Initial compression of a prefilled cache (video summary: "initial compression", which the
+ * pages leave out of their timings).  Encodes rows t < seq_lens[b] of every sequence from raw
+ * pages into the packed planes, takes spill slots from *spill_top in (sequence, token) order
+ * and advances it.  If the pool cannot hold them all: ZF_DEV_ESPILL, no spill written,
+ * spill_top unchanged, the planes of the rows unspecified.  Workspace: device memory of
+ * zf_encode_workspace_bytes(seqs) bytes, any contents. */
+zf_status zf_encode_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* raw_pages,
+                       void* workspace, size_t workspace_bytes, zf_stream_t stream);
+size_t zf_encode_workspace_bytes(const zf_seqs* seqs);
+
+/* Decode-step append: encodes one new token per sequence (k_new, v_new u16[batch][H][D])
+ * into row seq_lens[b] of its page, spill slots from *spill_top in batch order, then
+ * seq_lens[b] += 1 for every b.  All or nothing: on a device error (ZF_DEV_*) nothing is
+ * written and seq_lens are unchanged.  seqs->max_seq_len bounds the lengths after the append.
+ * Supports batch <= 4096. */
+zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
+                       const uint16_t* v_new, zf_stream_t stream);
+
+/* Inverse of the codec: writes rows t < seq_lens[b] as raw bf16 pages (lossless: the bits
+ * that were encoded). */
+zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw_pages_out,
+                       zf_stream_t stream);
+
+/* Fused decode attention over the packed cache (video summary: values rebuilt in registers
+ * by one integer add; no decompressed copy).  q: bf16 u16[batch][num_q_heads][D]; out: f32
+ * [batch][num_q_heads][D]; q head i uses kv head i / (num_q_heads / H).  out =
+ * softmax(scale * q K^T) V over the sequence's tokens in logical order; zeros when
+ * seq_lens[b] == 0.  Workspace: zf_attention_workspace_bytes(...) bytes that must be zero
+ * before the first call (zf_attention_workspace_init); every call leaves it reusable.  Calls
+ * sharing one workspace must not overlap.  Requires D == 128, page_size == 16 and
+ * num_q_heads == 4 * H in this version (ZF_EUNSUPPORTED otherwise). */
+zf_status zf_decode_attention(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* q,
+                              int32_t num_q_heads, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, zf_stream_t stream);
+
+/* The same attention kernel reading an uncompressed bf16 cache; same split plan and
+ * arithmetic, so its output is bitwise identical to zf_decode_attention on the encoded copy
+ * of the same pages.  status: device u32 for ZF_DEV_* bits (may not be NULL). */
+zf_status zf_decode_attention_raw(const uint16_t* raw_pages, int32_t num_pages,
+                                  int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                                  const zf_seqs* seqs, const uint16_t* q, int32_t num_q_heads,
+                                  float scale, float* out, void* workspace,
+                                  size_t workspace_bytes, uint32_t* status, zf_stream_t stream);
+
+size_t zf_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
+                                    int32_t head_dim, int32_t max_seq_len);
+/* Zero-fills a workspace on `stream` (a kernel, no memset node). */
+zf_status zf_attention_workspace_init(void* workspace, size_t workspace_bytes,
+                                      zf_stream_t stream);
+
+/* Copies the sticky status word to *host_status (synchronizes `stream`). */
+zf_status zf_get_status(const uint32_t* status, uint32_t* host_status, zf_stream_t stream);
+const char* zf_status_str(zf_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,117 @@
+"""The C ABI without a GPU: libzf.so loads, exports every function include/zf.h declares, and
+its host-side checks (sizes, argument validation, status strings) behave as documented.
+No call here enqueues GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_encode_amd as zf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zf.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zf_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for op in ("zf_encode_kv", "zf_append_kv", "zf_decode_kv", "zf_decode_attention"):
+        assert op in names
+
+
+def test_every_declared_function_is_exported():
+    lib = zf.load()
+    names = declared_functions()
+    assert set(names) == set(zf.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_cache_bytes_closed_form():
+    P, T, H, D = 10, 16, 8, 128
+    vals = P * H * 2 * T * D
+    assert zf.zf_cache_bytes(P, T, H, D) == vals + vals // 2 + vals // 64 + 2 * 4 * P * T
+    assert zf.zf_cache_bytes(P, T, H, 96) == 0          # not a whole number of blocks
+    assert zf.zf_cache_bytes(P, T, 16, 128) == 0        # 64 blocks per row: too many
+
+
+def test_attention_workspace_sizes():
+    assert zf.zf_attention_workspace_bytes(32, 8, 32, 128, 4097) > 0
+    assert zf.zf_attention_workspace_bytes(32, 8, 24, 128, 4097) == 0   # group of 3
+    assert zf.zf_attention_workspace_bytes(32, 8, 32, 64, 4097) == 0    # head_dim 64
+    a = zf.zf_attention_workspace_bytes(32, 8, 32, 128, 4097)
+    b = zf.zf_attention_workspace_bytes(32, 8, 32, 128, 8192)
+    assert b >= a
+
+
+def test_encode_workspace_size():
+    s = zf.zf_seqs(4, 10, None, None, 160)
+    assert zf.load().zf_encode_workspace_bytes(ctypes.byref(s)) == 256 + 4 * 10 * 4
+
+
+def _cache(**kw):
+    fields = dict(num_pages=4, page_size=16, num_kv_heads=8, head_dim=128, sm=256, nib=512,
+                  base=768, row_flags=1024, row_spill=1280, spill=1536, spill_slots=10,
+                  spill_top=1792, status=2048)
+    fields.update(kw)
+    return zf.zf_cache(**fields)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sm=None), zf.ZF_EINVAL),
+    (dict(nib=513), zf.ZF_EINVAL),             # misaligned
+    (dict(head_dim=100), zf.ZF_EUNSUPPORTED),
+    (dict(num_kv_heads=16), zf.ZF_EUNSUPPORTED),
+    (dict(status=None), zf.ZF_EINVAL),
+    (dict(spill_slots=1 << 32), zf.ZF_EUNSUPPORTED),
+])
+def test_bad_cache_is_rejected_before_any_launch(kw, code):
+    lib = zf.load()
+    c = _cache(**kw)
+    s = zf.zf_seqs(1, 1, 4096, 4096, 16)
+    assert lib.zf_decode_kv(ctypes.byref(c), ctypes.byref(s), 2304, None) == code
+    assert lib.zf_append_kv(ctypes.byref(c), ctypes.byref(s), 4096, 4096, None) == code
+
+
+@pytest.mark.parametrize("seqs,code", [
+    (dict(batch=-1), zf.ZF_EINVAL),
+    (dict(max_seq_len=17), zf.ZF_EINVAL),       # beyond max_pages_per_seq * page_size
+    (dict(page_table=None), zf.ZF_EINVAL),
+    (dict(seq_lens=4098), zf.ZF_EINVAL),        # not 4-byte aligned
+])
+def test_bad_seqs_are_rejected(seqs, code):
+    lib = zf.load()
+    f = dict(batch=1, max_pages_per_seq=1, page_table=4096, seq_lens=4096, max_seq_len=16)
+    f.update(seqs)
+    s = zf.zf_seqs(**f)
+    c = _cache()
+    assert lib.zf_decode_kv(ctypes.byref(c), ctypes.byref(s), 2304, None) == code
+
+
+def test_attention_shape_and_workspace_checks():
+    lib = zf.load()
+    c = _cache()
+    s = zf.zf_seqs(1, 1, 4096, 4096, 16)
+    # group of 3 query heads per kv head: unsupported
+    assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s), 4096, 24, 0.1, 8192, 12288,
+                                   1 << 20, None) == zf.ZF_EUNSUPPORTED
+    # too small a workspace
+    assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s), 4096, 32, 0.1, 8192, 12288,
+                                   16, None) == zf.ZF_EWORKSPACE
+    # empty batch: nothing to do
+    s0 = zf.zf_seqs(0, 0, None, None, 0)
+    assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s0), 4096, 32, 0.1, 8192, 12288,
+                                   0, None) == zf.ZF_OK
+
+
+def test_status_strings():
+    lib = zf.load()
+    for code in range(5):
+        assert lib.zf_status_str(code)
+    assert lib.zf_status_str(zf.ZF_EWORKSPACE) == b"workspace missing or too small"

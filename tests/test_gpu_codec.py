@@ -1,0 +1,142 @@
+"""GPU parity for the codec: zf_encode_kv, zf_append_kv and zf_decode_kv through the C ABI,
+bit-exact against the CPU oracle on every workload (packed planes, base, row flags, row spill
+slots, spill bytes, spill_top), plus the device-side error rules.
+
+Codec: ZipFusion video summary ("Run AI Faster With Lossless Compressed Memory", chapter
+"Twelve Bits and One Addition"); lossless, so decode must return the encoded bits exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_encode_amd as zf
+import oracle
+import synth
+from gpu_util import Setup, compare_packed, dev, host, log, oracle_cache, valid_rows
+
+pytestmark = pytest.mark.gpu
+
+SMALL = synth.WORKLOADS[0].replace(name="ragged_small", batch=5, ctx_min=1, ctx_max=300,
+                                   extra_tokens=3, pool_factor=1.3, p_wide_block=0.05, seed=21)
+
+
+def workload(key):
+    return SMALL if key == "small" else synth.WORKLOADS[key]
+
+
+@pytest.mark.parametrize("key", [0, "small", 1, 2, 3, 4])
+def test_encode_bitexact(key):
+    w = workload(key)
+    log(f"encode parity: workload {w.name}")
+    inst = synth.make(w)
+    s = Setup(inst)
+    assert s.status() == 0
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    compare_packed(s.cache, orc, valid_rows(inst), w.name)
+    log(f"  raw blocks {orc.spill_top} of {int(inst.seq_lens.sum()) * 32}")
+
+
+@pytest.mark.parametrize("key", [0, "small", 1, 4])
+def test_decode_roundtrip(key):
+    w = workload(key)
+    log(f"decode round trip: workload {w.name}")
+    inst = synth.make(w)
+    s = Setup(inst)
+    out = torch.zeros_like(s.raw)
+    zf.zf_decode_kv(s.cache, s.seqs, out)
+    torch.cuda.synchronize()
+    assert s.status() == 0
+    got = host(out, np.uint16)
+    rows = valid_rows(inst)
+    m = np.broadcast_to(rows[:, None, None, :, None], got.shape)
+    assert np.array_equal(got[m], inst.raw_pages[m])
+    untouched = ~m
+    assert not got[untouched].any(), "decode wrote outside the defined rows"
+
+
+def _append_steps(w, steps, check_every=1):
+    inst = synth.make(w)
+    s = Setup(inst)
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    lens = inst.seq_lens.copy()
+    for step in range(steps):
+        k, v = synth.tokens(w, lens)
+        zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
+        assert orc.append(lens, inst.page_table, k, v) == oracle.OK
+        if (step + 1) % check_every == 0 or step == steps - 1:
+            torch.cuda.synchronize()
+            assert s.status() == 0
+            assert np.array_equal(host(s.seqs.seq_lens), lens)
+            compare_packed(s.cache, orc, valid_rows(inst, lens), f"{w.name} step {step}")
+    return s, inst, lens
+
+
+@pytest.mark.parametrize("key,steps", [("small", 3), (1, 1), (3, 1), (4, 64)])
+def test_append_bitexact(key, steps):
+    w = workload(key)
+    if w.extra_tokens < steps:
+        w = w.replace(extra_tokens=steps)
+    log(f"append parity: workload {w.name}, {steps} steps")
+    _append_steps(w, steps, check_every=16)
+
+
+def test_append_spill_exhaustion_writes_nothing():
+    w = SMALL
+    inst = synth.make(w)
+    orc = oracle_cache(inst, 1 << 20)
+    need = orc.spill_top
+    s = Setup(inst, spill_slots=need)  # exactly full after the encode
+    assert s.status() == 0 and int(host(s.cache.spill_top)[0]) == need
+    before = {n: host(getattr(s.cache, n)).copy() for n in ("sm", "nib", "base", "row_flags", "row_spill", "spill")}
+    k, v = synth.tokens(w, inst.seq_lens)
+    k[:, :, 0] = 0  # every new row gets a raw block
+    zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert s.status() & zf.ZF_DEV_ESPILL
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == need
+    for n, a in before.items():
+        assert np.array_equal(host(getattr(s.cache, n)), a), n
+
+
+def test_encode_spill_exhaustion_keeps_pool():
+    inst = synth.make(SMALL)
+    orc = oracle_cache(inst, 1 << 20)
+    s = Setup(inst, spill_slots=orc.spill_top - 1)
+    assert s.status() & zf.ZF_DEV_ESPILL
+    assert int(host(s.cache.spill_top)[0]) == 0
+    assert not host(s.cache.spill).any()
+    # exactly enough slots: succeeds and fills the pool
+    s2 = Setup(inst, spill_slots=orc.spill_top)
+    assert s2.status() == 0
+    compare_packed(s2.cache, orc, valid_rows(inst), "exact pool")
+
+
+def test_bad_page_and_length_set_status():
+    inst = synth.make(SMALL)
+    pt = inst.page_table.copy()
+    pt[2, 0] = inst.num_pages + 7
+    bad = synth.Instance(inst.w, inst.seq_lens, pt, inst.num_pages, inst.raw_pages)
+    s = Setup(bad)
+    assert s.status() & zf.ZF_DEV_EPAGE
+    lens = inst.seq_lens.copy()
+    lens[1] = inst.page_table.shape[1] * 16 + 5
+    s = Setup(synth.Instance(inst.w, lens, inst.page_table, inst.num_pages, inst.raw_pages),
+              max_seq_len=inst.page_table.shape[1] * 16)
+    assert s.status() & zf.ZF_DEV_ELEN
+
+
+def test_encode_is_repeatable():
+    """Same input, same spill_top start: identical packed bytes (no order dependence)."""
+    inst = synth.make(synth.WORKLOADS[1].replace(batch=6))
+    a, b = Setup(inst), Setup(inst)
+    rows = valid_rows(inst)
+    for n in ("sm", "nib", "base", "row_flags", "row_spill", "spill", "spill_top"):
+        x, y = host(getattr(a.cache, n)), host(getattr(b.cache, n))
+        if x.ndim == 5:
+            m = np.broadcast_to(rows[:, None, None, :, None], x.shape)
+            assert np.array_equal(x[m], y[m]), n
+        elif x.ndim == 2 and n.startswith("row_"):
+            assert np.array_equal(x[rows], y[rows]), n
+        else:
+            assert np.array_equal(x, y), n
