@@ -1,0 +1,314 @@
+"""Decode-step benchmark for the compressed-KV path on one MI355X.
+
+One step = what a decode step does to one attention layer's cache: zf_append_kv (encode one
+new K/V token per sequence into the packed paged cache) followed by zf_decode_attention (fused
+GQA attention over the packed cache, every value rebuilt in registers).  Workload: the
+Llama-3.1-8B-shaped decode of the ZipFusion video summary ("Run AI Faster With Lossless
+Compressed Memory"): batch 32, 32 query / 8 KV heads, head_dim 128, 4096 cached tokens per
+sequence, 16-token pages in random order, synthetic bf16 K/V (seeded generator; no model
+weights exist here).  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  `value` = tokens/s of the whole job (sequences x steps / time), one
+layer.  `roofline` prices the attention kernel (the dominant one) against HBM: algorithmic
+bytes per launch (packed planes of the attended rows, spill slots of their raw blocks, q, out,
+page table and lengths) / its mean duration from HIP events on the launch stream.
+`cpu_baseline` times the CPU oracle (plain C, one thread) on a bounded sample of the same
+steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "compressed-KV decode attn: HBM GB/s, % of peak, tokens/s, compression ratio"
+WORKLOAD = 1
+ATTN_SOURCES = ["decode_attention_encode_amd/csrc/zf_attention.hip",
+                "decode_attention_encode_amd/csrc/zf_internal.h"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_llama8b_b32_ctx4096_hbm_counters.json")
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the raw twin, a cache-flushed attention, encode and decode")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and is not "
+              "sharded across GPUs (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_encode_amd as zf
+    import synth
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "launches": 3}))
+        return
+
+    W, K = args.warmup, args.steps
+    w = synth.WORKLOADS[WORKLOAD].replace(extra_tokens=W + K)
+    t0 = time.time()
+    inst = synth.make(w)
+    B, H, Hq, D, T = w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.page_size
+    lens0 = inst.seq_lens.copy()
+    # tokens and queries of every step, generated up front and made resident
+    ks, vs, qs = [], [], []
+    for s in range(W + K):
+        k, v = synth.tokens(w, lens0 + s)
+        ks.append(k)
+        vs.append(v)
+        qs.append(synth.query(w, s))
+    to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    k_dev = to(np.stack(ks))
+    v_dev = to(np.stack(vs))
+    q_dev = to(np.stack(qs))
+    gen_s = time.time() - t0
+
+    rows_cap = int(lens0.sum()) + B * (W + K)
+    spill_slots = rows_cap * 2 * H * (D // 64)
+    cache = zf.PackedCache.empty(inst.num_pages, T, H, D, spill_slots, device=dev)
+    max_len = int(lens0.max()) + W + K
+    seqs = zf.Seqs(to(inst.page_table), to(lens0.copy()), max_len)
+    raw = to(inst.raw_pages)
+    enc_ws = zf.encode_workspace(seqs)
+    zf.zf_encode_kv(cache, seqs, raw, enc_ws)
+    torch.cuda.synchronize()
+    assert zf.zf_get_status(cache.status) == 0
+    top0 = int(cache.spill_top.item())
+    rows0 = int(lens0.sum())
+    ws = zf.attention_workspace(B, H, Hq, D, max_len, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        zf.zf_append_kv(cache, seqs, k_dev[s], v_dev[s])
+        if ev is not None:
+            ev[0].record(stream)
+        zf.zf_decode_attention(cache, seqs, q_dev[s], scale, out, ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(W + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    status = zf.zf_get_status(cache.status)
+    assert status == 0, f"device status {status}"
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    # ---- algorithmic bytes of each timed attention launch
+    flags = cache.row_flags.cpu().numpy().view(np.uint32)
+    pt = inst.page_table
+    row_bytes = 2 * H * (D + D // 2 + D // 64) + 8  # planes + base + row flags + row spill
+    appended_raw = np.zeros(W + K, np.int64)
+    for s in range(W + K):
+        pos = lens0 + s
+        pages = pt[np.arange(B), pos // T]
+        f = flags[pages, pos % T]
+        appended_raw[s] = sum(bin(int(x)).count("1") for x in f)
+    cum_raw = top0 + np.cumsum(appended_raw)  # raw blocks present after step s's append
+    attn_bytes = []
+    for i in range(K):
+        s = W + i
+        L = lens0 + s + 1
+        nbytes = int(L.sum()) * row_bytes + 32 * int(cum_raw[s])
+        nbytes += B * Hq * D * (2 + 4) + int(np.ceil(L / T).sum()) * 4 + B * 4
+        attn_bytes.append(nbytes)
+    attn_bytes = np.array(attn_bytes, np.float64)
+    mean_attn_s = attn_ms.mean() / 1e3
+    achieved = attn_bytes.mean() / mean_attn_s / 1e9
+    tokens_attended = (lens0 + W + 1).sum() + B * (K - 1) / 2
+    uncompressed_eq = float(tokens_attended * H * 2 * D * 2) / mean_attn_s / 1e9
+    packed_valid = rows0 * row_bytes + 32 * top0
+    ratio = packed_valid / (rows0 * H * 2 * D * 2)
+
+    traffic = None
+    if os.path.exists(PMC_SUMMARY):
+        pmc = json.load(open(PMC_SUMMARY))
+        if pmc.get("attn_source_hash") == attn_source_hash():
+            traffic = pmc.get("hbm_bytes_per_launch")
+
+    extra = {
+        "attention_kernel_us_mean": round(attn_ms.mean() * 1e3, 2),
+        "attention_kernel_us_min": round(attn_ms.min() * 1e3, 2),
+        "attention_bytes_per_launch": int(attn_bytes.mean()),
+        "uncompressed_equivalent_GBps": round(uncompressed_eq, 1),
+        "compression_ratio": round(ratio, 4),
+        "raw_block_fraction": round(top0 / (rows0 * 2 * H * (D // 64)), 4),
+        "generation_s": round(gen_s, 1),
+    }
+
+    if args.extras:
+        extra.update(extras(torch, zf, inst, cache, seqs, raw, q_dev[W + K - 1], ws, out,
+                            scale, attn_bytes.mean(), row_bytes))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inst, lens0, ks, vs, qs, args.cpu_seconds, row_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": round(B * K / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 K/V: per-channel log-uniform scales, outlier and zero "
+                "blocks; no model weights)",
+        "config": {"workload": w.name, "batch": B, "context": int(lens0[0]), "q_heads": Hq,
+                   "kv_heads": H, "head_dim": D, "page_size": T, "layers": 1,
+                   "step": "append 1 token/seq + fused compressed attention"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(result))
+
+
+def extras(torch, zf, inst, cache, seqs, raw, q, ws, out, scale, attn_bytes, row_bytes):
+    """Twin (uncompressed) attention, flushed-cache attention, full encode / decode rates."""
+    res = {}
+    stream = torch.cuda.current_stream()
+
+    def timeit(fn, n=20, flush=None):
+        ts = []
+        for _ in range(n):
+            if flush is not None:
+                flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.mean(ts)) / 1e3
+
+    status = torch.zeros(1, dtype=torch.int32, device=raw.device)
+    # the twin reads raw pages holding the same tokens the packed cache holds
+    dec = torch.zeros_like(raw)
+    zf.zf_decode_kv(cache, seqs, dec)
+    t_twin = timeit(lambda: zf.zf_decode_attention_raw(dec, seqs, q, scale, out, ws, status))
+    t_pack = timeit(lambda: zf.zf_decode_attention(cache, seqs, q, scale, out, ws))
+    res["attention_packed_us"] = round(t_pack * 1e6, 2)
+    res["attention_twin_uncompressed_us"] = round(t_twin * 1e6, 2)
+    res["speedup_vs_uncompressed_twin"] = round(t_twin / t_pack, 3)
+    scratch = torch.empty(1 << 29, dtype=torch.uint8, device=raw.device)
+    flush = lambda: scratch.fill_(0)
+    t_flush = timeit(lambda: zf.zf_decode_attention(cache, seqs, q, scale, out, ws), n=10, flush=flush)
+    res["attention_after_512MiB_flush_us"] = round(t_flush * 1e6, 2)
+    res["attention_after_flush_GBps"] = round(attn_bytes / t_flush / 1e9, 1)
+    # full-cache encode and decode of the whole pool (the lengths as they are now)
+    lens = seqs.seq_lens.cpu().numpy()
+    rows = int(lens.sum())
+    raw_bytes = rows * 2 * inst.w.num_kv_heads * inst.w.head_dim * 2
+    top = int(cache.spill_top.item())
+    packed_bytes = rows * row_bytes + 32 * top
+    c2 = zf.PackedCache.empty(cache.num_pages, cache.page_size, cache.num_kv_heads,
+                              cache.head_dim, cache.spill_slots, device=raw.device)
+    enc_ws = zf.encode_workspace(seqs)
+
+    def enc():
+        c2.spill_top.zero_()
+        zf.zf_encode_kv(c2, seqs, dec, enc_ws)
+    t_enc = timeit(enc, n=10)
+    t_dec = timeit(lambda: zf.zf_decode_kv(cache, seqs, dec), n=10)
+    res["encode_GBps_read_plus_written"] = round((raw_bytes + packed_bytes) / t_enc / 1e9, 1)
+    res["decode_GBps_read_plus_written"] = round((raw_bytes + packed_bytes) / t_dec / 1e9, 1)
+    res["encode_us"] = round(t_enc * 1e6, 1)
+    res["decode_us"] = round(t_dec * 1e6, 1)
+    return res
+
+
+def cpu_baseline(w, inst, lens0, ks, vs, qs, budget_s, row_bytes):
+    """The oracle as it stands (plain C, one thread): whole decode steps of the same workload
+    (append one token per sequence + fp64 attention for every head), repeated until the
+    budget is spent; steps/s -> tokens/s."""
+    import oracle
+
+    T = w.page_size
+    c = oracle.Cache(inst.num_pages, T, w.num_kv_heads, w.head_dim,
+                     spill_slots=(int(lens0.sum()) + w.batch * len(ks)) * 32)
+    assert c.encode(lens0, inst.page_table, inst.raw_pages) == 0
+    raw = inst.raw_pages.copy()
+    lens = lens0.copy()
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(ks):
+        k, v = ks[done], vs[done]
+        pos = lens.copy()
+        assert c.append(lens, inst.page_table, k, v) == 0
+        for b in range(w.batch):
+            page = inst.page_table[b, pos[b] // T]
+            raw[page, :, 0, pos[b] % T] = k[b]
+            raw[page, :, 1, pos[b] % T] = v[b]
+        st, _ = oracle.attention(raw, lens, inst.page_table, qs[done])
+        assert st == 0
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(w.batch * done / el, 3), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} full decode steps (batch {w.batch}, append + fp64 attention over "
+                      f"{int(lens0[0]) + 1}+ tokens, all 32 heads), {el:.1f} s on one core"}
+
+
+if __name__ == "__main__":
+    main()
