@@ -292,23 +292,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_k(AttnArgs a, Loader ld) {
     return min(kT, L - (p_first + kWaves * n) * kT);
   };
 
-  typename Loader::Meta m_next{}, m_after{};
-  typename Loader::Bufs cur{};
-  if (nmine > 0) {
-    const typename Loader::Meta m0 = ld.issue_meta(pid_at(0), lane);
-    if (nmine > 1) m_next = ld.issue_meta(pid_at(1), lane);
-    cur = ld.issue_bufs(a.H, pid_at(0), h, lane, m0);
-  }
-
-  for (int n = 0; n < nmine; ++n) {
-    typename Loader::Bufs nxt{};
-    if (n + 1 < nmine) nxt = ld.issue_bufs(a.H, pid_at(n + 1), h, lane, m_next);
-    if (n + 2 < nmine) m_after = ld.issue_meta(pid_at(n + 2), lane);
-
+  // One buffer slot per wave: page n is rebuilt into bf16 pairs first, which frees the slot
+  // for page n + 1's planes and spill loads; those stay in flight while page n's MFMA,
+  // softmax and p.V run.  Row metadata travels two pages ahead.  The last page is peeled so
+  // that the loop's loads are unconditional (no buffer copies between iterations).
+  auto compute = [&](const int n, const uint32_t (&kp)[16], const uint32_t (&vp)[16]) {
     const int ntok = ntok_at(n);
     const bool valid = t < ntok;
-    uint32_t kp[16], vp[16];
-    ld.rebuild(cur, kp, vp);
 
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -382,8 +372,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_k(AttnArgs a, Loader ld) {
         }
       }
     }
-    cur = nxt;
-    m_next = m_after;
+  };
+
+  typename Loader::Meta meta_n1{};
+  typename Loader::Bufs buf{};
+  if (nmine > 0) {
+    const typename Loader::Meta meta0 = ld.issue_meta(pid_at(0), lane);
+    meta_n1 = ld.issue_meta(pid_at(min(1, nmine - 1)), lane);
+    buf = ld.issue_bufs(a.H, pid_at(0), h, lane, meta0);
+  }
+  for (int n = 0; n + 1 < nmine; ++n) {
+    uint32_t kp[16], vp[16];
+    ld.rebuild(buf, kp, vp);
+    buf = ld.issue_bufs(a.H, pid_at(n + 1), h, lane, meta_n1);
+    meta_n1 = ld.issue_meta(pid_at(min(n + 2, nmine - 1)), lane);
+    compute(n, kp, vp);
+  }
+  if (nmine > 0) {
+    uint32_t kp[16], vp[16];
+    ld.rebuild(buf, kp, vp);
+    compute(nmine - 1, kp, vp);
   }
   if (err) set_status(a.status, err);
 
