@@ -71,6 +71,9 @@ zf_status check_attention_shape(int32_t T, int32_t H, int32_t D, int32_t Hq) {
   return ZF_OK;
 }
 
+// Longest sequence the split plan covers: 256 splits of at most 256 pages of 16 tokens.
+constexpr int32_t kMaxAttentionLen = 256 * 256 * 16;
+
 }  // namespace
 
 extern "C" {
@@ -128,7 +131,7 @@ zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw
 
 size_t zf_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                                     int32_t head_dim, int32_t max_seq_len) {
-  if (batch < 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (batch < 0 || num_kv_heads <= 0 || max_seq_len < 0 || max_seq_len > kMaxAttentionLen) return 0;
   if (check_attention_shape(16, num_kv_heads, head_dim, num_q_heads) != ZF_OK) return 0;
   return zf::attention_workspace_bytes(batch, num_kv_heads, max_seq_len);
 }
@@ -143,6 +146,7 @@ static zf_status check_attention_io(const zf_seqs* seqs, int32_t num_kv_heads, i
                                     const uint16_t* q, int32_t num_q_heads, float* out,
                                     void* workspace, size_t workspace_bytes) {
   if (!aligned(q) || !aligned(out)) return ZF_EINVAL;
+  if (seqs->max_seq_len > kMaxAttentionLen) return ZF_EUNSUPPORTED;
   if (!aligned(workspace) ||
       workspace_bytes < zf::attention_workspace_bytes(seqs->batch, num_kv_heads, seqs->max_seq_len))
     return ZF_EWORKSPACE;

@@ -455,6 +455,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_k(AttnArgs a, Loader ld) {
 
 // Merges the split partials of one (sequence, kv head) in split order (a kernel of its own:
 // the launch boundary makes every split's partial visible without device-wide fences).
+// Each split's (m, l) pairs are staged in LDS in one parallel step, the per-split weights are
+// formed once, and every thread then reads its accumulator column with independent loads.
+constexpr int kMaxSplitsStaged = 256;
+
 __global__ __launch_bounds__(kThreads) void combine_k(AttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int32_t L = a.lens[b];
@@ -465,19 +469,34 @@ __global__ __launch_bounds__(kThreads) void combine_k(AttnArgs a) {
   const int64_t unit = (int64_t)b * a.H + h;
   const float* base = a.part + unit * a.nsplit_max * kPartFloats;
   const double c2 = a.scale_log2e;
+  __shared__ double s_m[kMaxSplitsStaged][kG];
+  __shared__ float s_w[kMaxSplitsStaged][kG];
+  __shared__ float s_lsum[kG];
+  for (int e = tid; e < nsplit * kG; e += kThreads) {
+    const int x = e / kG, i = e % kG;
+    s_m[x][i] = reinterpret_cast<const double*>(base + x * kPartFloats + kG * kD + kG)[i];
+    s_w[x][i] = base[x * kPartFloats + kG * kD + i];  // l, turned into weights below
+  }
+  __syncthreads();
+  if (tid < kG) {
+    const int i = tid;
+    double mm = -INFINITY;
+    for (int x = 0; x < nsplit; ++x) mm = fmax(mm, s_m[x][i]);
+    float lsum = 0.f;
+    for (int x = 0; x < nsplit; ++x) {
+      const float f = s_m[x][i] == -INFINITY ? 0.f : exp2f((float)((s_m[x][i] - mm) * c2));
+      lsum = fmaf(f, s_w[x][i], lsum);
+      s_w[x][i] = f;
+    }
+    s_lsum[i] = lsum;
+  }
+  __syncthreads();
   for (int e = tid; e < kG * kD; e += kThreads) {
     const int i = e / kD, d = e % kD;
-    double mm = -INFINITY;
-    for (int x = 0; x < nsplit; ++x)
-      mm = fmax(mm, reinterpret_cast<const double*>(base + x * kPartFloats + kG * kD + kG)[i]);
-    float sum = 0.f, lsum = 0.f;
-    for (int x = 0; x < nsplit; ++x) {
-      const float* px = base + x * kPartFloats;
-      const double mx = reinterpret_cast<const double*>(px + kG * kD + kG)[i];
-      const float f = mx == -INFINITY ? 0.f : exp2f((float)((mx - mm) * c2));
-      sum = fmaf(f, px[i * kD + d], sum);
-      lsum = fmaf(f, px[kG * kD + i], lsum);
-    }
+    float sum = 0.f;
+#pragma unroll 8
+    for (int x = 0; x < nsplit; ++x) sum = fmaf(s_w[x][i], base[x * kPartFloats + i * kD + d], sum);
+    const float lsum = s_lsum[i];
     a.out[((int64_t)b * a.H * kG + h * kG + i) * kD + d] = lsum > 0.f ? sum / lsum : 0.f;
   }
 }
@@ -512,6 +531,8 @@ static Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len) {
   }
   pps = (pps + kWaves - 1) / kWaves * kWaves;
   pps = std::min(std::max(pps, 8), kMaxPagesPerSplit);
+  if ((maxpages + pps - 1) / pps > kMaxSplitsStaged)  // very long sequences: fewer, longer splits
+    pps = std::min(kMaxPagesPerSplit, ((maxpages + kMaxSplitsStaged - 1) / kMaxSplitsStaged + kWaves - 1) / kWaves * kWaves);
   return Plan{pps, (maxpages + pps - 1) / pps};
 }
 

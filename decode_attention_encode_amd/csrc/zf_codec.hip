@@ -252,53 +252,48 @@ __global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint
 
 // ------------------------------------------------------------------------------ append
 
-// One workgroup: classify the B new rows, scan their raw counts in batch order, then write.
-// All or nothing: any device-detected problem leaves the cache and seq_lens untouched.
+// Append runs as two kernels.  append_pack_k: one workgroup per new row classifies its 32
+// blocks and writes their sm/nib/base bytes and the row's flag word into the row's slot,
+// which is not yet part of the sequence.  append_commit_k: one workgroup validates every row,
+// scans the rows' raw counts in batch order, and only if the whole batch fits in the spill
+// pool writes the spill slots and row_spill and advances seq_lens and spill_top.  So a failed
+// append changes no defined state: only the slots at position seq_lens[b] may be touched.
 constexpr int kAppendThreads = 1024;
 constexpr int kAppendMaxBatch = 4096;  // two u32 per row in LDS
 
-__global__ __launch_bounds__(kAppendThreads) void append_k(Geom g, SeqView s,
-                                                           const uint16_t* __restrict__ k_new,
-                                                           const uint16_t* __restrict__ v_new, uint8_t* sm,
-                                                           uint8_t* nib, uint8_t* base, uint32_t* row_flags,
-                                                           uint32_t* row_spill, uint8_t* spill,
-                                                           uint64_t* spill_top, uint64_t spill_slots,
-                                                           uint32_t* status) {
-  extern __shared__ uint32_t s_flags[];  // [B] row flags, then [B] exclusive prefixes
-  uint32_t* s_pref = s_flags + s.B;
-  __shared__ uint32_t s_err, s_tmp[kAppendThreads];
-  const int tid = threadIdx.x;
-  if (tid == 0) s_err = 0u;
-  for (int b = tid; b < s.B; b += kAppendThreads) s_flags[b] = 0u;
-  __syncthreads();
-  // phase 0: validate every row position and page
-  for (int b = tid; b < s.B; b += kAppendThreads) {
-    int32_t L = s.lens[b];
-    uint32_t e = 0;
-    if (L < 0 || (int64_t)L + 1 > (int64_t)s.maxp * g.T || L + 1 > s.max_seq_len) {
-      e = ZF_DEV_ELEN;
-    } else {
-      int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
-      if (pid < 0 || pid >= g.P) e = ZF_DEV_EPAGE;
-    }
-    if (e) atomicOr(&s_err, e);
+// Row of the new token of sequence b, or -1 (with the error bit) when it cannot be appended.
+__device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, int b, uint32_t* err) {
+  const int32_t L = s.lens[b];
+  if (L < 0 || (int64_t)L + 1 > (int64_t)s.maxp * g.T || L + 1 > s.max_seq_len) {
+    *err = ZF_DEV_ELEN;
+    return -1;
   }
-  __syncthreads();
-  if (s_err) {
-    if (tid == 0) set_status(status, s_err);
-    return;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
+  if (pid < 0 || pid >= g.P) {
+    *err = ZF_DEV_EPAGE;
+    return -1;
   }
-  const int nb = g.nb(), D = g.D, H = g.H;
-  const int rb = 2 * H * nb;  // blocks per row
-  const int lane8 = tid & 7;
-  const int64_t nblk = (int64_t)s.B * rb;
-  // phase 1: raw flags of the new rows
-  for (int64_t m = tid >> 3; m < nblk; m += kAppendThreads >> 3) {
-    const int b = (int)(m / rb), j = (int)(m % rb);
+  *err = 0;
+  return (int64_t)pid * g.T + L % g.T;
+}
+
+__global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new, uint8_t* sm,
+                                                     uint8_t* nib, uint8_t* base, uint32_t* row_flags) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane8 = tid & 7;
+  uint32_t err;
+  const int64_t row = append_row(g, s, b, &err);
+  if (row < 0) return;  // reported by append_commit_k
+  const int64_t pid = row / g.T, slot = row % g.T;
+  __shared__ uint32_t s_f;
+  if (tid == 0) s_f = 0u;
+  __syncthreads();
+  const int nb = g.nb(), D = g.D, H = g.H, rb = 2 * H * nb;
+  for (int j = tid >> 3; j < rb; j += blockDim.x >> 3) {
     const int half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
-    const uint16_t* src = (kv ? v_new : k_new) + ((int64_t)b * H + h) * D + half * kBlock + lane8 * 8;
-    uint4 in = *reinterpret_cast<const uint4*>(src);
-    uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)b * H + h) * D +
+                                                     half * kBlock + lane8 * 8);
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
     Window win = window8(w);
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) {
@@ -306,68 +301,96 @@ __global__ __launch_bounds__(kAppendThreads) void append_k(Geom g, SeqView s,
       win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
       win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
     }
-    if (lane8 == 0 && (win.special | (uint32_t)(win.emax - win.emin > 15u)))
-      atomicOr(&s_flags[b], 1u << j);
-  }
-  __syncthreads();
-  // phase 2: exclusive scan of raw counts in batch order
-  uint32_t carry = 0;
-  for (int b0 = 0; b0 < s.B; b0 += kAppendThreads) {
-    int b = b0 + tid;
-    uint32_t c = b < s.B ? __popc(s_flags[b]) : 0u;
-    s_tmp[tid] = c;
-    __syncthreads();
-    for (int o = 1; o < kAppendThreads; o <<= 1) {
-      uint32_t add = tid >= o ? s_tmp[tid - o] : 0u;
-      __syncthreads();
-      s_tmp[tid] += add;
-      __syncthreads();
-    }
-    if (b < s.B) s_pref[b] = carry + s_tmp[tid] - c;
-    carry += s_tmp[kAppendThreads - 1];
-    __syncthreads();
-  }
-  const uint64_t top = *spill_top;
-  if ((uint64_t)carry > spill_slots - top) {
-    if (tid == 0) set_status(status, ZF_DEV_ESPILL);
-    return;
-  }
-  // phase 3: write the rows
-  for (int64_t m = tid >> 3; m < nblk; m += kAppendThreads >> 3) {
-    const int b = (int)(m / rb), j = (int)(m % rb);
-    const int half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
-    const int32_t L = s.lens[b];
-    const int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
-    const int slot = L % g.T;
-    const uint16_t* src = (kv ? v_new : k_new) + ((int64_t)b * H + h) * D + half * kBlock + lane8 * 8;
-    uint4 in = *reinterpret_cast<const uint4*>(src);
-    uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    const uint32_t f = s_flags[b];
-    const uint32_t raw_blk = (f >> j) & 1u;
-    Window win = window8(w);
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
+    const uint32_t raw_blk = win.special | (uint32_t)(win.emax - win.emin > 15u);
     const uint32_t bexp = raw_blk ? 0u : win.emin;
     uint32_t smw[2], nibw, hiw;
     pack8(w, bexp, raw_blk, smw, nibw, hiw);
-    const int64_t v0 = (((int64_t)pid * H + h) * 2 + kv) * g.T * D + (int64_t)slot * D + half * kBlock + lane8 * 8;
+    const int64_t v0 = ((pid * H + h) * 2 + kv) * g.T * D + slot * D + half * kBlock + lane8 * 8;
     *reinterpret_cast<uint2*>(sm + v0) = make_uint2(smw[0], smw[1]);
     *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = nibw;
-    if (lane8 == 0) base[v0 / kBlock] = (uint8_t)bexp;
-    if (raw_blk) {
-      const uint64_t idx = top + s_pref[b] + __popc(f & ((1u << j) - 1u));
-      *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hiw;
+    if (lane8 == 0) {
+      base[v0 / kBlock] = (uint8_t)bexp;
+      if (raw_blk) atomicOr(&s_f, 1u << j);
     }
   }
+  __syncthreads();
+  if (tid == 0) row_flags[row] = s_f;
+}
+
+__global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqView s,
+                                                                  const uint16_t* __restrict__ k_new,
+                                                                  const uint16_t* __restrict__ v_new,
+                                                                  const uint32_t* row_flags, uint32_t* row_spill,
+                                                                  uint8_t* spill, uint64_t* spill_top,
+                                                                  uint64_t spill_slots, uint32_t* status) {
+  extern __shared__ uint32_t s_flags[];  // [B] row flags, then [B] exclusive prefixes
+  uint32_t* s_pref = s_flags + s.B;
+  __shared__ uint32_t s_err, s_total;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_err = 0u;
+  __syncthreads();
   for (int b = tid; b < s.B; b += kAppendThreads) {
-    const int32_t L = s.lens[b];
-    const int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
-    row_flags[(int64_t)pid * g.T + L % g.T] = s_flags[b];
-    row_spill[(int64_t)pid * g.T + L % g.T] = (uint32_t)(top + s_pref[b]);
+    uint32_t e;
+    const int64_t row = append_row(g, s, b, &e);
+    if (e) atomicOr(&s_err, e);
+    else s_flags[b] = row_flags[row];
   }
-  __syncthreads();  // every lane has read its length before any is advanced
+  __syncthreads();
+  if (s_err) {
+    if (tid == 0) set_status(status, s_err);
+    return;
+  }
+  // exclusive scan of raw counts in batch order (one wave)
+  if (tid < 64) {
+    uint32_t carry = 0;
+    for (int b0 = 0; b0 < s.B; b0 += 64) {
+      const int b = b0 + tid;
+      const uint32_t c = b < s.B ? __popc(s_flags[b]) : 0u;
+      uint32_t incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t up = __shfl_up((int)incl, o, 64);
+        if (tid >= o) incl += up;
+      }
+      if (b < s.B) s_pref[b] = carry + incl - c;
+      carry += __shfl((int)incl, 63, 64);
+    }
+    if (tid == 0) s_total = carry;
+  }
+  __syncthreads();
+  const uint64_t top = *spill_top;
+  const uint32_t total = s_total;
+  if ((uint64_t)total > spill_slots - top) {
+    if (tid == 0) set_status(status, ZF_DEV_ESPILL);
+    return;
+  }
+  // spill slots of the raw blocks: 8 lanes per block, blocks walked in (row, block) order
+  const int nb = g.nb(), D = g.D, H = g.H;
+  const uint32_t rb = 2u * H * nb, nblk = (uint32_t)s.B * rb;
+  const int lane8 = tid & 7;
+#pragma unroll 4
+  for (uint32_t m = tid >> 3; m < nblk; m += kAppendThreads >> 3) {
+    const uint32_t b = m / rb, j = m - b * rb;
+    const uint32_t f = s_flags[b];
+    if (!((f >> j) & 1u)) continue;
+    const uint32_t hk = j / nb, half = j - hk * nb, h = hk >> 1, kv = hk & 1;
+    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)b * H + h) * D +
+                                                     half * kBlock + lane8 * 8);
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t hi = 0u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
+    const uint64_t idx = top + s_pref[b] + __popc(f & ((1u << j) - 1u));
+    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
+  }
+  for (int b = tid; b < s.B; b += kAppendThreads) {
+    uint32_t e;
+    const int64_t row = append_row(g, s, b, &e);
+    row_spill[row] = (uint32_t)(top + s_pref[b]);
+  }
+  __syncthreads();  // every length has been read before any is advanced
   for (int b = tid; b < s.B; b += kAppendThreads) s.lens[b] += 1;
-  if (tid == 0) *spill_top = top + carry;
+  if (tid == 0) *spill_top = top + total;
 }
 
 // ------------------------------------------------------------------------------ decode
@@ -454,10 +477,11 @@ int append_max_batch() { return kAppendMaxBatch; }
 hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t st) {
   SeqView s = view(q);
+  hipLaunchKernelGGL(append_pack_k, dim3(q->batch), dim3(256), 0, st, g, s, k_new, v_new, c->sm, c->nib,
+                     c->base, c->row_flags);
   size_t lds = 2 * (size_t)q->batch * sizeof(uint32_t);
-  hipLaunchKernelGGL(append_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, k_new, v_new, c->sm,
-                     c->nib, c->base, c->row_flags, c->row_spill, c->spill, c->spill_top,
-                     c->spill_slots, c->status);
+  hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, k_new, v_new,
+                     c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
   return hipGetLastError();
 }
 

@@ -80,14 +80,17 @@ def test_append_bitexact(key, steps):
     _append_steps(w, steps, check_every=16)
 
 
-def test_append_spill_exhaustion_writes_nothing():
+def test_append_spill_exhaustion_changes_no_defined_state():
     w = SMALL
     inst = synth.make(w)
     orc = oracle_cache(inst, 1 << 20)
     need = orc.spill_top
     s = Setup(inst, spill_slots=need)  # exactly full after the encode
     assert s.status() == 0 and int(host(s.cache.spill_top)[0]) == need
-    before = {n: host(getattr(s.cache, n)).copy() for n in ("sm", "nib", "base", "row_flags", "row_spill", "spill")}
+    rows = valid_rows(inst)
+    names = ("sm", "nib", "base", "row_flags", "row_spill")
+    before = {n: host(getattr(s.cache, n)).copy() for n in names}
+    spill_before = host(s.cache.spill).copy()
     k, v = synth.tokens(w, inst.seq_lens)
     k[:, :, 0] = 0  # every new row gets a raw block
     zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
@@ -95,8 +98,20 @@ def test_append_spill_exhaustion_writes_nothing():
     assert s.status() & zf.ZF_DEV_ESPILL
     assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
     assert int(host(s.cache.spill_top)[0]) == need
-    for n, a in before.items():
-        assert np.array_equal(host(getattr(s.cache, n)), a), n
+    assert np.array_equal(host(s.cache.spill), spill_before)
+    for n in names:
+        a, b = host(getattr(s.cache, n)), before[n]
+        m = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
+        assert np.array_equal(a[m], b[m]), n
+    # the same call with room for the new rows then succeeds and matches the oracle
+    s2 = Setup(inst)
+    orc2 = oracle_cache(inst, s2.cache.spill_slots)
+    lens = inst.seq_lens.copy()
+    zf.zf_append_kv(s2.cache, s2.seqs, dev(k), dev(v))
+    assert orc2.append(lens, inst.page_table, k, v) == oracle.OK
+    torch.cuda.synchronize()
+    assert s2.status() == 0
+    compare_packed(s2.cache, orc2, valid_rows(inst, lens), "append after a failed one")
 
 
 def test_encode_spill_exhaustion_keeps_pool():
