@@ -4,8 +4,9 @@
 // cache stays compressed in HBM and each bf16 is rebuilt in registers with one integer add
 // (two values per 32-bit add here) right before it is used; decode is bound by the bytes
 // read per step, so reading 12-bit values instead of 16-bit ones is the whole gain.
-// Attention itself is the plain decode step (essay "Open weights as an optimization
-// surface": one new token per sequence attends over its KV cache).
+// Attention itself is the plain decode step (page "Open Weights: from files to tokens /
+// second", section "03 / The inference loop": one new token per sequence attends over its
+// KV cache).
 //
 // Mapping (head_dim 128, 16-token pages, 4 query heads per kv head):
 //   grid (split, kv head, sequence); 4 waves per workgroup; wave w takes pages w, w+4, ...

@@ -1,8 +1,8 @@
 // zf_codec.hip - block codec kernels for gfx950: full-cache encode, per-step append, decode.
 //
 // Codec: ZipFusion video summary ("Run AI Faster With Lossless Compressed Memory", chapter
-// "Twelve Bits and One Addition").  Paged cache: essay "Open weights as an optimization
-// surface" (KV memory handed out in fixed-size pages).
+// "Twelve Bits and One Addition").  Paged cache: page "Open Weights: from files to tokens /
+// second", section "09 / The optimization stack" (KV memory allocated in fixed-size blocks).
 //
 // Work split.  A raw page u16[H][2][T][D] is one contiguous 64 KB run (H = 8, T = 16,
 // D = 128), so one workgroup owns one (sequence, logical page) and streams it with 16-byte

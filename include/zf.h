@@ -7,8 +7,9 @@
  * (12 bits per value, 75 % of BF16, chapter "Twelve Bits and One Addition"); blocks whose
  * exponents are too spread out stay raw; attention rebuilds every value in registers with a
  * single integer addition instead of unpacking the cache to a buffer inside the decode loop.
- * The cache is paged (essay "Open weights as an optimization surface": KV memory allocated in
- * fixed-size blocks, decode phase reading the cache every step).
+ * The cache is paged (page "Open Weights: from files to tokens / second": section "09 / The
+ * optimization stack" allocates KV memory in blocks; section "03 / The inference loop" has
+ * decode read the cache every step).
  *
  * ---------------------------------------------------------------------------------- format
  * Geometry: num_pages pages of page_size tokens; num_kv_heads heads; head_dim a multiple of
@@ -124,10 +125,10 @@ zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw
  * by one integer add; no decompressed copy).  q: bf16 u16[batch][num_q_heads][D]; out: f32
  * [batch][num_q_heads][D]; q head i uses kv head i / (num_q_heads / H).  out =
  * softmax(scale * q K^T) V over the sequence's tokens in logical order; zeros when
- * seq_lens[b] == 0.  Workspace: zf_attention_workspace_bytes(...) bytes that must be zero
- * before the first call (zf_attention_workspace_init); every call leaves it reusable.  Calls
- * sharing one workspace must not overlap.  Requires D == 128, page_size == 16 and
- * num_q_heads == 4 * H in this version (ZF_EUNSUPPORTED otherwise). */
+ * seq_lens[b] == 0.  Workspace: zf_attention_workspace_bytes(...) bytes of device memory, any
+ * contents (it holds per-split partials); calls sharing one workspace must not overlap.
+ * Requires D == 128, page_size == 16, num_q_heads == 4 * H and max_seq_len <= 2^20 in this
+ * version (ZF_EUNSUPPORTED otherwise).  Two kernel launches (split attention, split merge). */
 zf_status zf_decode_attention(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* q,
                               int32_t num_q_heads, float scale, float* out, void* workspace,
                               size_t workspace_bytes, zf_stream_t stream);
@@ -143,7 +144,7 @@ zf_status zf_decode_attention_raw(const uint16_t* raw_pages, int32_t num_pages,
 
 size_t zf_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                                     int32_t head_dim, int32_t max_seq_len);
-/* Zero-fills a workspace on `stream` (a kernel, no memset node). */
+/* Zero-fills a workspace on `stream` (a kernel, no memset node); optional. */
 zf_status zf_attention_workspace_init(void* workspace, size_t workspace_bytes,
                                       zf_stream_t stream);
 

@@ -3,9 +3,9 @@
  *
  * Every loop here follows the definition directly: no blocking, no fusion, no reordering.
  * Codec: ZipFusion video summary, chapter "Twelve Bits and One Addition" (shared base
- * exponent, 4-bit offset, raw fallback, one-add rebuild).  Attention: essay "Open weights as
- * an optimization surface", decode phase / KV cache sections (softmax attention of one query
- * token over the cached tokens), computed in fp64.
+ * exponent, 4-bit offset, raw fallback, one-add rebuild).  Attention: page "Open Weights:
+ * from files to tokens / second", section "03 / The inference loop" (softmax attention of one
+ * query token over the cached tokens), computed in fp64.
  */
 #include "zf_oracle.h"
 

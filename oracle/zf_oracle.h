@@ -19,8 +19,8 @@
  *      nibbles (exponent >> 4), packed the same way, in a 32-byte spill slot.
  *  - Spill slots: a token row's raw blocks take consecutive slots in block order; rows are
  *    numbered (sequence, token) ascending for a full encode and in batch order for an append.
- *  - Attention (essay "Open weights as an optimization surface", sections on the decode phase
- *    and the KV cache): one query token per sequence attends over every cached token of its
+ *  - Attention (page "Open Weights: from files to tokens / second", section
+ *    "03 / The inference loop"): one query token per sequence attends over every cached token of its
  *    sequence; grouped-query heads share a KV head (q head -> q / (Hq / Hkv)); scaled dot
  *    product with scale 1/sqrt(D), softmax, weighted sum of V; computed in fp64 from the bf16
  *    inputs.

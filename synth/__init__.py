@@ -6,7 +6,8 @@ CPU oracle are fed from here, and from nowhere else.
 
 Workload shapes follow the ZipFusion video summary (page "Run AI Faster With Lossless
 Compressed Memory": Llama-3.1-8B-shaped decode at batch 32, 32 query / 8 KV heads) and the
-essay "Open weights as an optimization surface" (paged KV cache, decode phase).
+page "Open Weights: from files to tokens / second" (sections "03 / The inference loop" and
+"09 / The optimization stack": decode phase, paged KV cache).
 """
 from __future__ import annotations
 

@@ -6,7 +6,8 @@ path).  The compressed path must equal the twin bit for bit (same kernel, same s
 the compressed loader rebuilds exactly the bf16 bits the twin reads), must not depend on
 where pages sit physically, and must repeat bitwise.
 
-Attention: essay "Open weights as an optimization surface" (decode step over the KV cache);
+Attention: page "Open Weights: from files to tokens / second", section "03 / The inference
+loop" (decode step over the KV cache);
 compression in the loop: ZipFusion video summary ("Run AI Faster With Lossless Compressed
 Memory").
 """

@@ -1,7 +1,7 @@
 """Pins for the oracle's fp64 decode attention.
 
-Attention here is the plain definition (essay "Open weights as an optimization surface",
-decode phase and KV-cache sections): one query token per sequence, scaled dot products with
+Attention here is the plain definition (page "Open Weights: from files to tokens /
+second", section "03 / The inference loop"): one query token per sequence, scaled dot products with
 every cached token of its sequence reached through the page table, softmax, weighted sum of V;
 grouped-query heads share one KV head.  The pins are closed forms (one token, zero query,
 equal keys, a dominating logit, a two-token weight), a brute-force computation with library
