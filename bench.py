@@ -2,7 +2,9 @@
 
 One step = what a decode step does to one attention layer's cache: zf_append_kv (encode one
 new K/V token per sequence into the packed paged cache) followed by zf_decode_attention (fused
-GQA attention over the packed cache, every value rebuilt in registers).  Workload: the
+GQA attention over the packed cache, every value rebuilt in registers).  Steps rotate over
+several layer caches (3 by default, 1.35 GB) so that, as in a multi-layer model, a layer's
+cache is not still sitting in the 256 MB last-level cache when its next step comes.  Workload: the
 Llama-3.1-8B-shaped decode of the ZipFusion video summary ("Run AI Faster With Lossless
 Compressed Memory"): batch 32, 32 query / 8 KV heads, head_dim 128, 4096 cached tokens per
 sequence, 16-token pages in random order, synthetic bf16 K/V (seeded generator; no model
@@ -50,6 +52,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=3,
+                    help="layer caches the steps rotate over (1.35 GB at 3, beyond the 256 MB "
+                         "last-level cache, as in a multi-layer model)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--extras", action="store_true",
@@ -88,35 +93,41 @@ def main():
         return
 
     W, K = args.warmup, args.steps
-    w = synth.WORKLOADS[WORKLOAD].replace(extra_tokens=W + K)
+    NL = max(1, args.layers)
+    w = synth.WORKLOADS[WORKLOAD].replace(extra_tokens=(W + K + NL - 1) // NL + 1)
     t0 = time.time()
     inst = synth.make(w)
     B, H, Hq, D, T = w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.page_size
     lens0 = inst.seq_lens.copy()
-    # tokens and queries of every step, generated up front and made resident
+    to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    # step s works on layer s % NL; per layer the sequences grow by one token per visit
+    visits = [(s // NL) for s in range(W + K)]  # appends this layer has seen before step s
     ks, vs, qs = [], [], []
     for s in range(W + K):
-        k, v = synth.tokens(w, lens0 + s)
+        k, v = synth.tokens(w, lens0 + visits[s])
         ks.append(k)
         vs.append(v)
         qs.append(synth.query(w, s))
-    to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
     k_dev = to(np.stack(ks))
     v_dev = to(np.stack(vs))
     q_dev = to(np.stack(qs))
     gen_s = time.time() - t0
 
-    rows_cap = int(lens0.sum()) + B * (W + K)
+    rows_cap = int(lens0.sum()) + B * (w.extra_tokens + 1)
     spill_slots = rows_cap * 2 * H * (D // 64)
-    cache = zf.PackedCache.empty(inst.num_pages, T, H, D, spill_slots, device=dev)
-    max_len = int(lens0.max()) + W + K
-    seqs = zf.Seqs(to(inst.page_table), to(lens0.copy()), max_len)
+    max_len = int(lens0.max()) + w.extra_tokens
     raw = to(inst.raw_pages)
-    enc_ws = zf.encode_workspace(seqs)
-    zf.zf_encode_kv(cache, seqs, raw, enc_ws)
+    pt_dev = to(inst.page_table)
+    layers = []
+    for _ in range(NL):  # one packed cache per layer (same data), own lengths
+        cache = zf.PackedCache.empty(inst.num_pages, T, H, D, spill_slots, device=dev)
+        seqs = zf.Seqs(pt_dev, to(lens0.copy()), max_len)
+        zf.zf_encode_kv(cache, seqs, raw, zf.encode_workspace(seqs))
+        layers.append((cache, seqs))
     torch.cuda.synchronize()
-    assert zf.zf_get_status(cache.status) == 0
-    top0 = int(cache.spill_top.item())
+    for cache, _ in layers:
+        assert zf.zf_get_status(cache.status) == 0
+    top0 = int(layers[0][0].spill_top.item())
     rows0 = int(lens0.sum())
     ws = zf.attention_workspace(B, H, Hq, D, max_len, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
@@ -124,6 +135,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(s, ev=None):
+        cache, seqs = layers[s % NL]
         zf.zf_append_kv(cache, seqs, k_dev[s], v_dev[s])
         if ev is not None:
             ev[0].record(stream)
@@ -142,33 +154,37 @@ def main():
         step(W + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    status = zf.zf_get_status(cache.status)
-    assert status == 0, f"device status {status}"
+    for cache, _ in layers:
+        status = zf.zf_get_status(cache.status)
+        assert status == 0, f"device status {status}"
     attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
 
     # ---- algorithmic bytes of each timed attention launch
-    flags = cache.row_flags.cpu().numpy().view(np.uint32)
     pt = inst.page_table
     row_bytes = 2 * H * (D + D // 2 + D // 64) + 8  # planes + base + row flags + row spill
-    appended_raw = np.zeros(W + K, np.int64)
+    flags = [c.row_flags.cpu().numpy().view(np.uint32) for c, _ in layers]
+    raw_after = []  # raw blocks in the attended layer right after step s's append
+    seen = [top0] * NL
     for s in range(W + K):
-        pos = lens0 + s
+        lay = s % NL
+        pos = lens0 + visits[s]
         pages = pt[np.arange(B), pos // T]
-        f = flags[pages, pos % T]
-        appended_raw[s] = sum(bin(int(x)).count("1") for x in f)
-    cum_raw = top0 + np.cumsum(appended_raw)  # raw blocks present after step s's append
+        f = flags[lay][pages, pos % T]
+        seen[lay] += sum(bin(int(x)).count("1") for x in f)
+        raw_after.append(seen[lay])
     attn_bytes = []
+    tokens_attended = 0
     for i in range(K):
         s = W + i
-        L = lens0 + s + 1
-        nbytes = int(L.sum()) * row_bytes + 32 * int(cum_raw[s])
+        L = lens0 + visits[s] + 1
+        tokens_attended += int(L.sum())
+        nbytes = int(L.sum()) * row_bytes + 32 * int(raw_after[s])
         nbytes += B * Hq * D * (2 + 4) + int(np.ceil(L / T).sum()) * 4 + B * 4
         attn_bytes.append(nbytes)
     attn_bytes = np.array(attn_bytes, np.float64)
     mean_attn_s = attn_ms.mean() / 1e3
     achieved = attn_bytes.mean() / mean_attn_s / 1e9
-    tokens_attended = (lens0 + W + 1).sum() + B * (K - 1) / 2
-    uncompressed_eq = float(tokens_attended * H * 2 * D * 2) / mean_attn_s / 1e9
+    uncompressed_eq = tokens_attended / K * H * 2 * D * 2 / mean_attn_s / 1e9
     packed_valid = rows0 * row_bytes + 32 * top0
     ratio = packed_valid / (rows0 * H * 2 * D * 2)
 
@@ -179,6 +195,7 @@ def main():
             traffic = pmc.get("hbm_bytes_per_launch")
 
     extra = {
+        "layers_rotated": NL,
         "attention_kernel_us_mean": round(attn_ms.mean() * 1e3, 2),
         "attention_kernel_us_min": round(attn_ms.min() * 1e3, 2),
         "attention_bytes_per_launch": int(attn_bytes.mean()),
@@ -189,8 +206,8 @@ def main():
     }
 
     if args.extras:
-        extra.update(extras(torch, zf, inst, cache, seqs, raw, q_dev[W + K - 1], ws, out,
-                            scale, attn_bytes.mean(), row_bytes))
+        extra.update(extras(torch, zf, inst, layers, raw, q_dev[W + K - 1], ws, out, scale,
+                            attn_bytes.mean(), row_bytes))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -211,8 +228,8 @@ def main():
         "data": "synthetic (seeded bf16 K/V: per-channel log-uniform scales, outlier and zero "
                 "blocks; no model weights)",
         "config": {"workload": w.name, "batch": B, "context": int(lens0[0]), "q_heads": Hq,
-                   "kv_heads": H, "head_dim": D, "page_size": T, "layers": 1,
-                   "step": "append 1 token/seq + fused compressed attention"},
+                   "kv_heads": H, "head_dim": D, "page_size": T, "layers_rotated": NL,
+                   "step": "one layer: append 1 token/seq + fused compressed attention"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
@@ -222,39 +239,43 @@ def main():
     print(json.dumps(result))
 
 
-def extras(torch, zf, inst, cache, seqs, raw, q, ws, out, scale, attn_bytes, row_bytes):
-    """Twin (uncompressed) attention, flushed-cache attention, full encode / decode rates."""
+def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_bytes):
+    """Twin (uncompressed) attention over the same rotation of layer caches, the single-layer
+    warm-cache loop, and full-cache encode / decode rates."""
     res = {}
     stream = torch.cuda.current_stream()
+    NL = len(layers)
 
-    def timeit(fn, n=20, flush=None):
+    def timeit(fn, n=30):
+        fn(0)
+        torch.cuda.synchronize()
         ts = []
-        for _ in range(n):
-            if flush is not None:
-                flush()
+        for i in range(n):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            fn()
+            fn(i)
             b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        return float(np.mean(ts)) / 1e3
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ts])) / 1e3
 
     status = torch.zeros(1, dtype=torch.int32, device=raw.device)
-    # the twin reads raw pages holding the same tokens the packed cache holds
-    dec = torch.zeros_like(raw)
-    zf.zf_decode_kv(cache, seqs, dec)
-    t_twin = timeit(lambda: zf.zf_decode_attention_raw(dec, seqs, q, scale, out, ws, status))
-    t_pack = timeit(lambda: zf.zf_decode_attention(cache, seqs, q, scale, out, ws))
+    # twins: raw pages holding the tokens each packed layer holds now
+    twins = []
+    for cache, seqs in layers:
+        d = torch.zeros_like(raw)
+        zf.zf_decode_kv(cache, seqs, d)
+        twins.append(d)
+    t_pack = timeit(lambda i: zf.zf_decode_attention(layers[i % NL][0], layers[i % NL][1], q, scale, out, ws))
+    t_twin = timeit(lambda i: zf.zf_decode_attention_raw(twins[i % NL], layers[i % NL][1], q, scale, out, ws, status))
+    t_warm = timeit(lambda i: zf.zf_decode_attention(layers[0][0], layers[0][1], q, scale, out, ws))
     res["attention_packed_us"] = round(t_pack * 1e6, 2)
     res["attention_twin_uncompressed_us"] = round(t_twin * 1e6, 2)
     res["speedup_vs_uncompressed_twin"] = round(t_twin / t_pack, 3)
-    scratch = torch.empty(1 << 29, dtype=torch.uint8, device=raw.device)
-    flush = lambda: scratch.fill_(0)
-    t_flush = timeit(lambda: zf.zf_decode_attention(cache, seqs, q, scale, out, ws), n=10, flush=flush)
-    res["attention_after_512MiB_flush_us"] = round(t_flush * 1e6, 2)
-    res["attention_after_flush_GBps"] = round(attn_bytes / t_flush / 1e9, 1)
-    # full-cache encode and decode of the whole pool (the lengths as they are now)
+    res["attention_single_layer_warm_us"] = round(t_warm * 1e6, 2)
+    res["attention_single_layer_warm_GBps"] = round(attn_bytes / t_warm / 1e9, 1)
+    # full-cache encode and decode of one layer (the lengths as they are now)
+    cache, seqs = layers[0]
     lens = seqs.seq_lens.cpu().numpy()
     rows = int(lens.sum())
     raw_bytes = rows * 2 * inst.w.num_kv_heads * inst.w.head_dim * 2
@@ -264,11 +285,11 @@ def extras(torch, zf, inst, cache, seqs, raw, q, ws, out, scale, attn_bytes, row
                               cache.head_dim, cache.spill_slots, device=raw.device)
     enc_ws = zf.encode_workspace(seqs)
 
-    def enc():
+    def enc(i):
         c2.spill_top.zero_()
-        zf.zf_encode_kv(c2, seqs, dec, enc_ws)
+        zf.zf_encode_kv(c2, seqs, twins[0], enc_ws)
     t_enc = timeit(enc, n=10)
-    t_dec = timeit(lambda: zf.zf_decode_kv(cache, seqs, dec), n=10)
+    t_dec = timeit(lambda i: zf.zf_decode_kv(cache, seqs, twins[0]), n=10)
     res["encode_GBps_read_plus_written"] = round((raw_bytes + packed_bytes) / t_enc / 1e9, 1)
     res["decode_GBps_read_plus_written"] = round((raw_bytes + packed_bytes) / t_dec / 1e9, 1)
     res["encode_us"] = round(t_enc * 1e6, 1)
@@ -290,7 +311,8 @@ def cpu_baseline(w, inst, lens0, ks, vs, qs, budget_s, row_bytes):
     lens = lens0.copy()
     done = 0
     t0 = time.perf_counter()
-    while done < len(ks):
+    cap = inst.page_table.shape[1] * T
+    while done < len(ks) and int(lens.max()) < cap:
         k, v = ks[done], vs[done]
         pos = lens.copy()
         assert c.append(lens, inst.page_table, k, v) == 0
