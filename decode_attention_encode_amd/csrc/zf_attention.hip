@@ -12,16 +12,19 @@
 //   grid (split, kv head, sequence); 4 waves per workgroup; wave w takes pages w, w+4, ...
 //   of its split, one page per step of a software pipeline: row metadata (flags, spill
 //   base) two pages ahead, planes and spill slots one page ahead, compute on the current one.
-//   K: lane = token (lane & 15) x quarter (lane >> 4), 32 head_dim values per lane read as
-//   16-byte loads.  q.K^T runs on v_mfma_f32_16x16x32_bf16 with the rebuilt K pairs as B
-//   (k = head_dim, n = token) and the 4 query heads replicated over the 16 rows of A, so
-//   every lane receives the 4 scores of its own token without a cross-lane reduction.
-//   V: lane = token (lane & 7, two passes of 8 tokens) x 16 head_dim values (lane >> 3);
-//   p.V is fp32 FMAs into 4 heads x 16 dims per lane, reduced across the 8 token lanes once
-//   per split, then across the 4 waves in LDS.
-//   Softmax: running max per head in fp64, raised (with a rescale) only when a page exceeds
-//   it.  Pages holding a score with |q.k| > kBigScore get exact fp64 scores: at that size one
-//   fp32 ulp of a score is already a visible change of its weight.
+//   lane = (t = lane & 15, qd = lane >> 4).
+//   K: lane holds 32 head_dim values (quarter qd) of token t, read as 16-byte loads.
+//   Scores as S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (rebuilt K pairs as A, the 4 query
+//   heads replicated over the 16 columns of B): lane (t, qd) receives the scores of tokens
+//   4qd..4qd+3 for query head t & 3 -- exactly the A-operand layout of the p.V product.
+//   p.V on v_mfma_f32_16x16x16_bf16: A rows are the 4 heads' weights split into three bf16
+//   parts (rows 0-3 high, 4-7 middle, 8-11 low part; p = hi + mid + lo to ~2^-27), B is V
+//   with k = token: lane (t, qd) loads tokens 4qd..4qd+3, head_dim 8t..8t+7, rebuilds them
+//   and turns value pairs into token pairs with byte permutes.  The three row groups of the
+//   fp32 product are summed once per split.
+//   Softmax: running max in fp64, raised (with a rescale) only when a page exceeds it.  Pages
+//   holding a score with |q.k| > kBigScore get exact fp64 scores: at that size one fp32 ulp of
+//   a score is already a visible change of its weight.
 //   Splits of the token axis write (acc, l, m) partials; a second small kernel merges them
 //   in split order, so results do not depend on timing.
 // One kernel body serves the packed cache and raw bf16 pages (the uncompressed twin): both
@@ -34,33 +37,90 @@
 namespace zf {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kD = 128, kT = 16, kG = 4, kWaves = 4, kThreads = 64 * kWaves;
+// One workgroup of 8 waves per CU (two per SIMD): with two smaller workgroups sharing a CU, the
+// older one is issued first and the younger one then finishes alone at half occupancy.
+constexpr int kD = 128, kT = 16, kG = 4, kWaves = 8, kThreads = 64 * kWaves;
 constexpr double kLog2e = 1.4426950408889634;
-constexpr float kBigScore = 64.f;  // |q.k| above which a page's scores are recomputed in fp64
-constexpr int kMaxPagesPerSplit = 4 * 64;  // each wave keeps its page ids in one register
-// One split's partial: acc[kG][kD] f32, l[kG] f32, m[kG] f64 (8-byte aligned).
-constexpr int kPartFloats = kG * kD + kG + 2 * kG;
+constexpr float kBigScore = 64.f;  // |q.k| above which a score may need the fp64 path
+constexpr double kNegligible = 16.0;  // weights below 2^-16 of the largest never need it
+constexpr int kMaxPagesPerSplit = kWaves * 64;  // each wave keeps its page ids in one register
+// One split's partial, in doubles: acc[kG][kD], l[kG], m[kG].
+constexpr int kPartDoubles = kG * kD + 2 * kG;
 
 struct AttnArgs {
   int32_t B, H, maxp, max_seq_len, pps, nsplit_max, num_pages;
+  int32_t direct;  // one split per sequence: attn_k writes the output itself
   const int32_t* pt;
   const int32_t* lens;
   const uint16_t* q;
   double scale_log2e;
   float* out;
-  float* part;        // [B][H][nsplit_max][kPartFloats]
-  uint32_t* counter;  // [B][H]
+  double* part;  // [B][H][nsplit_max][kPartDoubles]
   uint32_t* status;
 };
 
-// ---------------------------------------------------------------- loaders
-// issue_meta / issue_bufs only start loads; rebuild turns one page's buffers into bf16 pairs:
-//   kp[4c + r] = K (dim 32*qd + 8c + r, same + 4) of token lane & 15
-//   vp[8ps + 4c + r] = V (dim 16*g + 8c + r, same + 4) of token 8*ps + (lane & 7), g = lane >> 3
+// ---------------------------------------------------------------- LDS staging
+// Pages travel HBM -> LDS with the direct global-to-LDS loads of gfx950 (each lane's bytes land
+// at base + lane * size), so a wave keeps several pages in flight without holding them in
+// VGPRs.  The loads are counted by hand: every wave issues a fixed number of them per page,
+// and waits with an exact vmcnt for the oldest page only.  LDS reads are inline asm that wait
+// for their own results, so the compiler never sees an LDS read it would have to fence against
+// the whole DMA queue.
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)(uintptr_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)(uintptr_t)lds, 4, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------- loaders
+// A loader moves one page (16 tokens of kv head h) into an LDS slot and rebuilds it as bf16 pairs:
+//   kp[4c + r]   K (head_dim 32*qd + 8c + r, same + 4) of token t
+//   vt[2n], vt[2n + 1]   V (tokens 4qd, 4qd+1) and (4qd+2, 4qd+3) at head_dim vdim(n, t)
+// with t = lane & 15, qd = lane >> 4.  kMetaLoads / kPageLoads: direct loads per meta / page.
+
+__device__ __forceinline__ int vdim(int n, int t) { return 8 * t + (n & 3) + 4 * (n >> 2); }
+
+// pr[j][r] = (value r, value r + 4) of token row j (8 values, 8t..8t+7) -> token pairs per dim
+__device__ __forceinline__ void to_token_pairs(const uint32_t (&pr)[4][4], uint32_t (&vt)[16]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    vt[2 * r + 0] = __builtin_amdgcn_perm(pr[1][r], pr[0][r], 0x05040100u);
+    vt[2 * r + 1] = __builtin_amdgcn_perm(pr[3][r], pr[2][r], 0x05040100u);
+    vt[2 * (r + 4) + 0] = __builtin_amdgcn_perm(pr[1][r], pr[0][r], 0x07060302u);
+    vt[2 * (r + 4) + 1] = __builtin_amdgcn_perm(pr[3][r], pr[2][r], 0x07060302u);
+  }
+}
+
+constexpr uint32_t kSlotBytes = 8192;  // one page of either loader
+constexpr uint32_t kMetaBytes = 256;   // one page's row metadata (packed loader)
+constexpr int kMetaRing = 8;
+
+// Packed page slot (lane L = (t, qd) reads every piece below with one 16-byte LDS read, and
+// the 16 lanes of a quarter wave always hit 16 different bank groups):
+//   [0, 2048)     K sm rows 0..15, 128 B each; 16-byte chunk c of row r at c ^ ((r >> 1) & 7)
+//   [2048, 4096)  V sm, per lane: the 8 bytes of head_dim 8t..8t+7 of rows 4qd..4qd+3
+//   [4096, 5120)  K nibble rows, 64 B each; chunk c of row r at c ^ ((r >> 2) & 3)
+//   [5120, 6144)  V nibbles, per lane: 4 bytes of rows 4qd..4qd+3
+//   [6144, 7168)  K spill piece of each lane (16 bytes)
+//   [7168, 8192)  V spill pieces, per lane: 4 bytes of rows 4qd..4qd+3
+// The V pieces are gathered 4 bytes per lane so that they land transposed.
+// Meta slot, one dword per lane of a 4-byte gather: words 0..15 row flags, 16..31 first spill
+// slots, 32..47 base bytes (K rows, then V rows), 48..63 row flags again; words 16..31 and
+// 48..63 hold row r at 4 * (r & 3) + (r >> 2), so rows r, r + 4, r + 8, r + 12 are adjacent.
 struct PackedLoader {
   const uint8_t* sm;
   const uint8_t* nib;
@@ -68,162 +128,215 @@ struct PackedLoader {
   const uint32_t* row_flags;
   const uint32_t* row_spill;
   const uint8_t* spill;  // a readable address even when spill_slots == 0
-  uint64_t spill_slots;
+  uint32_t max_slot;     // last usable spill slot (0 when the pool is empty)
 
-  struct Meta {
-    uint32_t fk, sk, fv[2], sv[2];  // flags and first spill slot of the rows this lane reads
-  };
-  struct Bufs {
-    uint4 ks0, ks1, kn, kh;
-    uint4 vs[2], vh2;  // vh2: the two passes' 8-byte spill pieces
-    uint2 vn[2];
-    uint32_t kb, vb[2], vmask;  // base bytes; bit ps of vmask = V block raw
-    uint32_t kraw;
-  };
+  static constexpr int kMetaLoads = 1, kPageLoads = 20;
 
-  __device__ __forceinline__ Meta issue_meta(int64_t pid, int lane) const {
-    const int t = lane & 15, tv = lane & 7;
-    Meta m;
-    m.fk = row_flags[pid * kT + t];
-    m.sk = row_spill[pid * kT + t];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      m.fv[ps] = row_flags[pid * kT + 8 * ps + tv];
-      m.sv[ps] = row_spill[pid * kT + 8 * ps + tv];
+  __device__ __forceinline__ void issue_meta(int64_t pid, int H, int h, int lane, uint32_t ms) const {
+    const int grp = lane >> 4, i = lane & 15;
+    const int rt = 4 * (i & 3) + (i >> 2);  // row stored at word i of the transposed groups
+    const uint32_t* fl = row_flags + pid * kT;
+    const uint32_t* sp = row_spill + pid * kT;
+    const uint32_t* bs = reinterpret_cast<const uint32_t*>(base + ((pid * H + h) * 2) * kT * 2);
+    const uint32_t* g = grp == 0 ? fl + i : grp == 1 ? sp + rt : grp == 2 ? bs + i : fl + rt;
+    dma4(g, ms);
+  }
+
+  // spill piece of the block whose lower raw blocks are `below` in its row: slot = first +
+  // popcount(below); clamped into the pool so that no metadata can address outside it (a
+  // compressed block loads a piece that is never used)
+  __device__ __forceinline__ const uint8_t* spill_at(uint32_t below, uint32_t first, const uint8_t* piece) const {
+    const uint32_t slot = min((uint32_t)__popc(below) + first, max_slot);
+    return piece + (uint64_t)slot * 32;
+  }
+
+  // ms: this page's meta slot (already arrived)
+  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, uint32_t ms) const {
+    const int t = lane & 15, qd = lane >> 4;
+    uint32_t fk, sk;
+    u32x4 fv, sv;
+    asm volatile(
+        "ds_read_b32 %0, %4\n\t"
+        "ds_read_b32 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fk), "=&v"(sk), "=&v"(fv), "=&v"(sv)
+        : "v"(ms + 4 * t), "v"(ms + 64 + 4 * (4 * (t & 3) + (t >> 2))),
+          "v"(ms + 192 + 16 * (lane & 3)), "v"(ms + 64 + 16 * (lane & 3))
+        : "memory");
+    // K: lane (t, qd) takes half qd & 1 of block (h, K, qd >> 1) of row t
+    const int jk = (h * 2 + 0) * 2 + (qd >> 1);
+    dma16(spill_at(fk & ((1u << jk) - 1u), sk, spill + (qd & 1) * 16), slot + 6144);
+    // V, gather j: lane l serves row 4j + (l & 3) of reader lane 16j + (l >> 2)
+    const int jv = (h * 2 + 1) * 2 + (lane >> 5);
+    const uint32_t vmask = (1u << jv) - 1u;
+    const uint8_t* vpiece = spill + ((lane >> 2) & 7) * 4;
+    dma4(spill_at(fv.x & vmask, sv.x, vpiece), slot + 7168);
+    dma4(spill_at(fv.y & vmask, sv.y, vpiece), slot + 7168 + 256);
+    dma4(spill_at(fv.z & vmask, sv.z, vpiece), slot + 7168 + 512);
+    dma4(spill_at(fv.w & vmask, sv.w, vpiece), slot + 7168 + 768);
+    const int64_t row0 = ((pid * H + h) * 2) * kT;  // K row 0 of the page
+    const uint8_t* smp = sm + row0 * kD;
+    const uint8_t* nbp = nib + row0 * (kD / 2);
+    {  // K sm: gather i, lane l -> LDS chunk 64i + l = row 8i + (l >> 3), position l & 7
+      const int r = lane >> 3, c = (lane & 7) ^ ((r >> 1) & 7);
+      const uint32_t o0 = (uint32_t)(r * 128 + c * 16);
+      const int r1 = 8 + (lane >> 3), c1 = (lane & 7) ^ ((r1 >> 1) & 7);
+      const uint32_t o1 = (uint32_t)(r1 * 128 + c1 * 16);
+      dma16(smp + o0, slot);
+      dma16(smp + o1, slot + 1024);
     }
-    return m;
-  }
-
-  // slot of block j of a row, or -1 when the block is compressed / out of the pool
-  __device__ __forceinline__ int64_t slot_of(uint32_t flags, uint32_t first, int j) const {
-    if (!((flags >> j) & 1u)) return -1;
-    const uint64_t slot = (uint64_t)first + __popc(flags & ((1u << j) - 1u));
-    return slot < spill_slots ? (int64_t)slot : -1;
-  }
-
-  __device__ __forceinline__ Bufs issue_bufs(int H, int64_t pid, int h, int lane, const Meta& m) const {
-    const int t = lane & 15, qd = lane >> 4, tv = lane & 7, g = lane >> 3;
-    Bufs b;
-    const int64_t krow = ((pid * H + h) * 2 + 0) * kT + t;
-    const uint4* kp = reinterpret_cast<const uint4*>(sm + krow * kD + qd * 32);
-    b.ks0 = kp[0];
-    b.ks1 = kp[1];
-    b.kn = *reinterpret_cast<const uint4*>(nib + krow * (kD / 2) + qd * 16);
-    b.kb = base[krow * 2 + (qd >> 1)];
-    const int64_t ks = slot_of(m.fk, m.sk, (h * 2 + 0) * 2 + (qd >> 1));
-    b.kraw = ks >= 0;
-    b.kh = *reinterpret_cast<const uint4*>(spill + (ks >= 0 ? ks * 32 + (qd & 1) * 16 : 0));
-    b.vmask = 0u;
-    uint32_t vh[4];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const int64_t vrow = ((pid * H + h) * 2 + 1) * kT + 8 * ps + tv;
-      b.vs[ps] = *reinterpret_cast<const uint4*>(sm + vrow * kD + g * 16);
-      b.vn[ps] = *reinterpret_cast<const uint2*>(nib + vrow * (kD / 2) + g * 8);
-      b.vb[ps] = base[vrow * 2 + (g >> 2)];
-      const int64_t vsl = slot_of(m.fv[ps], m.sv[ps], (h * 2 + 1) * 2 + (g >> 2));
-      b.vmask |= (uint32_t)(vsl >= 0) << ps;
-      const uint2 x = *reinterpret_cast<const uint2*>(spill + (vsl >= 0 ? vsl * 32 + (g & 3) * 8 : 0));
-      vh[2 * ps] = x.x;
-      vh[2 * ps + 1] = x.y;
+    {  // K nibbles: lane l -> row l >> 2, position l & 3
+      const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+      dma16(nbp + (uint32_t)(r * 64 + c * 16), slot + 4096);
     }
-    b.vh2 = make_uint4(vh[0], vh[1], vh[2], vh[3]);
-    return b;
+    {  // V sm: gather i, lane l -> reader lane 8i + (l >> 3), word l & 7
+      const uint32_t lo = (uint32_t)(((lane & 7) >> 1) * 128 + 8 * (lane >> 3) + 4 * (lane & 1));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma4(smp + 2048 + 512 * (i >> 1) + 64 * (i & 1) + lo, slot + 2048 + 256 * i);
+    }
+    {  // V nibbles: gather j, lane l -> reader lane 16j + (l >> 2), word l & 3
+      const uint32_t lo = (uint32_t)(64 * (lane & 3) + 4 * (lane >> 2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma4(nbp + 1024 + 256 * j + lo, slot + 5120 + 256 * j);
+    }
   }
 
-  __device__ __forceinline__ void rebuild(const Bufs& b, uint32_t kp[16], uint32_t vp[16]) const {
+  __device__ __forceinline__ void rebuild(int h, int lane, uint32_t slot, uint32_t ms, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
+    const int t = lane & 15, qd = lane >> 4;
+    const int sk = (t >> 1) & 7;
+    u32x4 ks0, ks1, kn, kh, vs0, vs1, vn, vh;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %12 offset:16\n\t"
+        "ds_read_b128 %6, %13\n\t"
+        "ds_read_b128 %7, %14\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(ks0), "=&v"(ks1), "=&v"(kn), "=&v"(kh), "=&v"(vs0), "=&v"(vs1), "=&v"(vn), "=&v"(vh)
+        : "v"(slot + t * 128 + ((2 * qd) ^ sk) * 16), "v"(slot + t * 128 + ((2 * qd + 1) ^ sk) * 16),
+          "v"(slot + 4096 + t * 64 + (qd ^ ((t >> 2) & 3)) * 16), "v"(slot + 6144 + lane * 16),
+          "v"(slot + 2048 + lane * 32), "v"(slot + 5120 + lane * 16), "v"(slot + 7168 + lane * 16)
+        : "memory");
+    uint32_t fk, kb;
+    u32x4 fv;
+    u32x2 vb;
+    asm volatile(
+        "ds_read_b32 %0, %4\n\t"
+        "ds_read_u8 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fk), "=&v"(kb), "=&v"(fv), "=&v"(vb)
+        : "v"(ms + 4 * t), "v"(ms + 128 + 2 * t + (qd >> 1)), "v"(ms + 16 * qd), "v"(ms + 160 + 8 * qd)
+        : "memory");
     {
-      const uint32_t bp = b.kraw ? 0u : b.kb * 0x00800080u;
-      const uint4 hi = b.kraw ? b.kh : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t smw[8] = {b.ks0.x, b.ks0.y, b.ks0.z, b.ks0.w, b.ks1.x, b.ks1.y, b.ks1.z, b.ks1.w};
-      const uint32_t nw[4] = {b.kn.x, b.kn.y, b.kn.z, b.kn.w};
-      const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
+      const bool kraw = (fk >> ((h * 2 + 0) * 2 + (qd >> 1))) & 1u;
+      const uint32_t bp = kraw ? 0u : kb * 0x00800080u;
+      const uint32_t smw[8] = {ks0.x, ks0.y, ks0.z, ks0.w, ks1.x, ks1.y, ks1.z, ks1.w};
+      const uint32_t nw[4] = {kn.x, kn.y, kn.z, kn.w};
+      const uint32_t hw[4] = {kraw ? kh.x : 0u, kraw ? kh.y : 0u, kraw ? kh.z : 0u, kraw ? kh.w : 0u};
 #pragma unroll
       for (int c = 0; c < 4; ++c) rebuild8(smw[2 * c], smw[2 * c + 1], nw[c], hw[c], bp, kp + 4 * c);
     }
-    const uint32_t vh[4] = {b.vh2.x, b.vh2.y, b.vh2.z, b.vh2.w};
+    uint32_t pr[4][4];
+    const int jv = (h * 2 + 1) * 2 + (t >> 3);
+    const uint32_t half = (uint32_t)(t >> 3);
+    const uint32_t vsw[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+    const uint32_t vna[4] = {vn.x, vn.y, vn.z, vn.w}, vha[4] = {vh.x, vh.y, vh.z, vh.w};
+    const uint32_t fva[4] = {fv.x, fv.y, fv.z, fv.w};
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const bool raw = (b.vmask >> ps) & 1u;
-      const uint32_t bp = raw ? 0u : b.vb[ps] * 0x00800080u;
-      const uint32_t smw[4] = {b.vs[ps].x, b.vs[ps].y, b.vs[ps].z, b.vs[ps].w};
-      const uint32_t nw[2] = {b.vn[ps].x, b.vn[ps].y};
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        rebuild8(smw[2 * c], smw[2 * c + 1], nw[c], raw ? vh[2 * ps + c] : 0u, bp, vp + 8 * ps + 4 * c);
+    for (int j = 0; j < 4; ++j) {
+      const bool raw = (fva[j] >> jv) & 1u;
+      const uint32_t word = j < 2 ? vb.x : vb.y;
+      const uint32_t bexp = (word >> (8 * (((2 * j) & 3) + half))) & 0xFFu;
+      const uint32_t bp = raw ? 0u : bexp * 0x00800080u;
+      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], raw ? vha[j] : 0u, bp, pr[j]);
     }
+    to_token_pairs(pr, vt);
   }
 };
 
+// Raw bf16 pages (the uncompressed twin): slot = K rows (256 B each, 16-byte chunk c of row r
+// at c ^ r) then V rows.
 struct RawLoader {
   const uint16_t* pages;
 
-  struct Meta {};
-  struct Bufs {
-    uint4 k[4];
-    uint4 v[2][2];
-  };
+  static constexpr int kMetaLoads = 0, kPageLoads = 8;
 
-  __device__ __forceinline__ Meta issue_meta(int64_t, int) const { return Meta{}; }
+  __device__ __forceinline__ void issue_meta(int64_t, int, int, int, uint32_t) const {}
 
-  __device__ __forceinline__ Bufs issue_bufs(int H, int64_t pid, int h, int lane, const Meta&) const {
-    const int t = lane & 15, qd = lane >> 4, tv = lane & 7, g = lane >> 3;
-    Bufs b;
-    const int64_t krow = ((pid * H + h) * 2 + 0) * kT + t;
-    const uint4* kp = reinterpret_cast<const uint4*>(pages + krow * kD + qd * 32);
+  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, uint32_t) const {
+    const uint8_t* pg = reinterpret_cast<const uint8_t*>(pages + ((pid * H + h) * 2) * kT * kD);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) b.k[c] = kp[c];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const int64_t vrow = ((pid * H + h) * 2 + 1) * kT + 8 * ps + tv;
-      const uint4* vp = reinterpret_cast<const uint4*>(pages + vrow * kD + g * 16);
-      b.v[ps][0] = vp[0];
-      b.v[ps][1] = vp[1];
+    for (int i = 0; i < 4; ++i) {  // gather i, lane l -> row 4i + (l >> 4), position l & 15
+      const int r = 4 * i + (lane >> 4), c = (lane & 15) ^ r;
+      dma16(pg + (uint32_t)(r * 256 + c * 16), slot + i * 1024);
     }
-    return b;
+#pragma unroll
+    for (int i = 4; i < 8; ++i) dma16(pg + (uint32_t)(i * 1024 + lane * 16), slot + i * 1024);
   }
 
-  __device__ __forceinline__ void rebuild(const Bufs& b, uint32_t kp[16], uint32_t vp[16]) const {
+  __device__ __forceinline__ void rebuild(int, int lane, uint32_t slot, uint32_t, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
+    const int t = lane & 15, qd = lane >> 4;
+    u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %12 offset:256\n\t"
+        "ds_read_b128 %6, %12 offset:512\n\t"
+        "ds_read_b128 %7, %12 offset:768\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(slot + t * 256 + ((4 * qd + 0) ^ t) * 16), "v"(slot + t * 256 + ((4 * qd + 1) ^ t) * 16),
+          "v"(slot + t * 256 + ((4 * qd + 2) ^ t) * 16), "v"(slot + t * 256 + ((4 * qd + 3) ^ t) * 16),
+          "v"(slot + 4096 + qd * 1024 + t * 16)
+        : "memory");
+    const u32x4 ka[4] = {k0, k1, k2, k3}, va[4] = {v0, v1, v2, v3};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t w[4] = {b.k[c].x, b.k[c].y, b.k[c].z, b.k[c].w};
+      const uint32_t w[4] = {ka[c].x, ka[c].y, ka[c].z, ka[c].w};
       natural_to_pairs(w, kp + 4 * c);
     }
+    uint32_t pr[4][4];
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint32_t w[4] = {b.v[ps][c].x, b.v[ps][c].y, b.v[ps][c].z, b.v[ps][c].w};
-        natural_to_pairs(w, vp + 8 * ps + 4 * c);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+      natural_to_pairs(w, pr[j]);
+    }
+    to_token_pairs(pr, vt);
   }
 };
 
 // ---------------------------------------------------------------- kernel
 
-__device__ __forceinline__ double row_max16(double v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmax(v, __shfl_xor(v, o, 16));
-  return v;
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
 }
+__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-__device__ __forceinline__ float row_sum16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 16);
-  return v;
-}
 
-// V accumulator slot j (0..15) of lane group g holds head_dim 16*g + 8*(j/8) + (j%8)/2 + 4*(j%2).
-__device__ __forceinline__ int vslot_dim(int g, int j) {
-  return 16 * g + 8 * (j >> 3) + ((j & 7) >> 1) + 4 * (j & 1);
-}
+// LDS per wave: two page slots and the meta ring; the end-of-split results reuse the wave's
+// own region once its loads have drained.
+constexpr uint32_t kWaveLds = 2 * kSlotBytes + kMetaRing * kMetaBytes;
+static_assert(kG * kD * sizeof(double) + 2 * kG * sizeof(double) <= kWaveLds, "results fit");
 
 template <class Loader>
-__global__ __launch_bounds__(kThreads, 2) void attn_k(AttnArgs a, Loader ld) {
+__global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t = lane & 15, qd = lane >> 4, tv = lane & 7, g = lane >> 3;
+  const int t = lane & 15, qd = lane >> 4;
+  const int head = t >> 2;  // query head of this lane's scores (and of its p.V A-operand row)
+  const int part = t & 3;   // which bf16 part of the weights this lane's A row carries
 
   int32_t L = a.lens[b];
   const int32_t cap = min(a.maxp * kT, a.max_seq_len);
@@ -235,22 +348,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_k(AttnArgs a, Loader ld) {
   const int nsplit = max(1, (npages + a.pps - 1) / a.pps);
   if (s >= nsplit) return;
 
-  // A operand: query head (lane & 15) & 3, head_dim 32*qd + 8c + (0,4,1,5,2,6,3,7)[k].
-  bf16x8 qa[4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
+  const uint32_t ring = (uint32_t)(uintptr_t)&s_ring[wave][0];
+  const uint32_t meta_ring = ring + 2 * kSlotBytes;
+
+  // B operand of the score MFMA: column t is query head t >> 2 (each head four times),
+  // head_dim 32*qd + 8c + (0,4,1,5,2,6,3,7)[k]
+  bf16x8 qb[4];
   {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.H * kG + h * kG + (t & 3)) * kD + qd * 32;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.H * kG + h * kG + head) * kD + qd * 32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 x = *reinterpret_cast<const uint4*>(qrow + 8 * c);
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
       uint32_t p[4];
       natural_to_pairs(w, p);
-      qa[c] = __builtin_bit_cast(bf16x8, (u32x4){p[0], p[1], p[2], p[3]});
+      qb[c] = __builtin_bit_cast(bf16x8, (u32x4){p[0], p[1], p[2], p[3]});
     }
   }
   // q in fp64, pair order, for the exact-score path: [head][quarter][pair] = (lo, hi) dims
   __shared__ double2 s_q64[kG][4][16];
-  {
+  if (tid < kG * 64) {
     const int i = tid >> 6, qq = (tid >> 4) & 3, k = tid & 15;
     const int dlo = 32 * qq + 8 * (k >> 2) + (k & 3);
     const uint16_t* qrow = a.q + ((int64_t)b * a.H * kG + h * kG + i) * kD;
@@ -273,46 +391,61 @@ __global__ __launch_bounds__(kThreads, 2) void attn_k(AttnArgs a, Loader ld) {
   }
   __syncthreads();
 
-  double m[kG];  // running max of the unscaled scores, fp64
-  float l[kG], acc[kG][16];
+  double m = -INFINITY;  // running max of head `head`'s unscaled scores (fp64)
+  double l = 0.0;        // this lane's share of head `head`'s weight sum (tokens 4qd..4qd+3)
+  // p.V output: lane (t, qd) receives rows 4qd..4qd+3 = the hi, mid, lo parts (and an empty
+  // fourth row) of head qd at head_dim vdim(n, t).  The parts of each page's MFMA (which
+  // starts from zero) are summed here in fp64: with outlier values the running sum reaches
+  // 1e4, where one fp32 rounding is already 5e-4.
+  double acc[8];
+  f32x4 cacc[8];  // the MFMA accumulators: rows 4qd + 1, 4qd + 2 carry mid and lo
 #pragma unroll
-  for (int i = 0; i < kG; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+  for (int n = 0; n < 8; ++n) {
+    acc[n] = 0.0;
+    cacc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const double c2 = a.scale_log2e;
+  double mc2 = 0.0;  // m * c2 once m is finite
 
+  // page n of this wave; indices past the end repeat the last page (their loads keep the
+  // per-page load count fixed and are never used)
   auto pid_at = [&](int n) -> int64_t {
-    const int32_t v = __builtin_amdgcn_readlane(my_pid, n);
+    const int32_t v = __builtin_amdgcn_readlane(my_pid, min(n, nmine - 1));
     return v < 0 ? 0 : v;
   };
   auto ntok_at = [&](int n) -> int {
     if (__builtin_amdgcn_readlane(my_pid, n) < 0) return 0;
     return min(kT, L - (p_first + kWaves * n) * kT);
   };
+  auto slot_of = [&](int n) -> uint32_t { return ring + (uint32_t)(n & 1) * kSlotBytes; };
+  auto meta_of = [&](int n) -> uint32_t { return meta_ring + (uint32_t)(n & (kMetaRing - 1)) * kMetaBytes; };
 
-  // One buffer slot per wave: page n is rebuilt into bf16 pairs first, which frees the slot
-  // for page n + 1's planes and spill loads; those stay in flight while page n's MFMA,
-  // softmax and p.V run.  Row metadata travels two pages ahead.  The last page is peeled so
-  // that the loop's loads are unconditional (no buffer copies between iterations).
-  auto compute = [&](const int n, const uint32_t (&kp)[16], const uint32_t (&vp)[16]) {
+  auto compute = [&](const int n, const uint32_t (&kp)[16], const uint32_t (&vt)[16]) {
     const int ntok = ntok_at(n);
-    const bool valid = t < ntok;
-
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8 kb = __builtin_bit_cast(bf16x8, (u32x4){kp[4 * c], kp[4 * c + 1], kp[4 * c + 2], kp[4 * c + 3]});
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, sc, 0, 0, 0);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, (u32x4){kp[4 * c], kp[4 * c + 1], kp[4 * c + 2], kp[4 * c + 3]});
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c], sc, 0, 0, 0);
     }
+    // sc[i]: token 4qd + i, head `head`; tokens past the end of the page count as -inf
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = 4 * qd + i < ntok ? sc[i] : -INFINITY;
+    float pm32 = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    pm32 = fmaxf(pm32, __shfl_xor(pm32, 16, 64));
+    pm32 = fmaxf(pm32, __shfl_xor(pm32, 32, 64));
+    // A score needs the exact path when it is large (one fp32 ulp of it is then a visible
+    // change of its weight) and its weight can matter: scores more than kNegligible / c2
+    // below the running maximum get a weight under 2^-kNegligible of the largest one.
+    const float floor32 = (float)(fmax(m, (double)pm32) - kNegligible / c2);
     bool big = false;
 #pragma unroll
-    for (int i = 0; i < kG; ++i) big |= valid && fabsf(sc[i]) > kBigScore;
-    double sd[kG];
+    for (int i = 0; i < 4; ++i) big |= fabsf(sc[i]) > kBigScore && sc[i] > floor32;
+    double sd[4];
     if (__any(big)) {
-      double part[kG] = {0.0, 0.0, 0.0, 0.0};
+      // exact fp64 scores: lane (t, qd) sums its 32 dims of token t for the 4 heads, the four
+      // quarters are added, and each lane then fetches its own (token, head) entries
+      double pd[kG] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const double klo = (double)__uint_as_float(kp[k] << 16);
@@ -320,139 +453,154 @@ __global__ __launch_bounds__(kThreads, 2) void attn_k(AttnArgs a, Loader ld) {
 #pragma unroll
         for (int i = 0; i < kG; ++i) {
           const double2 qq = s_q64[i][qd][k];
-          part[i] = fma(qq.x, klo, part[i]);
-          part[i] = fma(qq.y, khi, part[i]);
+          pd[i] = fma(qq.x, klo, pd[i]);
+          pd[i] = fma(qq.y, khi, pd[i]);
         }
       }
 #pragma unroll
       for (int i = 0; i < kG; ++i) {
-        part[i] += __shfl_xor(part[i], 16, 64);
-        part[i] += __shfl_xor(part[i], 32, 64);
-        sd[i] = valid ? part[i] : -INFINITY;
+        pd[i] += __shfl_xor(pd[i], 16, 64);
+        pd[i] += __shfl_xor(pd[i], 32, 64);
+      }
+      // lane (t', qd') offers head qd' of token t'; lane (t, qd) reads token 4qd + i, head t >> 2
+      const double offer = qd == 0 ? pd[0] : qd == 1 ? pd[1] : qd == 2 ? pd[2] : pd[3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double x = __shfl(offer, head * 16 + 4 * qd + i, 64);
+        sd[i] = 4 * qd + i < ntok ? x : -INFINITY;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kG; ++i) sd[i] = valid ? (double)sc[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) sd[i] = (double)sc[i];
     }
 
-    bool raise = false;
+    double pm = fmax(fmax(sd[0], sd[1]), fmax(sd[2], sd[3]));
+    pm = fmax(pm, __shfl_xor(pm, 16, 64));
+    pm = fmax(pm, __shfl_xor(pm, 32, 64));
+    if (__any(pm > m)) {
+      const double mn = fmax(m, pm);
+      const double alpha = exp2((m - mn) * c2);
+      m = mn;
+      mc2 = m * c2;
+      l *= alpha;
+      const double al = __shfl(alpha, 4 * qd, 64);  // acc holds head qd; lane 4qd has head qd
+      const float alf = (float)al;
 #pragma unroll
-    for (int i = 0; i < kG; ++i) raise |= sd[i] > m[i];
-    if (__any(raise)) {
-#pragma unroll
-      for (int i = 0; i < kG; ++i) {
-        const double mn = fmax(m[i], row_max16(sd[i]));
-        const float alpha = exp2f((float)((m[i] - mn) * c2));
-        m[i] = mn;
-        l[i] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+      for (int nn = 0; nn < 8; ++nn) {
+        acc[nn] *= al;
+        cacc[nn][1] *= alf;
+        cacc[nn][2] *= alf;
       }
     }
-    float pw[kG];
+    // weights 2^((s - m) c2); a page seen before any finite score leaves m = -inf and mc2 = 0
+    float p[4];
 #pragma unroll
-    for (int i = 0; i < kG; ++i) {
-      pw[i] = exp2f((float)((sd[i] - m[i]) * c2));
-      l[i] += pw[i];
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f((float)fma(sd[i], c2, -mc2));
+      l += p[i];
     }
-    // p.V: V lane (tv, g) needs the weights of token 8 * ps + tv (held by lane 8 * ps + tv)
+    // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo
+    uint32_t w[4];
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const bool vvalid = 8 * ps + tv < ntok;
-      float pv[kG];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t hi = bf16_bits(p[i]);
+      const float r1 = p[i] - bf16_value(hi);
+      const uint32_t mid = bf16_bits(r1);
+      const uint32_t lo = bf16_bits(r1 - bf16_value(mid));
+      w[i] = part == 0 ? hi : part == 1 ? mid : part == 2 ? lo : 0u;
+    }
+    const s16x4 pa = __builtin_bit_cast(s16x4, (u32x2){w[0] | (w[1] << 16), w[2] | (w[3] << 16)});
+    // rows 4qd + (0, 1, 2): hi, mid, lo parts of head qd.  The hi row restarts from zero on
+    // every page and is added in fp64; mid and lo (below 2^-8 of it) accumulate in the MFMA.
 #pragma unroll
-      for (int i = 0; i < kG; ++i) pv[i] = __shfl(pw[i], 8 * ps + tv, 64);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t x = vvalid ? vp[8 * ps + k] : 0u;
-        const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xFFFF0000u);
-#pragma unroll
-        for (int i = 0; i < kG; ++i) {
-          acc[i][2 * k] = fmaf(pv[i], lo, acc[i][2 * k]);
-          acc[i][2 * k + 1] = fmaf(pv[i], hi, acc[i][2 * k + 1]);
-        }
-      }
+    for (int nn = 0; nn < 8; ++nn) {
+      const s16x4 vb = __builtin_bit_cast(s16x4, (u32x2){vt[2 * nn], vt[2 * nn + 1]});
+      const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, cacc[nn], 0, 0, 0);
+      acc[nn] += (double)d[0];
+      cacc[nn] = d;
+      cacc[nn][0] = 0.f;
     }
   };
 
-  typename Loader::Meta meta_n1{};
-  typename Loader::Bufs buf{};
+  // Pipeline: page n sits in slot n & 1, its row metadata in meta slot n & 7.  Metadata goes
+  // out four pages ahead (the spill addresses of a page depend on it), planes and spill pieces
+  // two pages ahead; every step issues exactly one page's and one meta's worth of loads, so
+  // a fixed vmcnt finds page n (and meta n + 2) complete at the top of step n.
+  constexpr int kM = Loader::kMetaLoads, kP = Loader::kPageLoads;
   if (nmine > 0) {
-    const typename Loader::Meta meta0 = ld.issue_meta(pid_at(0), lane);
-    meta_n1 = ld.issue_meta(pid_at(min(1, nmine - 1)), lane);
-    buf = ld.issue_bufs(a.H, pid_at(0), h, lane, meta0);
-  }
-  for (int n = 0; n + 1 < nmine; ++n) {
-    uint32_t kp[16], vp[16];
-    ld.rebuild(buf, kp, vp);
-    buf = ld.issue_bufs(a.H, pid_at(n + 1), h, lane, meta_n1);
-    meta_n1 = ld.issue_meta(pid_at(min(n + 2, nmine - 1)), lane);
-    compute(n, kp, vp);
-  }
-  if (nmine > 0) {
-    uint32_t kp[16], vp[16];
-    ld.rebuild(buf, kp, vp);
-    compute(nmine - 1, kp, vp);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ld.issue_meta(pid_at(k), a.H, h, lane, meta_of(k));
+    wait_vm<3 * kM>();
+    ld.issue_page(pid_at(0), a.H, h, lane, slot_of(0), meta_of(0));
+    ld.issue_meta(pid_at(4), a.H, h, lane, meta_of(4));
+    wait_vm<3 * kM + kP>();
+    ld.issue_page(pid_at(1), a.H, h, lane, slot_of(1), meta_of(1));
+    ld.issue_meta(pid_at(5), a.H, h, lane, meta_of(5));
+    for (int n = 0; n < nmine; ++n) {
+      wait_vm<kP + kM>();
+      uint32_t kp[16], vt[16];
+      ld.rebuild(h, lane, slot_of(n), meta_of(n), kp, vt);
+      ld.issue_page(pid_at(n + 2), a.H, h, lane, slot_of(n), meta_of(n + 2));
+      ld.issue_meta(pid_at(n + 6), a.H, h, lane, meta_of(n + 6));
+      compute(n, kp, vt);
+    }
+    wait_vm<0>();  // the loads past the end still target this wave's LDS
   }
   if (err) set_status(a.status, err);
 
-  // ---- reduce over the 8 token lanes of each g: reduce-scatter, lane tv keeps [8tv, 8tv + 8)
-  float* flat = &acc[0][0];
+  // ---- per-wave results to the wave's own LDS region: lane (t, qd) holds head qd at
+  //      head_dim vdim(n, t)
 #pragma unroll
-  for (int step = 0; step < 3; ++step) {
-    const int half = 32 >> step, mask = 4 >> step;
-    const bool up = (tv & mask) != 0;
+  for (int nn = 0; nn < 8; ++nn) acc[nn] += (double)cacc[nn][1] + (double)cacc[nn][2];
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  double* w_acc = reinterpret_cast<double*>(&s_ring[wave][0]);  // [kG][kD], then m[kG], l[kG]
 #pragma unroll
-    for (int k = 0; k < half; ++k) {
-      const float send = up ? flat[k] : flat[k + half];
-      const float keep = up ? flat[k + half] : flat[k];
-      flat[k] = keep + __shfl_xor(send, mask, 8);
-    }
-  }
-  // flat[0..7] of lane (tv, g) = head tv / 2, V slots 8 * (tv % 2) + k
-  __shared__ float s_acc[kWaves][kG][kD];
-  __shared__ double s_m[kWaves][kG];
-  __shared__ float s_l[kWaves][kG];
-  {
-    const int i = tv >> 1;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s_acc[wave][i][vslot_dim(g, 8 * (tv & 1) + k)] = flat[k];
-  }
-#pragma unroll
-  for (int i = 0; i < kG; ++i) {
-    const float lt = row_sum16(l[i]);
-    if (lane == 0) {
-      s_m[wave][i] = m[i];
-      s_l[wave][i] = lt;
-    }
+  for (int nn = 0; nn < 8; ++nn) w_acc[qd * kD + vdim(nn, t)] = acc[nn];
+  if (lane < 16 && part == 0) {  // lane 4i holds head i
+    w_acc[kG * kD + head] = m;
+    w_acc[kG * kD + kG + head] = l;
   }
   __syncthreads();
 
-  // ---- merge the 4 waves, write this split's partial: acc[kG][kD] f32, l[kG] f32, m[kG] f64
+  // ---- merge the waves (fp64) into this split's partial acc[kG][kD], l[kG], m[kG], or with
+  //      a single split straight into the output
+  auto wres = [&](int w2) { return reinterpret_cast<const double*>(&s_ring[w2][0]); };
   const int64_t unit = (int64_t)b * a.H + h;
-  float* part = a.part + (unit * a.nsplit_max + s) * kPartFloats;
-  for (int e = tid; e < kG * kD; e += kThreads) {
-    const int i = e / kD, d = e % kD;
+  double* part_out = a.part + (unit * a.nsplit_max + s) * kPartDoubles;
+  __shared__ double s_f[kWaves][kG];
+  __shared__ double s_lsum[kG];
+  if (tid < kG) {
     double mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmax(mm, s_m[w][i]);
-    float sum = 0.f, lsum = 0.f;
+    for (int w2 = 0; w2 < kWaves; ++w2) mm = fmax(mm, wres(w2)[kG * kD + tid]);
+    double lsum = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = s_m[w][i] == -INFINITY ? 0.f : exp2f((float)((s_m[w][i] - mm) * c2));
-      sum = fmaf(f, s_acc[w][i][d], sum);
-      lsum = fmaf(f, s_l[w][i], lsum);
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      const double mw = wres(w2)[kG * kD + tid];
+      const double f = mw == -INFINITY ? 0.0 : exp2((mw - mm) * c2);
+      s_f[w2][tid] = f;
+      lsum += f * wres(w2)[kG * kD + kG + tid];
     }
-    part[i * kD + d] = sum;
-    if (d == 0) {
-      part[kG * kD + i] = lsum;
-      reinterpret_cast<double*>(part + kG * kD + kG)[i] = mm;
+    s_lsum[tid] = lsum;
+    if (!a.direct) {
+      part_out[kG * kD + tid] = lsum;
+      part_out[kG * kD + kG + tid] = mm;
     }
   }
-
+  __syncthreads();
+  for (int e = tid; e < kG * kD; e += kThreads) {
+    double sum = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) sum += s_f[w2][e / kD] * wres(w2)[e];
+    if (a.direct) {
+      const double lsum = s_lsum[e / kD];
+      a.out[((int64_t)b * a.H * kG + h * kG) * kD + e] = lsum > 0.0 ? (float)(sum / lsum) : 0.f;
+    } else {
+      part_out[e] = sum;
+    }
+  }
 }
-
-
 
 // Merges the split partials of one (sequence, kv head) in split order (a kernel of its own:
 // the launch boundary makes every split's partial visible without device-wide fences).
@@ -468,25 +616,25 @@ __global__ __launch_bounds__(kThreads) void combine_k(AttnArgs a) {
   const int npages = (L + kT - 1) / kT;
   const int nsplit = max(1, (npages + a.pps - 1) / a.pps);
   const int64_t unit = (int64_t)b * a.H + h;
-  const float* base = a.part + unit * a.nsplit_max * kPartFloats;
+  const double* base = a.part + unit * a.nsplit_max * kPartDoubles;
   const double c2 = a.scale_log2e;
   __shared__ double s_m[kMaxSplitsStaged][kG];
-  __shared__ float s_w[kMaxSplitsStaged][kG];
-  __shared__ float s_lsum[kG];
+  __shared__ double s_w[kMaxSplitsStaged][kG];
+  __shared__ double s_lsum[kG];
   for (int e = tid; e < nsplit * kG; e += kThreads) {
     const int x = e / kG, i = e % kG;
-    s_m[x][i] = reinterpret_cast<const double*>(base + x * kPartFloats + kG * kD + kG)[i];
-    s_w[x][i] = base[x * kPartFloats + kG * kD + i];  // l, turned into weights below
+    s_m[x][i] = base[x * kPartDoubles + kG * kD + kG + i];
+    s_w[x][i] = base[x * kPartDoubles + kG * kD + i];  // l, turned into weights below
   }
   __syncthreads();
   if (tid < kG) {
     const int i = tid;
     double mm = -INFINITY;
     for (int x = 0; x < nsplit; ++x) mm = fmax(mm, s_m[x][i]);
-    float lsum = 0.f;
+    double lsum = 0.0;
     for (int x = 0; x < nsplit; ++x) {
-      const float f = s_m[x][i] == -INFINITY ? 0.f : exp2f((float)((s_m[x][i] - mm) * c2));
-      lsum = fmaf(f, s_w[x][i], lsum);
+      const double f = s_m[x][i] == -INFINITY ? 0.0 : exp2((s_m[x][i] - mm) * c2);
+      lsum += f * s_w[x][i];
       s_w[x][i] = f;
     }
     s_lsum[i] = lsum;
@@ -494,11 +642,11 @@ __global__ __launch_bounds__(kThreads) void combine_k(AttnArgs a) {
   __syncthreads();
   for (int e = tid; e < kG * kD; e += kThreads) {
     const int i = e / kD, d = e % kD;
-    float sum = 0.f;
+    double sum = 0.0;
 #pragma unroll 8
-    for (int x = 0; x < nsplit; ++x) sum = fmaf(s_w[x][i], base[x * kPartFloats + i * kD + d], sum);
-    const float lsum = s_lsum[i];
-    a.out[((int64_t)b * a.H * kG + h * kG + i) * kD + d] = lsum > 0.f ? sum / lsum : 0.f;
+    for (int x = 0; x < nsplit; ++x) sum += s_w[x][i] * base[x * kPartDoubles + i * kD + d];
+    const double lsum = s_lsum[i];
+    a.out[((int64_t)b * a.H * kG + h * kG + i) * kD + d] = lsum > 0.0 ? (float)(sum / lsum) : 0.f;
   }
 }
 
@@ -518,20 +666,20 @@ static int env_pps() {
   return v;
 }
 
-// Pages per split: about 1024 workgroups (4 per CU on 256 CUs), at least 2 pages per
-// wave, at most 64 per wave, and splits of one sequence as equal as the multiple of 4 allows.
+// Pages per split: about one workgroup per CU (256), at least one page per wave, at most 64
+// per wave, and splits of one sequence as equal as the multiple of kWaves allows.
 static Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len) {
   const int maxpages = std::max(1, (max_seq_len + kT - 1) / kT);
   int pps = env_pps();
   if (pps == 0) {
     const int64_t units = std::max<int64_t>((int64_t)B * H, 1);
-    int64_t splits = std::max<int64_t>(1, (1024 + units - 1) / units);
-    splits = std::min<int64_t>(splits, (maxpages + 7) / 8);
+    int64_t splits = std::max<int64_t>(1, (256 + units - 1) / units);
+    splits = std::min<int64_t>(splits, (maxpages + kWaves - 1) / kWaves);
     splits = std::max<int64_t>(splits, 1);
     pps = (int)((maxpages + splits - 1) / splits);
   }
   pps = (pps + kWaves - 1) / kWaves * kWaves;
-  pps = std::min(std::max(pps, 8), kMaxPagesPerSplit);
+  pps = std::min(std::max(pps, kWaves), kMaxPagesPerSplit);
   if ((maxpages + pps - 1) / pps > kMaxSplitsStaged)  // very long sequences: fewer, longer splits
     pps = std::min(kMaxPagesPerSplit, ((maxpages + kMaxSplitsStaged - 1) / kMaxSplitsStaged + kWaves - 1) / kWaves * kWaves);
   return Plan{pps, (maxpages + pps - 1) / pps};
@@ -539,7 +687,7 @@ static Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len) {
 
 size_t attention_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
   Plan pl = make_plan(B, H, max_seq_len);
-  size_t part = (size_t)B * H * pl.nsplit_max * kPartFloats * sizeof(float);
+  size_t part = (size_t)B * H * pl.nsplit_max * kPartDoubles * sizeof(double);
   size_t cnt = (size_t)B * H * sizeof(uint32_t);
   return 256 + ((cnt + 255) / 256) * 256 + part;
 }
@@ -557,18 +705,18 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   a.pps = pl.pps;
   a.nsplit_max = pl.nsplit_max;
   a.num_pages = num_pages;
+  a.direct = pl.nsplit_max == 1;
   a.pt = q->page_table;
   a.lens = q->seq_lens;
   a.q = qv;
   a.scale_log2e = (double)scale * kLog2e;
   a.out = out;
   size_t cnt = (size_t)q->batch * H * sizeof(uint32_t);
-  a.counter = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 256);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + 256 + ((cnt + 255) / 256) * 256);
+  a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + 256 + ((cnt + 255) / 256) * 256);
   a.status = status;
   dim3 grid(pl.nsplit_max, H, q->batch);
   hipLaunchKernelGGL(attn_k<Loader>, grid, dim3(kThreads), 0, st, a, ld);
-  hipLaunchKernelGGL(combine_k, dim3(H, q->batch), dim3(kThreads), 0, st, a);
+  if (!a.direct) hipLaunchKernelGGL(combine_k, dim3(H, q->batch), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -576,7 +724,8 @@ hipError_t launch_attention_packed(const zf_cache* c, const zf_seqs* q, const ui
                                    float scale, float* out, void* ws, hipStream_t st) {
   // the spill address of a compressed block is never used, but it must be readable
   const uint8_t* spill = c->spill_slots > 0 ? c->spill : c->sm;
-  PackedLoader ld{c->sm, c->nib, c->base, c->row_flags, c->row_spill, spill, c->spill_slots};
+  const uint32_t max_slot = c->spill_slots > 0 ? (uint32_t)(c->spill_slots - 1) : 0u;  // < 2^32
+  PackedLoader ld{c->sm, c->nib, c->base, c->row_flags, c->row_spill, spill, max_slot};
   return launch(ld, c->num_pages, c->num_kv_heads, q, qv, scale, out, ws, c->status, st);
 }
 

@@ -128,7 +128,8 @@ zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw
  * seq_lens[b] == 0.  Workspace: zf_attention_workspace_bytes(...) bytes of device memory, any
  * contents (it holds per-split partials); calls sharing one workspace must not overlap.
  * Requires D == 128, page_size == 16, num_q_heads == 4 * H and max_seq_len <= 2^20 in this
- * version (ZF_EUNSUPPORTED otherwise).  Two kernel launches (split attention, split merge). */
+ * version (ZF_EUNSUPPORTED otherwise).  One kernel launch when max_seq_len fits one split per
+ * (sequence, kv head), else two (split attention, split merge). */
 zf_status zf_decode_attention(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* q,
                               int32_t num_q_heads, float scale, float* out, void* workspace,
                               size_t workspace_bytes, zf_stream_t stream);
