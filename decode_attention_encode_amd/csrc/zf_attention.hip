@@ -138,8 +138,11 @@ struct PackedLoader {
     const uint32_t* fl = row_flags + pid * kT;
     const uint32_t* sp = row_spill + pid * kT;
     const uint32_t* bs = reinterpret_cast<const uint32_t*>(base + ((pid * H + h) * 2) * kT * 2);
-    const uint32_t* g = grp == 0 ? fl + i : grp == 1 ? sp + rt : grp == 2 ? bs + i : fl + rt;
-    dma4(g, ms);
+    // branch-free pick of the lane's source (selects, not divergent code)
+    const uint64_t a0 = (uint64_t)(fl + (grp == 0 ? i : rt)), a1 = (uint64_t)(sp + rt), a2 = (uint64_t)(bs + i);
+    const uint64_t m1 = 0ull - (uint64_t)(grp == 1), m2 = 0ull - (uint64_t)(grp == 2);
+    const uint64_t g = (a0 & ~(m1 | m2)) | (a1 & m1) | (a2 & m2);
+    dma4(reinterpret_cast<const void*>(g), ms);
   }
 
   // spill piece of the block whose lower raw blocks are `below` in its row: slot = first +
@@ -150,21 +153,31 @@ struct PackedLoader {
     return piece + (uint64_t)slot * 32;
   }
 
-  // ms: this page's meta slot (already arrived)
-  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, uint32_t ms) const {
-    const int t = lane & 15, qd = lane >> 4;
-    uint32_t fk, sk;
-    u32x4 fv, sv;
+  // The row metadata issue_page needs, read from a meta slot ahead of time.
+  struct Issue {
+    uint32_t fk, sk;  // flags, first spill slot of row t
+    u32x4 fv, sv;     // the same for rows 4j + (lane & 3), j = 0..3
+  };
+
+  __device__ __forceinline__ Issue read_issue(int lane, uint32_t ms) const {
+    const int t = lane & 15;
+    Issue r;
     asm volatile(
         "ds_read_b32 %0, %4\n\t"
         "ds_read_b32 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
+        "ds_read_b128 %2, %6 offset:128\n\t"
+        "ds_read_b128 %3, %6\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(fk), "=&v"(sk), "=&v"(fv), "=&v"(sv)
-        : "v"(ms + 4 * t), "v"(ms + 64 + 4 * (4 * (t & 3) + (t >> 2))),
-          "v"(ms + 192 + 16 * (lane & 3)), "v"(ms + 64 + 16 * (lane & 3))
+        : "=&v"(r.fk), "=&v"(r.sk), "=&v"(r.fv), "=&v"(r.sv)
+        : "v"(ms + 4 * t), "v"(ms + 64 + 4 * (4 * (t & 3) + (t >> 2))), "v"(ms + 64 + 16 * (lane & 3))
         : "memory");
+    return r;
+  }
+
+  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue& m) const {
+    const int t = lane & 15, qd = lane >> 4;
+    const uint32_t fk = m.fk, sk = m.sk;
+    const u32x4 fv = m.fv, sv = m.sv;
     // K: lane (t, qd) takes half qd & 1 of block (h, K, qd >> 1) of row t
     const int jk = (h * 2 + 0) * 2 + (qd >> 1);
     dma16(spill_at(fk & ((1u << jk) - 1u), sk, spill + (qd & 1) * 16), slot + 6144);
@@ -204,59 +217,74 @@ struct PackedLoader {
     }
   }
 
-  __device__ __forceinline__ void rebuild(int h, int lane, uint32_t slot, uint32_t ms, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
+  // One page's bytes as this lane needs them (read from LDS in one go).
+  struct Page {
+    u32x4 ks0, ks1, kn, kh, vs0, vs1, vn, vh, fv;
+    uint32_t fk, kb;
+    u32x2 vb;
+  };
+
+  // page n from its slot and meta slot ms, plus the issue metadata of a later page from ms2
+  __device__ __forceinline__ Page read(int lane, uint32_t slot, uint32_t ms, uint32_t ms2, Issue& next) const {
     const int t = lane & 15, qd = lane >> 4;
     const int sk = (t >> 1) & 7;
-    u32x4 ks0, ks1, kn, kh, vs0, vs1, vn, vh;
+    Page p;
     asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %12 offset:16\n\t"
-        "ds_read_b128 %6, %13\n\t"
-        "ds_read_b128 %7, %14\n\t"
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %17\n\t"
+        "ds_read_b128 %2, %18\n\t"
+        "ds_read_b128 %3, %19 offset:1024\n\t"
+        "ds_read_b128 %4, %20\n\t"
+        "ds_read_b128 %5, %20 offset:16\n\t"
+        "ds_read_b128 %6, %19\n\t"
+        "ds_read_b128 %7, %19 offset:2048\n\t"
+        "ds_read_b128 %8, %21\n\t"
+        "ds_read_b32 %9, %22\n\t"
+        "ds_read_u8 %10, %23\n\t"
+        "ds_read_b64 %11, %24\n\t"
+        "ds_read_b32 %12, %25\n\t"
+        "ds_read_b32 %13, %26\n\t"
+        "ds_read_b128 %14, %27 offset:128\n\t"
+        "ds_read_b128 %15, %27\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(ks0), "=&v"(ks1), "=&v"(kn), "=&v"(kh), "=&v"(vs0), "=&v"(vs1), "=&v"(vn), "=&v"(vh)
+        : "=&v"(p.ks0), "=&v"(p.ks1), "=&v"(p.kn), "=&v"(p.kh), "=&v"(p.vs0), "=&v"(p.vs1),
+          "=&v"(p.vn), "=&v"(p.vh), "=&v"(p.fv), "=&v"(p.fk), "=&v"(p.kb), "=&v"(p.vb),
+          "=&v"(next.fk), "=&v"(next.sk), "=&v"(next.fv), "=&v"(next.sv)
         : "v"(slot + t * 128 + ((2 * qd) ^ sk) * 16), "v"(slot + t * 128 + ((2 * qd + 1) ^ sk) * 16),
-          "v"(slot + 4096 + t * 64 + (qd ^ ((t >> 2) & 3)) * 16), "v"(slot + 6144 + lane * 16),
-          "v"(slot + 2048 + lane * 32), "v"(slot + 5120 + lane * 16), "v"(slot + 7168 + lane * 16)
+          "v"(slot + 4096 + t * 64 + (qd ^ ((t >> 2) & 3)) * 16), "v"(slot + 5120 + lane * 16),
+          "v"(slot + 2048 + lane * 32), "v"(ms + 16 * qd), "v"(ms + 4 * t),
+          "v"(ms + 128 + 2 * t + (qd >> 1)), "v"(ms + 160 + 8 * qd), "v"(ms2 + 4 * t),
+          "v"(ms2 + 64 + 4 * (4 * (t & 3) + (t >> 2))), "v"(ms2 + 64 + 16 * (lane & 3))
         : "memory");
-    uint32_t fk, kb;
-    u32x4 fv;
-    u32x2 vb;
-    asm volatile(
-        "ds_read_b32 %0, %4\n\t"
-        "ds_read_u8 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b64 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(fk), "=&v"(kb), "=&v"(fv), "=&v"(vb)
-        : "v"(ms + 4 * t), "v"(ms + 128 + 2 * t + (qd >> 1)), "v"(ms + 16 * qd), "v"(ms + 160 + 8 * qd)
-        : "memory");
+    return p;
+  }
+
+  __device__ __forceinline__ void rebuild(const Page& p, int h, int lane, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
+    const int t = lane & 15, qd = lane >> 4;
     {
-      const bool kraw = (fk >> ((h * 2 + 0) * 2 + (qd >> 1))) & 1u;
-      const uint32_t bp = kraw ? 0u : kb * 0x00800080u;
-      const uint32_t smw[8] = {ks0.x, ks0.y, ks0.z, ks0.w, ks1.x, ks1.y, ks1.z, ks1.w};
-      const uint32_t nw[4] = {kn.x, kn.y, kn.z, kn.w};
-      const uint32_t hw[4] = {kraw ? kh.x : 0u, kraw ? kh.y : 0u, kraw ? kh.z : 0u, kraw ? kh.w : 0u};
+      // raw block: base 0 and the spill piece; compressed: the base and no high nibbles
+      const uint32_t kraw = (p.fk >> ((h * 2 + 0) * 2 + (qd >> 1))) & 1u;
+      const uint32_t bp = (p.kb * 0x00800080u) & (kraw - 1u);
+      const uint32_t hm = 0u - kraw;
+      const uint32_t smw[8] = {p.ks0.x, p.ks0.y, p.ks0.z, p.ks0.w, p.ks1.x, p.ks1.y, p.ks1.z, p.ks1.w};
+      const uint32_t nw[4] = {p.kn.x, p.kn.y, p.kn.z, p.kn.w};
+      const uint32_t hw[4] = {p.kh.x & hm, p.kh.y & hm, p.kh.z & hm, p.kh.w & hm};
 #pragma unroll
       for (int c = 0; c < 4; ++c) rebuild8(smw[2 * c], smw[2 * c + 1], nw[c], hw[c], bp, kp + 4 * c);
     }
     uint32_t pr[4][4];
     const int jv = (h * 2 + 1) * 2 + (t >> 3);
     const uint32_t half = (uint32_t)(t >> 3);
-    const uint32_t vsw[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
-    const uint32_t vna[4] = {vn.x, vn.y, vn.z, vn.w}, vha[4] = {vh.x, vh.y, vh.z, vh.w};
-    const uint32_t fva[4] = {fv.x, fv.y, fv.z, fv.w};
+    const uint32_t vsw[8] = {p.vs0.x, p.vs0.y, p.vs0.z, p.vs0.w, p.vs1.x, p.vs1.y, p.vs1.z, p.vs1.w};
+    const uint32_t vna[4] = {p.vn.x, p.vn.y, p.vn.z, p.vn.w}, vha[4] = {p.vh.x, p.vh.y, p.vh.z, p.vh.w};
+    const uint32_t fva[4] = {p.fv.x, p.fv.y, p.fv.z, p.fv.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool raw = (fva[j] >> jv) & 1u;
-      const uint32_t word = j < 2 ? vb.x : vb.y;
+      const uint32_t raw = (fva[j] >> jv) & 1u;
+      const uint32_t word = j < 2 ? p.vb.x : p.vb.y;
       const uint32_t bexp = (word >> (8 * (((2 * j) & 3) + half))) & 0xFFu;
-      const uint32_t bp = raw ? 0u : bexp * 0x00800080u;
-      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], raw ? vha[j] : 0u, bp, pr[j]);
+      const uint32_t bp = (bexp * 0x00800080u) & (raw - 1u);
+      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], vha[j] & (0u - raw), bp, pr[j]);
     }
     to_token_pairs(pr, vt);
   }
@@ -269,9 +297,11 @@ struct RawLoader {
 
   static constexpr int kMetaLoads = 0, kPageLoads = 8;
 
+  struct Issue {};
+  __device__ __forceinline__ Issue read_issue(int, uint32_t) const { return Issue{}; }
   __device__ __forceinline__ void issue_meta(int64_t, int, int, int, uint32_t) const {}
 
-  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, uint32_t) const {
+  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue&) const {
     const uint8_t* pg = reinterpret_cast<const uint8_t*>(pages + ((pid * H + h) * 2) * kT * kD);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // gather i, lane l -> row 4i + (l >> 4), position l & 15
@@ -282,9 +312,13 @@ struct RawLoader {
     for (int i = 4; i < 8; ++i) dma16(pg + (uint32_t)(i * 1024 + lane * 16), slot + i * 1024);
   }
 
-  __device__ __forceinline__ void rebuild(int, int lane, uint32_t slot, uint32_t, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
+  struct Page {
+    u32x4 k[4], v[4];
+  };
+
+  __device__ __forceinline__ Page read(int lane, uint32_t slot, uint32_t, uint32_t, Issue&) const {
     const int t = lane & 15, qd = lane >> 4;
-    u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
+    Page p;
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
         "ds_read_b128 %1, %9\n\t"
@@ -295,21 +329,25 @@ struct RawLoader {
         "ds_read_b128 %6, %12 offset:512\n\t"
         "ds_read_b128 %7, %12 offset:768\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "=&v"(p.k[0]), "=&v"(p.k[1]), "=&v"(p.k[2]), "=&v"(p.k[3]), "=&v"(p.v[0]), "=&v"(p.v[1]),
+          "=&v"(p.v[2]), "=&v"(p.v[3])
         : "v"(slot + t * 256 + ((4 * qd + 0) ^ t) * 16), "v"(slot + t * 256 + ((4 * qd + 1) ^ t) * 16),
           "v"(slot + t * 256 + ((4 * qd + 2) ^ t) * 16), "v"(slot + t * 256 + ((4 * qd + 3) ^ t) * 16),
           "v"(slot + 4096 + qd * 1024 + t * 16)
         : "memory");
-    const u32x4 ka[4] = {k0, k1, k2, k3}, va[4] = {v0, v1, v2, v3};
+    return p;
+  }
+
+  __device__ __forceinline__ void rebuild(const Page& p, int, int, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t w[4] = {ka[c].x, ka[c].y, ka[c].z, ka[c].w};
+      const uint32_t w[4] = {p.k[c].x, p.k[c].y, p.k[c].z, p.k[c].w};
       natural_to_pairs(w, kp + 4 * c);
     }
     uint32_t pr[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+      const uint32_t w[4] = {p.v[j].x, p.v[j].y, p.v[j].z, p.v[j].w};
       natural_to_pairs(w, pr[j]);
     }
     to_token_pairs(pr, vt);
@@ -317,6 +355,42 @@ struct RawLoader {
 };
 
 // ---------------------------------------------------------------- kernel
+
+// Reductions across the four 16-lane rows of a wave64 without going through LDS, on gfx950's
+// permlane swaps: a swap of v with itself leaves {v[l], v[l ^ 16]} (permlane16) or
+// {v[l], v[l ^ 32]} (permlane32) in its two results, in a lane-dependent order that symmetric
+// reductions (max, sum) never need to resolve.
+// The two doubles {v[l], v[l ^ 16]} (or ^ 32) of a lane: both halves are swapped the same way,
+// so the pairs stay whole.
+template <bool k32>
+__device__ __forceinline__ void pair_d(double v, double& a, double& b) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  const auto l = k32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false) : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = k32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false) : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  a = __longlong_as_double((int64_t)(((uint64_t)h[0] << 32) | l[0]));
+  b = __longlong_as_double((int64_t)(((uint64_t)h[1] << 32) | l[1]));
+}
+// max / sum over the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48) of a double
+__device__ __forceinline__ double rows_max_d(double v) {
+  double a, b;
+  pair_d<false>(v, a, b);
+  pair_d<true>(fmax(a, b), a, b);
+  return fmax(a, b);
+}
+__device__ __forceinline__ double rows_sum_d(double v) {
+  double a, b;
+  pair_d<false>(v, a, b);
+  pair_d<true>(a + b, a, b);
+  return a + b;
+}
+// max over the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48) of a float
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
@@ -337,6 +411,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const int t = lane & 15, qd = lane >> 4;
   const int head = t >> 2;  // query head of this lane's scores (and of its p.V A-operand row)
   const int part = t & 3;   // which bf16 part of the weights this lane's A row carries
+  const float k0 = part == 0 ? 1.f : 0.f, k1 = part == 1 ? 1.f : 0.f, k2 = part == 2 ? 1.f : 0.f;
+  const uint32_t wmask = part == 3 ? 0u : 0xFFFFu;
 
   int32_t L = a.lens[b];
   const int32_t cap = min(a.maxp * kT, a.max_seq_len);
@@ -389,6 +465,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       my_pid = -1;  // page skipped: read page 0, count no token
     }
   }
+  // pin the q unpacking here: placed after the first page loads, its wait for q would also
+  // wait for them
+  asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
   __syncthreads();
 
   double m = -INFINITY;  // running max of head `head`'s unscaled scores (fp64)
@@ -429,11 +508,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c], sc, 0, 0, 0);
     }
     // sc[i]: token 4qd + i, head `head`; tokens past the end of the page count as -inf
+    if (ntok < kT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = 4 * qd + i < ntok ? sc[i] : -INFINITY;
-    float pm32 = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    pm32 = fmaxf(pm32, __shfl_xor(pm32, 16, 64));
-    pm32 = fmaxf(pm32, __shfl_xor(pm32, 32, 64));
+      for (int i = 0; i < 4; ++i) sc[i] = 4 * qd + i < ntok ? sc[i] : -INFINITY;
+    }
+    const float pm32 = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     // A score needs the exact path when it is large (one fp32 ulp of it is then a visible
     // change of its weight) and its weight can matter: scores more than kNegligible / c2
     // below the running maximum get a weight under 2^-kNegligible of the largest one.
@@ -459,15 +538,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       }
 #pragma unroll
       for (int i = 0; i < kG; ++i) {
-        pd[i] += __shfl_xor(pd[i], 16, 64);
-        pd[i] += __shfl_xor(pd[i], 32, 64);
+        pd[i] = rows_sum_d(pd[i]);
       }
       // lane (t', qd') offers head qd' of token t'; lane (t, qd) reads token 4qd + i, head t >> 2
       const double offer = qd == 0 ? pd[0] : qd == 1 ? pd[1] : qd == 2 ? pd[2] : pd[3];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const double x = __shfl(offer, head * 16 + 4 * qd + i, 64);
-        sd[i] = 4 * qd + i < ntok ? x : -INFINITY;
+        sd[i] = sc[i] == -INFINITY ? -INFINITY : x;  // keeps the tokens past the end out
       }
     } else {
 #pragma unroll
@@ -475,8 +553,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     }
 
     double pm = fmax(fmax(sd[0], sd[1]), fmax(sd[2], sd[3]));
-    pm = fmax(pm, __shfl_xor(pm, 16, 64));
-    pm = fmax(pm, __shfl_xor(pm, 32, 64));
+    pm = rows_max_d(pm);
     if (__any(pm > m)) {
       const double mn = fmax(m, pm);
       const double alpha = exp2((m - mn) * c2);
@@ -499,15 +576,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       p[i] = __builtin_amdgcn_exp2f((float)fma(sd[i], c2, -mc2));
       l += p[i];
     }
-    // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo
+    // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo:
+    // x0 = p, x1 = p - bf16(p), x2 = x1 - bf16(x1); row part takes bf16(x_part) (row 3: 0)
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t hi = bf16_bits(p[i]);
-      const float r1 = p[i] - bf16_value(hi);
-      const uint32_t mid = bf16_bits(r1);
-      const uint32_t lo = bf16_bits(r1 - bf16_value(mid));
-      w[i] = part == 0 ? hi : part == 1 ? mid : part == 2 ? lo : 0u;
+      const float x1 = p[i] - bf16_value(bf16_bits(p[i]));
+      const float x2 = x1 - bf16_value(bf16_bits(x1));
+      // exact selection by 0/1 factors (p, x1, x2 are finite), no divergent code
+      const float x = fmaf(x2, k2, fmaf(x1, k1, p[i] * k0));
+      w[i] = bf16_bits(x) & wmask;
     }
     const s16x4 pa = __builtin_bit_cast(s16x4, (u32x2){w[0] | (w[1] << 16), w[2] | (w[3] << 16)});
     // rows 4qd + (0, 1, 2): hi, mid, lo parts of head qd.  The hi row restarts from zero on
@@ -522,26 +600,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     }
   };
 
-  // Pipeline: page n sits in slot n & 1, its row metadata in meta slot n & 7.  Metadata goes
-  // out four pages ahead (the spill addresses of a page depend on it), planes and spill pieces
-  // two pages ahead; every step issues exactly one page's and one meta's worth of loads, so
-  // a fixed vmcnt finds page n (and meta n + 2) complete at the top of step n.
+  // Pipeline: page n sits in slot n & 1, its row metadata in meta slot n & 7.  Step n issues
+  // page n + 2 (planes and spill pieces; the spill addresses come from its metadata, read one
+  // step earlier) and the metadata of page n + 6.  Every step issues exactly one page's and one
+  // meta's worth of loads, so a fixed vmcnt finds everything of step n - 2 and earlier landed
+  // at the top of step n.
   constexpr int kM = Loader::kMetaLoads, kP = Loader::kPageLoads;
   if (nmine > 0) {
+    // virtual steps -6 .. -1 of the loop below: metas 0..5, pages 0 and 1
 #pragma unroll
     for (int k = 0; k < 4; ++k) ld.issue_meta(pid_at(k), a.H, h, lane, meta_of(k));
     wait_vm<3 * kM>();
-    ld.issue_page(pid_at(0), a.H, h, lane, slot_of(0), meta_of(0));
+    ld.issue_page(pid_at(0), a.H, h, lane, slot_of(0), ld.read_issue(lane, meta_of(0)));
     ld.issue_meta(pid_at(4), a.H, h, lane, meta_of(4));
-    wait_vm<3 * kM + kP>();
-    ld.issue_page(pid_at(1), a.H, h, lane, slot_of(1), meta_of(1));
+    wait_vm<kP + 2 * kM>();
+    ld.issue_page(pid_at(1), a.H, h, lane, slot_of(1), ld.read_issue(lane, meta_of(1)));
+    typename Loader::Issue next = ld.read_issue(lane, meta_of(2));
     ld.issue_meta(pid_at(5), a.H, h, lane, meta_of(5));
     for (int n = 0; n < nmine; ++n) {
+      // every load of step n - 2 and earlier has landed: page n, metas up to n + 4
       wait_vm<kP + kM>();
-      uint32_t kp[16], vt[16];
-      ld.rebuild(h, lane, slot_of(n), meta_of(n), kp, vt);
-      ld.issue_page(pid_at(n + 2), a.H, h, lane, slot_of(n), meta_of(n + 2));
+      // page n leaves its slot (LDS -> VGPRs) together with the issue metadata of page n + 3;
+      // page n + 2's loads then go into the freed slot and the rebuild runs while they fly
+      const typename Loader::Issue cur = next;
+      const typename Loader::Page pg = ld.read(lane, slot_of(n), meta_of(n), meta_of(n + 3), next);
+      ld.issue_page(pid_at(n + 2), a.H, h, lane, slot_of(n), cur);
       ld.issue_meta(pid_at(n + 6), a.H, h, lane, meta_of(n + 6));
+      uint32_t kp[16], vt[16];
+      ld.rebuild(pg, h, lane, kp, vt);
       compute(n, kp, vt);
     }
     wait_vm<0>();  // the loads past the end still target this wave's LDS
@@ -552,8 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   //      head_dim vdim(n, t)
 #pragma unroll
   for (int nn = 0; nn < 8; ++nn) acc[nn] += (double)cacc[nn][1] + (double)cacc[nn][2];
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = rows_sum_d(l);
   double* w_acc = reinterpret_cast<double*>(&s_ring[wave][0]);  // [kG][kD], then m[kG], l[kG]
 #pragma unroll
   for (int nn = 0; nn < 8; ++nn) w_acc[qd * kD + vdim(nn, t)] = acc[nn];
