@@ -80,6 +80,18 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)(uintptr_t)lds, 4, 0, 0);
 }
+// The same through a buffer resource: LDS dest = lds + lane * size, global = resource base +
+// voff + soff (soff moves the global address only); reads outside the resource return zeros.
+constexpr int32_t kRawBufferWord3 = 0x00020000;  // 32-bit data format, no swizzle (gfx9 raw buffer)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ void dmab16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dmab4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds, 4, voff, soff, 0, 0);
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -189,31 +201,29 @@ struct PackedLoader {
     dma4(spill_at(fv.y & vmask, sv.y, vpiece), slot + 7168 + 256);
     dma4(spill_at(fv.z & vmask, sv.z, vpiece), slot + 7168 + 512);
     dma4(spill_at(fv.w & vmask, sv.w, vpiece), slot + 7168 + 768);
+    // the planes of (page, h): sm of K rows then V rows (4 KB), nibbles likewise (2 KB)
     const int64_t row0 = ((pid * H + h) * 2) * kT;  // K row 0 of the page
-    const uint8_t* smp = sm + row0 * kD;
-    const uint8_t* nbp = nib + row0 * (kD / 2);
+    const __amdgpu_buffer_rsrc_t smr = buffer_of(sm + row0 * kD, 2 * kT * kD);
+    const __amdgpu_buffer_rsrc_t nbr = buffer_of(nib + row0 * (kD / 2), 2 * kT * (kD / 2));
     {  // K sm: gather i, lane l -> LDS chunk 64i + l = row 8i + (l >> 3), position l & 7
       const int r = lane >> 3, c = (lane & 7) ^ ((r >> 1) & 7);
-      const uint32_t o0 = (uint32_t)(r * 128 + c * 16);
       const int r1 = 8 + (lane >> 3), c1 = (lane & 7) ^ ((r1 >> 1) & 7);
-      const uint32_t o1 = (uint32_t)(r1 * 128 + c1 * 16);
-      dma16(smp + o0, slot);
-      dma16(smp + o1, slot + 1024);
+      dmab16(smr, slot, (uint32_t)(r * 128 + c * 16), 0);
+      dmab16(smr, slot + 1024, (uint32_t)(r1 * 128 + c1 * 16), 0);
     }
     {  // K nibbles: lane l -> row l >> 2, position l & 3
       const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
-      dma16(nbp + (uint32_t)(r * 64 + c * 16), slot + 4096);
+      dmab16(nbr, slot + 4096, (uint32_t)(r * 64 + c * 16), 0);
     }
     {  // V sm: gather i, lane l -> reader lane 8i + (l >> 3), word l & 7
       const uint32_t lo = (uint32_t)(((lane & 7) >> 1) * 128 + 8 * (lane >> 3) + 4 * (lane & 1));
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma4(smp + 2048 + 512 * (i >> 1) + 64 * (i & 1) + lo, slot + 2048 + 256 * i);
+      for (int i = 0; i < 8; ++i) dmab4(smr, slot + 2048 + 256 * i, lo, 2048 + 512 * (i >> 1) + 64 * (i & 1));
     }
     {  // V nibbles: gather j, lane l -> reader lane 16j + (l >> 2), word l & 3
       const uint32_t lo = (uint32_t)(64 * (lane & 3) + 4 * (lane >> 2));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma4(nbp + 1024 + 256 * j + lo, slot + 5120 + 256 * j);
+      for (int j = 0; j < 4; ++j) dmab4(nbr, slot + 5120 + 256 * j, lo, 1024 + 256 * j);
     }
   }
 
@@ -302,14 +312,14 @@ struct RawLoader {
   __device__ __forceinline__ void issue_meta(int64_t, int, int, int, uint32_t) const {}
 
   __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue&) const {
-    const uint8_t* pg = reinterpret_cast<const uint8_t*>(pages + ((pid * H + h) * 2) * kT * kD);
+    const __amdgpu_buffer_rsrc_t pr = buffer_of(pages + ((pid * H + h) * 2) * kT * kD, 2 * kT * kD * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // gather i, lane l -> row 4i + (l >> 4), position l & 15
       const int r = 4 * i + (lane >> 4), c = (lane & 15) ^ r;
-      dma16(pg + (uint32_t)(r * 256 + c * 16), slot + i * 1024);
+      dmab16(pr, slot + i * 1024, (uint32_t)(r * 256 + c * 16), 0);
     }
 #pragma unroll
-    for (int i = 4; i < 8; ++i) dma16(pg + (uint32_t)(i * 1024 + lane * 16), slot + i * 1024);
+    for (int i = 4; i < 8; ++i) dmab16(pr, slot + i * 1024, (uint32_t)(lane * 16), i * 1024);
   }
 
   struct Page {
