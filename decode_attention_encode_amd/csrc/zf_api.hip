@@ -73,6 +73,7 @@ zf_status check_attention_shape(int32_t T, int32_t H, int32_t D, int32_t Hq) {
 
 // Longest sequence the split plan covers: 256 splits of at most 256 pages of 16 tokens.
 constexpr int32_t kMaxAttentionLen = 256 * 256 * 16;
+constexpr uint64_t kMaxAttentionSpillSlots = ((uint64_t)1 << 32) / 32 - 1;  // 32-bit byte offsets
 
 }  // namespace
 
@@ -164,6 +165,8 @@ zf_status zf_decode_attention(const zf_cache* cache, const zf_seqs* seqs, const 
   if ((s = check_attention_shape(cache->page_size, cache->num_kv_heads, cache->head_dim,
                                  num_q_heads)) != ZF_OK)
     return s;
+  // the kernel addresses the spill pool with 32-bit byte offsets
+  if (cache->spill_slots > kMaxAttentionSpillSlots) return ZF_EUNSUPPORTED;
   if (seqs->batch == 0) return ZF_OK;
   if ((s = check_attention_io(seqs, cache->num_kv_heads, cache->head_dim, q, num_q_heads, out,
                               workspace, workspace_bytes)) != ZF_OK)

@@ -92,6 +92,16 @@ __device__ __forceinline__ void dmab16(__amdgpu_buffer_rsrc_t r, uint32_t lds, u
 __device__ __forceinline__ void dmab4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds, 4, voff, soff, 0, 0);
 }
+// Progress of the waves of a workgroup, for the pair balancing below (LDS, asm so that the
+// compiler does not fence these accesses against the page loads in flight).
+__device__ __forceinline__ void lds_store_u32(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_load_u32(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+  return v;
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -139,8 +149,8 @@ struct PackedLoader {
   const uint8_t* base;
   const uint32_t* row_flags;
   const uint32_t* row_spill;
-  const uint8_t* spill;  // a readable address even when spill_slots == 0
-  uint32_t max_slot;     // last usable spill slot (0 when the pool is empty)
+  const uint8_t* spill;  // a valid address even when the pool is empty
+  uint32_t spill_bytes;  // spill_slots * 32 (below 2^32)
 
   static constexpr int kMetaLoads = 1, kPageLoads = 20;
 
@@ -157,12 +167,12 @@ struct PackedLoader {
     dma4(reinterpret_cast<const void*>(g), ms);
   }
 
-  // spill piece of the block whose lower raw blocks are `below` in its row: slot = first +
-  // popcount(below); clamped into the pool so that no metadata can address outside it (a
-  // compressed block loads a piece that is never used)
-  __device__ __forceinline__ const uint8_t* spill_at(uint32_t below, uint32_t first, const uint8_t* piece) const {
-    const uint32_t slot = min((uint32_t)__popc(below) + first, max_slot);
-    return piece + (uint64_t)slot * 32;
+  // Byte offset of a spill piece in the pool: slot = first + popcount(lower raw blocks of the
+  // row).  A compressed block gets an offset past the end, so its lanes load zeros; raw
+  // blocks carry base 0.  The rebuild then needs no raw flag at all.
+  __device__ __forceinline__ uint32_t spill_off(uint32_t flags, uint32_t first, int j, uint32_t piece) const {
+    const uint32_t slot = (uint32_t)__popc(flags & ((1u << j) - 1u)) + first;
+    return ((flags >> j) & 1u) ? slot * 32u + piece : 0xFFFFFFFFu;
   }
 
   // The row metadata issue_page needs, read from a meta slot ahead of time.
@@ -190,17 +200,17 @@ struct PackedLoader {
     const int t = lane & 15, qd = lane >> 4;
     const uint32_t fk = m.fk, sk = m.sk;
     const u32x4 fv = m.fv, sv = m.sv;
+    // the spill pool as a bounds-checked buffer: offsets past its end read zeros
+    const __amdgpu_buffer_rsrc_t spr = buffer_of(spill, spill_bytes);
     // K: lane (t, qd) takes half qd & 1 of block (h, K, qd >> 1) of row t
-    const int jk = (h * 2 + 0) * 2 + (qd >> 1);
-    dma16(spill_at(fk & ((1u << jk) - 1u), sk, spill + (qd & 1) * 16), slot + 6144);
+    dmab16(spr, slot + 6144, spill_off(fk, sk, (h * 2 + 0) * 2 + (qd >> 1), (qd & 1) * 16), 0);
     // V, gather j: lane l serves row 4j + (l & 3) of reader lane 16j + (l >> 2)
     const int jv = (h * 2 + 1) * 2 + (lane >> 5);
-    const uint32_t vmask = (1u << jv) - 1u;
-    const uint8_t* vpiece = spill + ((lane >> 2) & 7) * 4;
-    dma4(spill_at(fv.x & vmask, sv.x, vpiece), slot + 7168);
-    dma4(spill_at(fv.y & vmask, sv.y, vpiece), slot + 7168 + 256);
-    dma4(spill_at(fv.z & vmask, sv.z, vpiece), slot + 7168 + 512);
-    dma4(spill_at(fv.w & vmask, sv.w, vpiece), slot + 7168 + 768);
+    const uint32_t vpiece = ((lane >> 2) & 7) * 4;
+    dmab4(spr, slot + 7168, spill_off(fv.x, sv.x, jv, vpiece), 0);
+    dmab4(spr, slot + 7168 + 256, spill_off(fv.y, sv.y, jv, vpiece), 0);
+    dmab4(spr, slot + 7168 + 512, spill_off(fv.z, sv.z, jv, vpiece), 0);
+    dmab4(spr, slot + 7168 + 768, spill_off(fv.w, sv.w, jv, vpiece), 0);
     // the planes of (page, h): sm of K rows then V rows (4 KB), nibbles likewise (2 KB)
     const int64_t row0 = ((pid * H + h) * 2) * kT;  // K row 0 of the page
     const __amdgpu_buffer_rsrc_t smr = buffer_of(sm + row0 * kD, 2 * kT * kD);
@@ -229,8 +239,8 @@ struct PackedLoader {
 
   // One page's bytes as this lane needs them (read from LDS in one go).
   struct Page {
-    u32x4 ks0, ks1, kn, kh, vs0, vs1, vn, vh, fv;
-    uint32_t fk, kb;
+    u32x4 ks0, ks1, kn, kh, vs0, vs1, vn, vh;
+    uint32_t kb;
     u32x2 vb;
   };
 
@@ -240,61 +250,55 @@ struct PackedLoader {
     const int sk = (t >> 1) & 7;
     Page p;
     asm volatile(
-        "ds_read_b128 %0, %16\n\t"
-        "ds_read_b128 %1, %17\n\t"
-        "ds_read_b128 %2, %18\n\t"
-        "ds_read_b128 %3, %19 offset:1024\n\t"
-        "ds_read_b128 %4, %20\n\t"
-        "ds_read_b128 %5, %20 offset:16\n\t"
-        "ds_read_b128 %6, %19\n\t"
-        "ds_read_b128 %7, %19 offset:2048\n\t"
-        "ds_read_b128 %8, %21\n\t"
-        "ds_read_b32 %9, %22\n\t"
-        "ds_read_u8 %10, %23\n\t"
-        "ds_read_b64 %11, %24\n\t"
-        "ds_read_b32 %12, %25\n\t"
-        "ds_read_b32 %13, %26\n\t"
-        "ds_read_b128 %14, %27 offset:128\n\t"
-        "ds_read_b128 %15, %27\n\t"
+        "ds_read_b128 %0, %14\n\t"
+        "ds_read_b128 %1, %15\n\t"
+        "ds_read_b128 %2, %16\n\t"
+        "ds_read_b128 %3, %17 offset:1024\n\t"
+        "ds_read_b128 %4, %18\n\t"
+        "ds_read_b128 %5, %18 offset:16\n\t"
+        "ds_read_b128 %6, %17\n\t"
+        "ds_read_b128 %7, %17 offset:2048\n\t"
+        "ds_read_u8 %8, %19\n\t"
+        "ds_read_b64 %9, %20\n\t"
+        "ds_read_b32 %10, %21\n\t"
+        "ds_read_b32 %11, %22\n\t"
+        "ds_read_b128 %12, %23 offset:128\n\t"
+        "ds_read_b128 %13, %23\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(p.ks0), "=&v"(p.ks1), "=&v"(p.kn), "=&v"(p.kh), "=&v"(p.vs0), "=&v"(p.vs1),
-          "=&v"(p.vn), "=&v"(p.vh), "=&v"(p.fv), "=&v"(p.fk), "=&v"(p.kb), "=&v"(p.vb),
+          "=&v"(p.vn), "=&v"(p.vh), "=&v"(p.kb), "=&v"(p.vb),
           "=&v"(next.fk), "=&v"(next.sk), "=&v"(next.fv), "=&v"(next.sv)
         : "v"(slot + t * 128 + ((2 * qd) ^ sk) * 16), "v"(slot + t * 128 + ((2 * qd + 1) ^ sk) * 16),
           "v"(slot + 4096 + t * 64 + (qd ^ ((t >> 2) & 3)) * 16), "v"(slot + 5120 + lane * 16),
-          "v"(slot + 2048 + lane * 32), "v"(ms + 16 * qd), "v"(ms + 4 * t),
-          "v"(ms + 128 + 2 * t + (qd >> 1)), "v"(ms + 160 + 8 * qd), "v"(ms2 + 4 * t),
-          "v"(ms2 + 64 + 4 * (4 * (t & 3) + (t >> 2))), "v"(ms2 + 64 + 16 * (lane & 3))
+          "v"(slot + 2048 + lane * 32), "v"(ms + 128 + 2 * t + (qd >> 1)), "v"(ms + 160 + 8 * qd),
+          "v"(ms2 + 4 * t), "v"(ms2 + 64 + 4 * (4 * (t & 3) + (t >> 2))), "v"(ms2 + 64 + 16 * (lane & 3))
         : "memory");
     return p;
   }
 
-  __device__ __forceinline__ void rebuild(const Page& p, int h, int lane, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
-    const int t = lane & 15, qd = lane >> 4;
+  __device__ __forceinline__ void rebuild_k(const Page& p, int, int, uint32_t (&kp)[16]) const {
     {
-      // raw block: base 0 and the spill piece; compressed: the base and no high nibbles
-      const uint32_t kraw = (p.fk >> ((h * 2 + 0) * 2 + (qd >> 1))) & 1u;
-      const uint32_t bp = (p.kb * 0x00800080u) & (kraw - 1u);
-      const uint32_t hm = 0u - kraw;
+      // a raw block has base 0 and its spill piece, a compressed one its base and zeros
+      const uint32_t bp = p.kb * 0x00800080u;
       const uint32_t smw[8] = {p.ks0.x, p.ks0.y, p.ks0.z, p.ks0.w, p.ks1.x, p.ks1.y, p.ks1.z, p.ks1.w};
       const uint32_t nw[4] = {p.kn.x, p.kn.y, p.kn.z, p.kn.w};
-      const uint32_t hw[4] = {p.kh.x & hm, p.kh.y & hm, p.kh.z & hm, p.kh.w & hm};
+      const uint32_t hw[4] = {p.kh.x, p.kh.y, p.kh.z, p.kh.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) rebuild8(smw[2 * c], smw[2 * c + 1], nw[c], hw[c], bp, kp + 4 * c);
     }
+  }
+
+  __device__ __forceinline__ void rebuild_v(const Page& p, int, int lane, uint32_t (&vt)[16]) const {
+    const int t = lane & 15;
     uint32_t pr[4][4];
-    const int jv = (h * 2 + 1) * 2 + (t >> 3);
     const uint32_t half = (uint32_t)(t >> 3);
     const uint32_t vsw[8] = {p.vs0.x, p.vs0.y, p.vs0.z, p.vs0.w, p.vs1.x, p.vs1.y, p.vs1.z, p.vs1.w};
     const uint32_t vna[4] = {p.vn.x, p.vn.y, p.vn.z, p.vn.w}, vha[4] = {p.vh.x, p.vh.y, p.vh.z, p.vh.w};
-    const uint32_t fva[4] = {p.fv.x, p.fv.y, p.fv.z, p.fv.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t raw = (fva[j] >> jv) & 1u;
       const uint32_t word = j < 2 ? p.vb.x : p.vb.y;
       const uint32_t bexp = (word >> (8 * (((2 * j) & 3) + half))) & 0xFFu;
-      const uint32_t bp = (bexp * 0x00800080u) & (raw - 1u);
-      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], vha[j] & (0u - raw), bp, pr[j]);
+      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], vha[j], bexp * 0x00800080u, pr[j]);
     }
     to_token_pairs(pr, vt);
   }
@@ -348,12 +352,15 @@ struct RawLoader {
     return p;
   }
 
-  __device__ __forceinline__ void rebuild(const Page& p, int, int, uint32_t (&kp)[16], uint32_t (&vt)[16]) const {
+  __device__ __forceinline__ void rebuild_k(const Page& p, int, int, uint32_t (&kp)[16]) const {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t w[4] = {p.k[c].x, p.k[c].y, p.k[c].z, p.k[c].w};
       natural_to_pairs(w, kp + 4 * c);
     }
+  }
+
+  __device__ __forceinline__ void rebuild_v(const Page& p, int, int, uint32_t (&vt)[16]) const {
     uint32_t pr[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -435,6 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   if (s >= nsplit) return;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
+  __shared__ uint32_t s_prog[kWaves];  // pages finished by each wave
   const uint32_t ring = (uint32_t)(uintptr_t)&s_ring[wave][0];
   const uint32_t meta_ring = ring + 2 * kSlotBytes;
 
@@ -478,6 +486,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   // pin the q unpacking here: placed after the first page loads, its wait for q would also
   // wait for them
   asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
+  if (lane == 0) s_prog[wave] = 0u;
   __syncthreads();
 
   double m = -INFINITY;  // running max of head `head`'s unscaled scores (fp64)
@@ -509,8 +518,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   auto slot_of = [&](int n) -> uint32_t { return ring + (uint32_t)(n & 1) * kSlotBytes; };
   auto meta_of = [&](int n) -> uint32_t { return meta_ring + (uint32_t)(n & (kMetaRing - 1)) * kMetaBytes; };
 
-  auto compute = [&](const int n, const uint32_t (&kp)[16], const uint32_t (&vt)[16]) {
+  auto compute = [&](const int n, const typename Loader::Page& pg) {
     const int ntok = ntok_at(n);
+    uint32_t kp[16];
+    ld.rebuild_k(pg, h, lane, kp);
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -562,6 +573,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       for (int i = 0; i < 4; ++i) sd[i] = (double)sc[i];
     }
 
+    // V is rebuilt here, where its independent work can fill the latency of the row maxima
+    uint32_t vt[16];
+    ld.rebuild_v(pg, h, lane, vt);
     double pm = fmax(fmax(sd[0], sd[1]), fmax(sd[2], sd[3]));
     pm = rows_max_d(pm);
     if (__any(pm > m)) {
@@ -627,7 +641,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     ld.issue_page(pid_at(1), a.H, h, lane, slot_of(1), ld.read_issue(lane, meta_of(1)));
     typename Loader::Issue next = ld.read_issue(lane, meta_of(2));
     ld.issue_meta(pid_at(5), a.H, h, lane, meta_of(5));
+    // Waves w and w + 4 share a SIMD, and the SIMD issues the older one first: left alone, w
+    // finishes well before w + 4, which then runs by itself at half occupancy.  Each step, the
+    // wave of the pair that is behind raises its priority (the pages each wave takes are fixed,
+    // so the results do not depend on this).
+    const uint32_t prog_me = (uint32_t)(uintptr_t)&s_prog[wave];
+    const uint32_t prog_other = (uint32_t)(uintptr_t)&s_prog[wave ^ 4];
     for (int n = 0; n < nmine; ++n) {
+      lds_store_u32(prog_me, (uint32_t)n);
+      if (n > __builtin_amdgcn_readfirstlane(lds_load_u32(prog_other))) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(2);
       // every load of step n - 2 and earlier has landed: page n, metas up to n + 4
       wait_vm<kP + kM>();
       // page n leaves its slot (LDS -> VGPRs) together with the issue metadata of page n + 3;
@@ -636,11 +659,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       const typename Loader::Page pg = ld.read(lane, slot_of(n), meta_of(n), meta_of(n + 3), next);
       ld.issue_page(pid_at(n + 2), a.H, h, lane, slot_of(n), cur);
       ld.issue_meta(pid_at(n + 6), a.H, h, lane, meta_of(n + 6));
-      uint32_t kp[16], vt[16];
-      ld.rebuild(pg, h, lane, kp, vt);
-      compute(n, kp, vt);
+      compute(n, pg);
     }
     wait_vm<0>();  // the loads past the end still target this wave's LDS
+    lds_store_u32(prog_me, 0x7FFFFFFFu);  // done: never hold the partner back
+    __builtin_amdgcn_s_setprio(0);
   }
   if (err) set_status(a.status, err);
 
@@ -819,8 +842,8 @@ hipError_t launch_attention_packed(const zf_cache* c, const zf_seqs* q, const ui
                                    float scale, float* out, void* ws, hipStream_t st) {
   // the spill address of a compressed block is never used, but it must be readable
   const uint8_t* spill = c->spill_slots > 0 ? c->spill : c->sm;
-  const uint32_t max_slot = c->spill_slots > 0 ? (uint32_t)(c->spill_slots - 1) : 0u;  // < 2^32
-  PackedLoader ld{c->sm, c->nib, c->base, c->row_flags, c->row_spill, spill, max_slot};
+  const uint32_t spill_bytes = (uint32_t)(c->spill_slots * 32);  // validated below 2^32
+  PackedLoader ld{c->sm, c->nib, c->base, c->row_flags, c->row_spill, spill, spill_bytes};
   return launch(ld, c->num_pages, c->num_kv_heads, q, qv, scale, out, ws, c->status, st);
 }
 
