@@ -409,10 +409,6 @@ __device__ __forceinline__ float rows_max(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
-}
-__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
 
 // LDS per wave: two page slots and the meta ring; the end-of-split results reuse the wave's
@@ -429,7 +425,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const int head = t >> 2;  // query head of this lane's scores (and of its p.V A-operand row)
   const int part = t & 3;   // which bf16 part of the weights this lane's A row carries
   const float k0 = part == 0 ? 1.f : 0.f, k1 = part == 1 ? 1.f : 0.f, k2 = part == 2 ? 1.f : 0.f;
-  const uint32_t wmask = part == 3 ? 0u : 0xFFFFu;
 
   int32_t L = a.lens[b];
   const int32_t cap = min(a.maxp * kT, a.max_seq_len);
@@ -503,7 +498,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     cacc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const double c2 = a.scale_log2e;
-  double mc2 = 0.0;  // m * c2 once m is finite
+  double mc2 = 0.0;        // m * c2 once m is finite
+  float m32 = -INFINITY;   // m in fp32, for the exact-path test
+  const float negl32 = (float)(kNegligible / c2);
 
   // page n of this wave; indices past the end repeat the last page (their loads keep the
   // per-page load count fixed and are never used)
@@ -537,11 +534,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     // A score needs the exact path when it is large (one fp32 ulp of it is then a visible
     // change of its weight) and its weight can matter: scores more than kNegligible / c2
     // below the running maximum get a weight under 2^-kNegligible of the largest one.
-    const float floor32 = (float)(fmax(m, (double)pm32) - kNegligible / c2);
+    const float floor32 = fmaxf(m32, pm32) - negl32;
     bool big = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) big |= fabsf(sc[i]) > kBigScore && sc[i] > floor32;
-    double sd[4];
+    double sd[4], pm;
     if (__any(big)) {
       // exact fp64 scores: lane (t, qd) sums its 32 dims of token t for the 4 heads, the four
       // quarters are added, and each lane then fetches its own (token, head) entries
@@ -568,20 +565,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
         const double x = __shfl(offer, head * 16 + 4 * qd + i, 64);
         sd[i] = sc[i] == -INFINITY ? -INFINITY : x;  // keeps the tokens past the end out
       }
+      pm = rows_max_d(fmax(fmax(sd[0], sd[1]), fmax(sd[2], sd[3])));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sd[i] = (double)sc[i];
+      pm = (double)pm32;  // the same maximum
     }
 
-    // V is rebuilt here, where its independent work can fill the latency of the row maxima
+    // V is rebuilt here, where its independent work can fill the latency of the maxima
     uint32_t vt[16];
     ld.rebuild_v(pg, h, lane, vt);
-    double pm = fmax(fmax(sd[0], sd[1]), fmax(sd[2], sd[3]));
-    pm = rows_max_d(pm);
     if (__any(pm > m)) {
       const double mn = fmax(m, pm);
       const double alpha = exp2((m - mn) * c2);
       m = mn;
+      m32 = (float)m;
       mc2 = m * c2;
       l *= alpha;
       const double al = __shfl(alpha, 4 * qd, 64);  // acc holds head qd; lane 4qd has head qd
@@ -600,18 +598,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       p[i] = __builtin_amdgcn_exp2f((float)fma(sd[i], c2, -mc2));
       l += p[i];
     }
-    // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo:
-    // x0 = p, x1 = p - bf16(p), x2 = x1 - bf16(x1); row part takes bf16(x_part) (row 3: 0)
-    uint32_t w[4];
+    // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo, all
+    // three by truncation: hi = the top 8 significant bits of p, mid those of x1 = p - hi,
+    // lo = x1 - mid (at most 8 bits left).  The differences are exact, so the three parts
+    // sum to p exactly.  Row `part` takes its part (row 3: zero).
+    uint32_t xb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x1 = p[i] - bf16_value(bf16_bits(p[i]));
-      const float x2 = x1 - bf16_value(bf16_bits(x1));
+      const float x1 = p[i] - __uint_as_float(__float_as_uint(p[i]) & 0xFFFF0000u);
+      const float x2 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
       // exact selection by 0/1 factors (p, x1, x2 are finite), no divergent code
-      const float x = fmaf(x2, k2, fmaf(x1, k1, p[i] * k0));
-      w[i] = bf16_bits(x) & wmask;
+      xb[i] = __float_as_uint(fmaf(x2, k2, fmaf(x1, k1, p[i] * k0)));
     }
-    const s16x4 pa = __builtin_bit_cast(s16x4, (u32x2){w[0] | (w[1] << 16), w[2] | (w[3] << 16)});
+    // the high halves (the truncated bf16 parts) of two values per register
+    const s16x4 pa = __builtin_bit_cast(s16x4, (u32x2){__builtin_amdgcn_perm(xb[1], xb[0], 0x07060302u),
+                                                        __builtin_amdgcn_perm(xb[3], xb[2], 0x07060302u)});
     // rows 4qd + (0, 1, 2): hi, mid, lo parts of head qd.  The hi row restarts from zero on
     // every page and is added in fp64; mid and lo (below 2^-8 of it) accumulate in the MFMA.
 #pragma unroll
