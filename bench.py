@@ -13,7 +13,9 @@ weights exist here).  Inputs are resident in HBM before the timed region.
 Prints one JSON line.  `value` = tokens/s of the whole job (sequences x steps / time), one
 layer.  `roofline` prices the attention kernel (the dominant one) against HBM: algorithmic
 bytes per launch (packed planes of the attended rows, spill slots of their raw blocks, q, out,
-page table and lengths) / its mean duration from HIP events on the launch stream.
+page table and lengths) / its mean duration from HIP events on the launch stream, stamped at
+the kernel's own start and end (zf_time_next_attention: the interval a kernel trace reports);
+the call time with dispatch overhead is reported beside it.
 `cpu_baseline` times the CPU oracle (plain C, one thread) on a bounded sample of the same
 steps.
 """
@@ -138,16 +140,20 @@ def main():
         cache, seqs = layers[s % NL]
         zf.zf_append_kv(cache, seqs, k_dev[s], v_dev[s])
         if ev is not None:
-            ev[0].record(stream)
+            ev[2].record(stream)
+            zf.zf_time_next_attention(ev[0], ev[1])  # the kernel's own start / end stamps
         zf.zf_decode_attention(cache, seqs, q_dev[s], scale, out, ws)
         if ev is not None:
-            ev[1].record(stream)
+            ev[3].record(stream)
 
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    # per timed step: kernel start / end (device timestamps of the dispatch) and call start / end
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(K)]
+    for ev in evs:
+        for e in ev:
+            e.record(stream)  # creates the events on the device
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
@@ -157,7 +163,8 @@ def main():
     for cache, _ in layers:
         status = zf.zf_get_status(cache.status)
         assert status == 0, f"device status {status}"
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])   # kernel execution
+    call_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])   # call, dispatch included
 
     # ---- algorithmic bytes of each timed attention launch
     pt = inst.page_table
@@ -198,6 +205,7 @@ def main():
         "layers_rotated": NL,
         "attention_kernel_us_mean": round(attn_ms.mean() * 1e3, 2),
         "attention_kernel_us_min": round(attn_ms.min() * 1e3, 2),
+        "attention_call_us_mean": round(call_ms.mean() * 1e3, 2),
         "attention_bytes_per_launch": int(attn_bytes.mean()),
         "uncompressed_equivalent_GBps": round(uncompressed_eq, 1),
         "compression_ratio": round(ratio, 4),

@@ -21,8 +21,8 @@ ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN = 1, 2, 4
 
 EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_append_kv",
            "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_raw",
-           "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_get_status",
-           "zf_status_str")
+           "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
+           "zf_get_status", "zf_status_str")
 
 
 class ZfError(RuntimeError):
@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                    ctypes.c_float, vp, vp, sz, vp, vp]),
         "zf_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "zf_attention_workspace_init": (ctypes.c_int, [vp, sz, vp]),
+        "zf_time_next_attention": (ctypes.c_int, [vp, vp]),
         "zf_get_status": (ctypes.c_int, [vp, vp, vp]),
         "zf_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -205,6 +206,15 @@ def zf_decode_attention_raw(raw_pages: torch.Tensor, seqs: Seqs, q: torch.Tensor
                                           workspace.numel() * workspace.element_size(),
                                           _ptr(status), _stream(stream)),
            "zf_decode_attention_raw")
+
+
+def zf_time_next_attention(start: "torch.cuda.Event | None", stop: "torch.cuda.Event | None") -> None:
+    """The next attention call on this thread stamps `start` / `stop` at its kernel's own begin and
+    end (device timestamps).  The events must already exist on the device: torch creates them at
+    their first record(), so record each once beforehand."""
+    a = None if start is None else start.cuda_event
+    b = None if stop is None else stop.cuda_event
+    _check(load().zf_time_next_attention(a, b), "zf_time_next_attention")
 
 
 def zf_get_status(status: torch.Tensor, stream=None) -> int:

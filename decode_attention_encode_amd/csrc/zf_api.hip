@@ -17,6 +17,7 @@ hipError_t launch_attention_raw(const uint16_t*, int32_t, int32_t, const zf_seqs
                                 const uint16_t*, float, float*, void*, uint32_t*, hipStream_t);
 size_t attention_workspace_bytes(int32_t, int32_t, int32_t);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
+void set_attention_timing(hipEvent_t, hipEvent_t);
 }  // namespace zf
 
 namespace {
@@ -192,6 +193,12 @@ zf_status zf_decode_attention_raw(const uint16_t* raw_pages, int32_t num_pages,
   return hip_status(zf::launch_attention_raw(raw_pages, num_pages, num_kv_heads, seqs, q, scale,
                                              out, workspace, status,
                                              static_cast<hipStream_t>(stream)));
+}
+
+zf_status zf_time_next_attention(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return ZF_EINVAL;
+  zf::set_attention_timing(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+  return ZF_OK;
 }
 
 zf_status zf_get_status(const uint32_t* status, uint32_t* host_status, zf_stream_t stream) {

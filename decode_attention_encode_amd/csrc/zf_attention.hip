@@ -30,6 +30,7 @@
 // One kernel body serves the packed cache and raw bf16 pages (the uncompressed twin): both
 // loaders hand the same bf16 pairs to the same arithmetic, so the outputs match bit for bit.
 #include <algorithm>
+#include <hip/hip_ext.h>
 #include <stdlib.h>
 
 #include "zf_internal.h"
@@ -811,6 +812,13 @@ size_t attention_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
   return 256 + ((cnt + 255) / 256) * 256 + part;
 }
 
+struct TimingEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+static thread_local TimingEvents t_timing;
+
+void set_attention_timing(hipEvent_t start, hipEvent_t stop) { t_timing = TimingEvents{start, stop}; }
+
 template <class Loader>
 static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const zf_seqs* q,
                          const uint16_t* qv, float scale, float* out, void* ws, uint32_t* status,
@@ -834,7 +842,13 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + 256 + ((cnt + 255) / 256) * 256);
   a.status = status;
   dim3 grid(pl.nsplit_max, H, q->batch);
-  hipLaunchKernelGGL(attn_k<Loader>, grid, dim3(kThreads), 0, st, a, ld);
+  if (t_timing.start) {  // one-shot device timestamps of this kernel (profiling aid)
+    const TimingEvents ev = t_timing;
+    t_timing = TimingEvents{};
+    hipExtLaunchKernelGGL(attn_k<Loader>, grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0, a, ld);
+  } else {
+    hipLaunchKernelGGL(attn_k<Loader>, grid, dim3(kThreads), 0, st, a, ld);
+  }
   if (!a.direct) hipLaunchKernelGGL(combine_k, dim3(H, q->batch), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }

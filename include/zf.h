@@ -150,6 +150,14 @@ size_t zf_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t
 zf_status zf_attention_workspace_init(void* workspace, size_t workspace_bytes,
                                       zf_stream_t stream);
 
+/* Profiling aid, outside the method: the next zf_decode_attention or zf_decode_attention_raw
+ * call made by this host thread records `start_event` when its attention kernel begins
+ * executing on the device and `stop_event` when it ends (the dispatch's own timestamps, the
+ * interval a kernel trace reports, without launch overhead); the split merge, when there is
+ * one, is not included.  One-shot: that call clears the setting.  Both are caller-created,
+ * timing-enabled hipEvent_t handles, or both NULL (clears).  ZF_EINVAL if exactly one is NULL. */
+zf_status zf_time_next_attention(void* start_event, void* stop_event);
+
 /* Copies the sticky status word to *host_status (synchronizes `stream`). */
 zf_status zf_get_status(const uint32_t* status, uint32_t* host_status, zf_stream_t stream);
 const char* zf_status_str(zf_status s);

@@ -115,3 +115,22 @@ def test_status_strings():
     for code in range(5):
         assert lib.zf_status_str(code)
     assert lib.zf_status_str(zf.ZF_EWORKSPACE) == b"workspace missing or too small"
+
+
+def test_time_next_attention_arguments():
+    lib = zf.load()
+    assert lib.zf_time_next_attention(None, None) == zf.ZF_OK          # clears
+    assert lib.zf_time_next_attention(4096, None) == zf.ZF_EINVAL       # exactly one event
+    assert lib.zf_time_next_attention(None, 4096) == zf.ZF_EINVAL
+
+
+def test_attention_rejects_spill_pool_beyond_32bit_offsets():
+    lib = zf.load()
+    s = zf.zf_seqs(1, 1, 4096, 4096, 16)
+    ok = _cache(spill_slots=(1 << 27) - 1)
+    big = _cache(spill_slots=1 << 27)
+    # rejected before any launch; the in-range pool gets past this check to the I/O checks
+    assert lib.zf_decode_attention(ctypes.byref(big), ctypes.byref(s), 4096, 32, ctypes.c_float(0.1),
+                                   4096, 4096, 1 << 20, None) == zf.ZF_EUNSUPPORTED
+    assert lib.zf_decode_attention(ctypes.byref(ok), ctypes.byref(s), 4096, 32, ctypes.c_float(0.1),
+                                   4096, 4096, 0, None) == zf.ZF_EWORKSPACE

@@ -217,3 +217,23 @@ def test_host_argument_errors_raise():
     ws = zf.attention_workspace(SMALL.batch, 8, 32, 128, s.seqs.max_seq_len)
     with pytest.raises(zf.ZfError, match="unsupported"):
         zf.zf_decode_attention(s.cache, s.seqs, bad_q, 0.1, out, ws)
+
+
+@pytest.mark.gpu
+def test_time_next_attention_stamps_the_kernel():
+    inst = synth.make(synth.WORKLOADS[0])
+    s = Setup(inst)
+    q = synth.query(inst.w, 0)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record(stream)
+    ev[2].record(stream)
+    zf.zf_time_next_attention(ev[0], ev[1])
+    out = s.attention(q)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms, call_ms = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    assert 0.0 < kernel_ms <= call_ms
+    assert s.status() == 0
+    assert torch.equal(out, s.attention(q))  # one-shot: the next call launches normally
