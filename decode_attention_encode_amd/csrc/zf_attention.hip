@@ -49,7 +49,8 @@ constexpr int kD = 128, kT = 16, kG = 4, kWaves = 8, kThreads = 64 * kWaves;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr float kBigScore = 64.f;  // |q.k| above which a score may need the fp64 path
 constexpr double kNegligible = 16.0;  // weights below 2^-16 of the largest never need it
-constexpr int kMaxPagesPerSplit = kWaves * 64;  // each wave keeps its page ids in one register
+constexpr int kMaxPagesPerSplit = kWaves * 64;
+constexpr uint32_t kXcds = 8;  // MI355X: workgroups are dispatched round-robin over 8 XCDs  // each wave keeps its page ids in one register
 // One split's partial, in doubles: acc[kG][kD], l[kG], m[kG].
 constexpr int kPartDoubles = kG * kD + 2 * kG;
 
@@ -280,7 +281,7 @@ struct PackedLoader {
   __device__ __forceinline__ void rebuild_k(const Page& p, int, int, uint32_t (&kp)[16]) const {
     {
       // a raw block has base 0 and its spill piece, a compressed one its base and zeros
-      const uint32_t bp = p.kb * 0x00800080u;
+      const uint32_t bp = p.kb * 0x00010001u;
       const uint32_t smw[8] = {p.ks0.x, p.ks0.y, p.ks0.z, p.ks0.w, p.ks1.x, p.ks1.y, p.ks1.z, p.ks1.w};
       const uint32_t nw[4] = {p.kn.x, p.kn.y, p.kn.z, p.kn.w};
       const uint32_t hw[4] = {p.kh.x, p.kh.y, p.kh.z, p.kh.w};
@@ -299,7 +300,7 @@ struct PackedLoader {
     for (int j = 0; j < 4; ++j) {
       const uint32_t word = j < 2 ? p.vb.x : p.vb.y;
       const uint32_t bexp = (word >> (8 * (((2 * j) & 3) + half))) & 0xFFu;
-      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], vha[j], bexp * 0x00800080u, pr[j]);
+      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], vha[j], bexp * 0x00010001u, pr[j]);
     }
     to_token_pairs(pr, vt);
   }
@@ -419,7 +420,15 @@ static_assert(kG * kD * sizeof(double) + 2 * kG * sizeof(double) <= kWaveLds, "r
 
 template <class Loader>
 __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Workgroup ids go round-robin over the 8 XCDs; each XCD takes a contiguous run of units
+  // (split fastest, then kv head, then sequence), so the kv heads of a sequence share one L2
+  // for the page metadata and spill lines they all read.
+  const uint32_t per_xcd = gridDim.x / kXcds;
+  const uint32_t job = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (job >= (uint32_t)a.nsplit_max * (uint32_t)a.H * (uint32_t)a.B) return;  // <= maxp * B < 2^31
+  const int s = (int)(job % (uint32_t)a.nsplit_max);
+  const int h = (int)((job / (uint32_t)a.nsplit_max) % (uint32_t)a.H);
+  const int b = (int)(job / ((uint32_t)a.nsplit_max * (uint32_t)a.H));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 15, qd = lane >> 4;
@@ -841,7 +850,8 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   size_t cnt = (size_t)q->batch * H * sizeof(uint32_t);
   a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + 256 + ((cnt + 255) / 256) * 256);
   a.status = status;
-  dim3 grid(pl.nsplit_max, H, q->batch);
+  const uint32_t units = (uint32_t)pl.nsplit_max * (uint32_t)H * (uint32_t)q->batch;
+  dim3 grid((units + kXcds - 1) / kXcds * kXcds);
   if (t_timing.start) {  // one-shot device timestamps of this kernel (profiling aid)
     const TimingEvents ev = t_timing;
     t_timing = TimingEvents{};

@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t
       if (idx < spill_slots) hi = *reinterpret_cast<const uint32_t*>(spill + idx * 32u + lane8 * 4);
       else err = ZF_DEV_ESPILL;
     } else {
-      base_pair = (uint32_t)base[v0 / kBlock] * 0x00800080u;
+      base_pair = (uint32_t)base[v0 / kBlock] * 0x00010001u;
     }
     uint32_t pr[4], w[4];
     rebuild8(smw.x, smw.y, nibw, hi, base_pair, pr);

@@ -70,16 +70,17 @@ __device__ __forceinline__ void pack8(const uint32_t w[4], uint32_t base, uint32
 
 // ---------------------------------------------------------------- rebuild (decode, attention)
 
-// Rebuilds the pair (value r, value r + 4) of an 8-value group: the sm bytes of values 0..3
-// are in s0, of 4..7 in s1 (s0x, s1x: the same words shifted left by 8); nibble of value v at
-// bits 4v of `nib`; `hi` holds a raw block's exponent high nibbles the same way (0 for a
-// compressed block) and `base_pair` = base * 0x00800080 (0 for a raw block).  Returns value r
-// in the low half and value r + 4 in the high half.
+// Rebuilds the 8 values of a group as 4 pairs, pair r = (value r, value r + 4), value r in the
+// low half.  s0 holds the sm bytes of values 0..3, s1 those of 4..7; `nib` the offset of value v
+// at bits 4v; `hi` a raw block's exponent high nibbles the same way (zero for a compressed
+// block); `base16` = base * 0x00010001 (zero for a raw block).
 //
-// v_perm_b32 selectors 8..11 produce 0xFF or 0x00 from the sign bit of byte 1 or 3 of either
-// source, which moves each sign to bit 15 of its half in the same instruction that spreads the
-// sm bytes; the nibble and high-nibble fields are then inserted with bitfield selects, and a
-// single add of the base completes both values.
+// First the exponent bytes, e = offset | high nibble << 4, for the even values (xe) and the odd
+// values (xo).  Per pair, one byte permute spreads e of both values into the low bytes of the two
+// halves, one add-and-shift puts (e + base) << 7 in bits 7..14 -- the single add of the method,
+// done for two values -- and a bitfield select merges it with the sm bytes, which a second
+// permute duplicates into both bytes of each half: bit 15 then carries the sign and bits 0..6
+// the mantissa, the rest is replaced.
 // v_bfi_b32: (a & mask) | (b & ~mask) in one instruction (the mask comes from an SGPR).
 __device__ __forceinline__ uint32_t bitselect(uint32_t mask, uint32_t a, uint32_t b) {
   uint32_t r;
@@ -87,28 +88,17 @@ __device__ __forceinline__ uint32_t bitselect(uint32_t mask, uint32_t a, uint32_
   return r;
 }
 
-template <int r>
-__device__ __forceinline__ uint32_t rebuild_pair(uint32_t s0, uint32_t s1, uint32_t s0x,
-                                                 uint32_t s1x, uint32_t nib, uint32_t hi,
-                                                 uint32_t base_pair) {
-  constexpr uint32_t sel = (r & 2) ? 0x0B070903u : 0x0A050801u;  // [b, sign(b), b', sign(b')]
-  const uint32_t p = (r & 1) ? __builtin_amdgcn_perm(s1, s0, sel) : __builtin_amdgcn_perm(s1x, s0x, sel);
-  const uint32_t n = (r <= 1) ? (nib << (7 - 4 * r)) : (nib >> (4 * r - 7));
-  const uint32_t e = (r <= 2) ? (hi << (11 - 4 * r)) : (hi >> 1);
-  uint32_t x = bitselect(0x07800780u, n, p);  // nibble -> bits 7..10 (and 23..26)
-  x = bitselect(0x78007800u, e, x);           // high nibble -> bits 11..14
-  return x + base_pair;                                  // the one add: + base << 7, twice
-}
-
-// The 4 pairs of one 8-value group, pair r = (value r, value r + 4).
-__device__ __forceinline__ void rebuild8(uint32_t s0, uint32_t s1, uint32_t nib,
-                                         uint32_t spill_hi, uint32_t base_pair,
-                                         uint32_t out[4]) {
-  const uint32_t s0x = s0 << 8, s1x = s1 << 8;
-  out[0] = rebuild_pair<0>(s0, s1, s0x, s1x, nib, spill_hi, base_pair);
-  out[1] = rebuild_pair<1>(s0, s1, s0x, s1x, nib, spill_hi, base_pair);
-  out[2] = rebuild_pair<2>(s0, s1, s0x, s1x, nib, spill_hi, base_pair);
-  out[3] = rebuild_pair<3>(s0, s1, s0x, s1x, nib, spill_hi, base_pair);
+__device__ __forceinline__ void rebuild8(uint32_t s0, uint32_t s1, uint32_t nib, uint32_t hi,
+                                         uint32_t base16, uint32_t out[4]) {
+  const uint32_t xe = bitselect(0x0F0F0F0Fu, nib, hi << 4);  // e of values 0, 2, 4, 6
+  const uint32_t xo = bitselect(0x0F0F0F0Fu, nib >> 4, hi);  // e of values 1, 3, 5, 7
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t k = (uint32_t)(r >> 1);  // byte of value r in xe / xo
+    const uint32_t epair = __builtin_amdgcn_perm(0u, (r & 1) ? xo : xe, 0x0C000C00u | ((k + 2) << 16) | k);
+    const uint32_t spair = __builtin_amdgcn_perm(s1, s0, (uint32_t)r * 0x0101u + (uint32_t)(r + 4) * 0x01010000u);
+    out[r] = bitselect(0x7F807F80u, (epair + base16) << 7, spair);
+  }
 }
 
 // Natural order (value 2k low, 2k+1 high in word k) from the (r, r+4) pair order.
