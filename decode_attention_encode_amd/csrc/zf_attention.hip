@@ -290,19 +290,29 @@ struct PackedLoader {
     }
   }
 
+  // V is rebuilt in groups of two token rows: group (q, hh) takes dims 4hh..4hh+3 of rows 2q
+  // and 2q + 1 as the 8 values of rebuild8 (row 2q first), so each rebuilt pair is already the
+  // (token, token + 1) pair the p.V operand wants.  The nibble and spill words of the two rows
+  // are joined by one byte permute; both rows' bases sit in one base word (bytes half and
+  // 2 + half), which one more permute spreads into the two halves.
   __device__ __forceinline__ void rebuild_v(const Page& p, int, int lane, uint32_t (&vt)[16]) const {
-    const int t = lane & 15;
-    uint32_t pr[4][4];
-    const uint32_t half = (uint32_t)(t >> 3);
+    const uint32_t half = (uint32_t)((lane & 15) >> 3);
+    const uint32_t bsel = 0x0C000C00u | ((2u + half) << 16) | half;
     const uint32_t vsw[8] = {p.vs0.x, p.vs0.y, p.vs0.z, p.vs0.w, p.vs1.x, p.vs1.y, p.vs1.z, p.vs1.w};
     const uint32_t vna[4] = {p.vn.x, p.vn.y, p.vn.z, p.vn.w}, vha[4] = {p.vh.x, p.vh.y, p.vh.z, p.vh.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t word = j < 2 ? p.vb.x : p.vb.y;
-      const uint32_t bexp = (word >> (8 * (((2 * j) & 3) + half))) & 0xFFu;
-      rebuild8(vsw[2 * j], vsw[2 * j + 1], vna[j], vha[j], bexp * 0x00010001u, pr[j]);
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t b16 = __builtin_amdgcn_perm(0u, q ? p.vb.y : p.vb.x, bsel);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
+        uint32_t pr[4];
+        rebuild8(vsw[4 * q + hh], vsw[4 * q + 2 + hh], __builtin_amdgcn_perm(vna[2 * q + 1], vna[2 * q], sel),
+                 __builtin_amdgcn_perm(vha[2 * q + 1], vha[2 * q], sel), b16, pr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vt[2 * (r + 4 * hh) + q] = pr[r];
+      }
     }
-    to_token_pairs(pr, vt);
   }
 };
 
@@ -390,12 +400,30 @@ __device__ __forceinline__ void pair_d(double v, double& a, double& b) {
   a = __longlong_as_double((int64_t)(((uint64_t)h[0] << 32) | l[0]));
   b = __longlong_as_double((int64_t)(((uint64_t)h[1] << 32) | l[1]));
 }
+// Maxima as single instructions.  fmax / fmaxf first quiet a possible signalling NaN in each
+// operand with an extra max; every operand here is the result of arithmetic or a copy of one,
+// never a signalling NaN, so the plain instruction gives the same result.
+__device__ __forceinline__ float max_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ double max_f64(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 // max / sum over the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48) of a double
 __device__ __forceinline__ double rows_max_d(double v) {
   double a, b;
   pair_d<false>(v, a, b);
-  pair_d<true>(fmax(a, b), a, b);
-  return fmax(a, b);
+  pair_d<true>(max_f64(a, b), a, b);
+  return max_f64(a, b);
 }
 __device__ __forceinline__ double rows_sum_d(double v) {
   double a, b;
@@ -406,9 +434,9 @@ __device__ __forceinline__ double rows_sum_d(double v) {
 // max over the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48) of a float
 __device__ __forceinline__ float rows_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float m1 = max_f32(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_f32(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 
@@ -434,7 +462,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const int t = lane & 15, qd = lane >> 4;
   const int head = t >> 2;  // query head of this lane's scores (and of its p.V A-operand row)
   const int part = t & 3;   // which bf16 part of the weights this lane's A row carries
-  const float k0 = part == 0 ? 1.f : 0.f, k1 = part == 1 ? 1.f : 0.f, k2 = part == 2 ? 1.f : 0.f;
+  // masks of the weight split below: row 0 keeps p, row 1 takes p - hi, row 2 (p - hi) - mid,
+  // row 3 p - p = 0
+  const uint32_t mask1 = part == 0 ? 0u : part == 3 ? 0xFFFFFFFFu : 0xFFFF0000u;
+  const uint32_t mask2 = part == 2 ? 0xFFFF0000u : 0u;
 
   int32_t L = a.lens[b];
   const int32_t cap = min(a.maxp * kT, a.max_seq_len);
@@ -540,11 +571,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = 4 * qd + i < ntok ? sc[i] : -INFINITY;
     }
-    const float pm32 = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float pm32 = rows_max(max_f32(max3_f32(sc[0], sc[1], sc[2]), sc[3]));
     // A score needs the exact path when it is large (one fp32 ulp of it is then a visible
     // change of its weight) and its weight can matter: scores more than kNegligible / c2
     // below the running maximum get a weight under 2^-kNegligible of the largest one.
-    const float floor32 = fmaxf(m32, pm32) - negl32;
+    const float floor32 = max_f32(m32, pm32) - negl32;
     bool big = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) big |= fabsf(sc[i]) > kBigScore && sc[i] > floor32;
@@ -575,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
         const double x = __shfl(offer, head * 16 + 4 * qd + i, 64);
         sd[i] = sc[i] == -INFINITY ? -INFINITY : x;  // keeps the tokens past the end out
       }
-      pm = rows_max_d(fmax(fmax(sd[0], sd[1]), fmax(sd[2], sd[3])));
+      pm = rows_max_d(max_f64(max_f64(sd[0], sd[1]), max_f64(sd[2], sd[3])));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sd[i] = (double)sc[i];
@@ -611,14 +642,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo, all
     // three by truncation: hi = the top 8 significant bits of p, mid those of x1 = p - hi,
     // lo = x1 - mid (at most 8 bits left).  The differences are exact, so the three parts
-    // sum to p exactly.  Row `part` takes its part (row 3: zero).
+    // sum to p exactly.  Each row subtracts only the parts before its own (masks of 0 subtract
+    // zero), so the truncation below leaves row `part` its part; row 3 subtracts p itself.
     uint32_t xb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x1 = p[i] - __uint_as_float(__float_as_uint(p[i]) & 0xFFFF0000u);
-      const float x2 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
-      // exact selection by 0/1 factors (p, x1, x2 are finite), no divergent code
-      xb[i] = __float_as_uint(fmaf(x2, k2, fmaf(x1, k1, p[i] * k0)));
+      const float x1 = p[i] - __uint_as_float(__float_as_uint(p[i]) & mask1);
+      xb[i] = __float_as_uint(x1 - __uint_as_float(__float_as_uint(x1) & mask2));
     }
     // the high halves (the truncated bf16 parts) of two values per register
     const s16x4 pa = __builtin_bit_cast(s16x4, (u32x2){__builtin_amdgcn_perm(xb[1], xb[0], 0x07060302u),
