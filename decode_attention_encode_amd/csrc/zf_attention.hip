@@ -9,22 +9,22 @@
 // KV cache).
 //
 // Mapping (head_dim 128, 16-token pages, 4 query heads per kv head):
-//   grid (split, kv head, sequence); 4 waves per workgroup; wave w takes pages w, w+4, ...
-//   of its split, one page per step of a software pipeline: row metadata (flags, spill
-//   base) two pages ahead, planes and spill slots one page ahead, compute on the current one.
-//   lane = (t = lane & 15, qd = lane >> 4).
-//   K: lane holds 32 head_dim values (quarter qd) of token t, read as 16-byte loads.
+//   one workgroup of 8 waves per (split, kv head, sequence); wave w takes pages w, w+8, ...
+//   of its split, one page per step of a software pipeline: row metadata (flags, first spill
+//   slots, bases) six pages ahead, planes and spill slots two pages ahead, all staged in LDS by
+//   direct loads; compute on the current page.  lane = (t = lane & 15, qd = lane >> 4).
+//   K: lane holds 32 head_dim values (quarter qd) of token krow(t), read as 16-byte loads.
 //   Scores as S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (rebuilt K pairs as A, the 4 query
 //   heads replicated over the 16 columns of B): lane (t, qd) receives the scores of tokens
-//   4qd..4qd+3 for query head t & 3 -- exactly the A-operand layout of the p.V product.
-//   p.V on v_mfma_f32_16x16x16_bf16: A rows are the 4 heads' weights split into three bf16
-//   parts (rows 0-3 high, 4-7 middle, 8-11 low part; p = hi + mid + lo to ~2^-27), B is V
-//   with k = token: lane (t, qd) loads tokens 4qd..4qd+3, head_dim 8t..8t+7, rebuilds them
-//   and turns value pairs into token pairs with byte permutes.  The three row groups of the
-//   fp32 product are summed once per split.
+//   qd, qd + 4, qd + 8, qd + 12 for query head t >> 2 -- exactly the A-operand layout of the
+//   p.V product.
+//   p.V on v_mfma_f32_16x16x16_bf16: A row 4i + j carries part j of head i's weights (three
+//   bf16 parts by truncation, hi + mid + lo = p exactly; row 4i + 3 zero), B is V with
+//   k = token: lane (t, qd) rebuilds V rows qd + 4j at head_dim 8t..8t+7 straight into token
+//   pairs.  The hi row goes to fp64 every page, mid and lo stay in the MFMA accumulators.
 //   Softmax: running max in fp64, raised (with a rescale) only when a page exceeds it.  Pages
-//   holding a score with |q.k| > kBigScore get exact fp64 scores: at that size one fp32 ulp of
-//   a score is already a visible change of its weight.
+//   holding a score with |q.k| > kBigScore that can still matter get exact fp64 scores: at that
+//   size one fp32 ulp of a score is already a visible change of its weight.
 //   Splits of the token axis write (acc, l, m) partials; a second small kernel merges them
 //   in split order, so results do not depend on timing.
 // One kernel body serves the packed cache and raw bf16 pages (the uncompressed twin): both
@@ -112,13 +112,20 @@ __device__ __forceinline__ void wait_vm() {
 
 // ---------------------------------------------------------------- loaders
 // A loader moves one page (16 tokens of kv head h) into an LDS slot and rebuilds it as bf16 pairs:
-//   kp[4c + r]   K (head_dim 32*qd + 8c + r, same + 4) of token t
-//   vt[2n], vt[2n + 1]   V (tokens 4qd, 4qd+1) and (4qd+2, 4qd+3) at head_dim vdim(n, t)
+//   kp[4c + r]   K (head_dim 32*qd + 8c + r, same + 4) of token krow(t)
+//   vt[2n], vt[2n + 1]   V (tokens qd, qd + 4) and (qd + 8, qd + 12) at head_dim vdim(n, t)
 // with t = lane & 15, qd = lane >> 4.  kMetaLoads / kPageLoads: direct loads per meta / page.
+//
+// Token order: row i of the score MFMA's A operand holds token krow(i), so its output row
+// 4qd + r -- the r-th score of lane (t, qd) -- is token qd + 4r.  The p.V operands use the same
+// order (k index 4qd + r is token qd + 4r), and the four V rows a lane needs, qd + 4j, are then
+// four consecutive rows across the quarters of a wave: plain row-major V in LDS is read without
+// bank conflicts.
 
+__device__ __forceinline__ int krow(int i) { return (i >> 2) + 4 * (i & 3); }
 __device__ __forceinline__ int vdim(int n, int t) { return 8 * t + (n & 3) + 4 * (n >> 2); }
 
-// pr[j][r] = (value r, value r + 4) of token row j (8 values, 8t..8t+7) -> token pairs per dim
+// pr[j][r] = (value r, value r + 4) of V row j (8 values, 8t..8t+7) -> token pairs per dim
 __device__ __forceinline__ void to_token_pairs(const uint32_t (&pr)[4][4], uint32_t (&vt)[16]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -133,18 +140,18 @@ constexpr uint32_t kSlotBytes = 8192;  // one page of either loader
 constexpr uint32_t kMetaBytes = 256;   // one page's row metadata (packed loader)
 constexpr int kMetaRing = 8;
 
-// Packed page slot (lane L = (t, qd) reads every piece below with one 16-byte LDS read, and
-// the 16 lanes of a quarter wave always hit 16 different bank groups):
+// Packed page slot.  Every load is 16 bytes per lane; the reads of a quarter wave (16-byte
+// reads) or of a half wave (8- and 4-byte reads) always hit distinct banks:
 //   [0, 2048)     K sm rows 0..15, 128 B each; 16-byte chunk c of row r at c ^ ((r >> 1) & 7)
-//   [2048, 4096)  V sm, per lane: the 8 bytes of head_dim 8t..8t+7 of rows 4qd..4qd+3
+//   [2048, 4096)  V sm rows, 128 B each, as in memory
 //   [4096, 5120)  K nibble rows, 64 B each; chunk c of row r at c ^ ((r >> 2) & 3)
-//   [5120, 6144)  V nibbles, per lane: 4 bytes of rows 4qd..4qd+3
-//   [6144, 7168)  K spill piece of each lane (16 bytes)
-//   [7168, 8192)  V spill pieces, per lane: 4 bytes of rows 4qd..4qd+3
-// The V pieces are gathered 4 bytes per lane so that they land transposed.
-// Meta slot, one dword per lane of a 4-byte gather: words 0..15 row flags, 16..31 first spill
-// slots, 32..47 base bytes (K rows, then V rows), 48..63 row flags again; words 16..31 and
-// 48..63 hold row r at 4 * (r & 3) + (r >> 2), so rows r, r + 4, r + 8, r + 12 are adjacent.
+//   [5120, 6144)  V nibble rows, 64 B each, as in memory
+//   [6144, 7168)  V spill: row r's two V blocks of head h (32-byte slot each, zeros when the
+//                 block is compressed), 64 B per row
+//   [7168, 8192)  K spill the same way, chunk c of row r at c ^ ((r >> 2) & 3)
+// Meta slot, one dword per lane of a 4-byte gather: words 2r, 2r + 1 = flags and first spill
+// slot of row r (r < 16); words 32..39 the K base bytes of head h (row r at byte 2r + half),
+// words 40..47 the V base words in the order 0, 2, 4, 6, 1, 3, 5, 7; words 48..63 unused.
 struct PackedLoader {
   const uint8_t* sm;
   const uint8_t* nib;
@@ -154,19 +161,19 @@ struct PackedLoader {
   const uint8_t* spill;  // a valid address even when the pool is empty
   uint32_t spill_bytes;  // spill_slots * 32 (below 2^32)
 
-  static constexpr int kMetaLoads = 1, kPageLoads = 20;
+  static constexpr int kMetaLoads = 1, kPageLoads = 8;
 
   __device__ __forceinline__ void issue_meta(int64_t pid, int H, int h, int lane, uint32_t ms) const {
-    const int grp = lane >> 4, i = lane & 15;
-    const int rt = 4 * (i & 3) + (i >> 2);  // row stored at word i of the transposed groups
-    const uint32_t* fl = row_flags + pid * kT;
-    const uint32_t* sp = row_spill + pid * kT;
-    const uint32_t* bs = reinterpret_cast<const uint32_t*>(base + ((pid * H + h) * 2) * kT * 2);
-    // branch-free pick of the lane's source (selects, not divergent code)
-    const uint64_t a0 = (uint64_t)(fl + (grp == 0 ? i : rt)), a1 = (uint64_t)(sp + rt), a2 = (uint64_t)(bs + i);
-    const uint64_t m1 = 0ull - (uint64_t)(grp == 1), m2 = 0ull - (uint64_t)(grp == 2);
-    const uint64_t g = (a0 & ~(m1 | m2)) | (a1 & m1) | (a2 & m2);
-    dma4(reinterpret_cast<const void*>(g), ms);
+    // the lane's source: array and word are fixed per lane, only the page moves (arithmetic
+    // selects, no divergent code)
+    const bool is_spill = lane < 32 && (lane & 1), is_base = lane >= 32 && lane < 48;
+    const int v = lane - 40;  // V base position v -> word 8 + 2 (v & 3) + (v >> 2)
+    const uint32_t word = lane < 32 ? lane >> 1 : lane < 40 ? lane - 32 : lane < 48 ? 8 + 2 * (v & 3) + (v >> 2) : lane - 48;
+    const uint64_t d_sp = (uint64_t)row_spill - (uint64_t)row_flags;
+    const uint64_t d_bs = (uint64_t)(base + (int64_t)h * 2 * kT * 2) - (uint64_t)row_flags;
+    const uint64_t delta = ((0ull - (uint64_t)is_spill) & d_sp) | ((0ull - (uint64_t)is_base) & d_bs);
+    const uint64_t stride = is_base ? (uint64_t)H * 2 * kT * 2 : (uint64_t)kT * 4;
+    dma4(reinterpret_cast<const void*>((uint64_t)row_flags + delta + 4ull * word + (uint64_t)pid * stride), ms);
   }
 
   // Byte offset of a spill piece in the pool: slot = first + popcount(lower raw blocks of the
@@ -177,103 +184,86 @@ struct PackedLoader {
     return ((flags >> j) & 1u) ? slot * 32u + piece : 0xFFFFFFFFu;
   }
 
-  // The row metadata issue_page needs, read from a meta slot ahead of time.
+  // The row metadata issue_page needs, read from a meta slot ahead of time: flags and first
+  // spill slot of row lane >> 2.
   struct Issue {
-    uint32_t fk, sk;  // flags, first spill slot of row t
-    u32x4 fv, sv;     // the same for rows 4j + (lane & 3), j = 0..3
+    u32x2 fs;
   };
 
   __device__ __forceinline__ Issue read_issue(int lane, uint32_t ms) const {
-    const int t = lane & 15;
     Issue r;
-    asm volatile(
-        "ds_read_b32 %0, %4\n\t"
-        "ds_read_b32 %1, %5\n\t"
-        "ds_read_b128 %2, %6 offset:128\n\t"
-        "ds_read_b128 %3, %6\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r.fk), "=&v"(r.sk), "=&v"(r.fv), "=&v"(r.sv)
-        : "v"(ms + 4 * t), "v"(ms + 64 + 4 * (4 * (t & 3) + (t >> 2))), "v"(ms + 64 + 16 * (lane & 3))
-        : "memory");
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r.fs) : "v"(ms + 8 * (lane >> 2)) : "memory");
     return r;
   }
 
   __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue& m) const {
-    const int t = lane & 15, qd = lane >> 4;
-    const uint32_t fk = m.fk, sk = m.sk;
-    const u32x4 fv = m.fv, sv = m.sv;
-    // the spill pool as a bounds-checked buffer: offsets past its end read zeros
+    // spill: lane l loads 16 bytes of row l >> 2, chunk l & 3 of the row's 64 bytes (K chunks
+    // swizzled); the pool as a bounds-checked buffer, so offsets past its end read zeros
     const __amdgpu_buffer_rsrc_t spr = buffer_of(spill, spill_bytes);
-    // K: lane (t, qd) takes half qd & 1 of block (h, K, qd >> 1) of row t
-    dmab16(spr, slot + 6144, spill_off(fk, sk, (h * 2 + 0) * 2 + (qd >> 1), (qd & 1) * 16), 0);
-    // V, gather j: lane l serves row 4j + (l & 3) of reader lane 16j + (l >> 2)
-    const int jv = (h * 2 + 1) * 2 + (lane >> 5);
-    const uint32_t vpiece = ((lane >> 2) & 7) * 4;
-    dmab4(spr, slot + 7168, spill_off(fv.x, sv.x, jv, vpiece), 0);
-    dmab4(spr, slot + 7168 + 256, spill_off(fv.y, sv.y, jv, vpiece), 0);
-    dmab4(spr, slot + 7168 + 512, spill_off(fv.z, sv.z, jv, vpiece), 0);
-    dmab4(spr, slot + 7168 + 768, spill_off(fv.w, sv.w, jv, vpiece), 0);
+    const int r = lane >> 2;
+    const int ck = (lane & 3) ^ ((r >> 2) & 3), cv = lane & 3;
+    dmab16(spr, slot + 7168, spill_off(m.fs.x, m.fs.y, (h * 2 + 0) * 2 + (ck >> 1), (ck & 1) * 16), 0);
+    dmab16(spr, slot + 6144, spill_off(m.fs.x, m.fs.y, (h * 2 + 1) * 2 + (cv >> 1), (cv & 1) * 16), 0);
     // the planes of (page, h): sm of K rows then V rows (4 KB), nibbles likewise (2 KB)
     const int64_t row0 = ((pid * H + h) * 2) * kT;  // K row 0 of the page
     const __amdgpu_buffer_rsrc_t smr = buffer_of(sm + row0 * kD, 2 * kT * kD);
     const __amdgpu_buffer_rsrc_t nbr = buffer_of(nib + row0 * (kD / 2), 2 * kT * (kD / 2));
     {  // K sm: gather i, lane l -> LDS chunk 64i + l = row 8i + (l >> 3), position l & 7
-      const int r = lane >> 3, c = (lane & 7) ^ ((r >> 1) & 7);
+      const int r0 = lane >> 3, c0 = (lane & 7) ^ ((r0 >> 1) & 7);
       const int r1 = 8 + (lane >> 3), c1 = (lane & 7) ^ ((r1 >> 1) & 7);
-      dmab16(smr, slot, (uint32_t)(r * 128 + c * 16), 0);
+      dmab16(smr, slot, (uint32_t)(r0 * 128 + c0 * 16), 0);
       dmab16(smr, slot + 1024, (uint32_t)(r1 * 128 + c1 * 16), 0);
     }
     {  // K nibbles: lane l -> row l >> 2, position l & 3
-      const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
-      dmab16(nbr, slot + 4096, (uint32_t)(r * 64 + c * 16), 0);
+      const int rn = lane >> 2, cn = (lane & 3) ^ ((rn >> 2) & 3);
+      dmab16(nbr, slot + 4096, (uint32_t)(rn * 64 + cn * 16), 0);
     }
-    {  // V sm: gather i, lane l -> reader lane 8i + (l >> 3), word l & 7
-      const uint32_t lo = (uint32_t)(((lane & 7) >> 1) * 128 + 8 * (lane >> 3) + 4 * (lane & 1));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dmab4(smr, slot + 2048 + 256 * i, lo, 2048 + 512 * (i >> 1) + 64 * (i & 1));
-    }
-    {  // V nibbles: gather j, lane l -> reader lane 16j + (l >> 2), word l & 3
-      const uint32_t lo = (uint32_t)(64 * (lane & 3) + 4 * (lane >> 2));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dmab4(nbr, slot + 5120 + 256 * j, lo, 1024 + 256 * j);
-    }
+    // V sm and nibbles as they are in memory
+    dmab16(smr, slot + 2048, (uint32_t)(lane * 16), 2048);
+    dmab16(smr, slot + 3072, (uint32_t)(lane * 16), 3072);
+    dmab16(nbr, slot + 5120, (uint32_t)(lane * 16), 1024);
   }
 
-  // One page's bytes as this lane needs them (read from LDS in one go).
+  // One page's bytes as this lane needs them (read from LDS in one go): K row krow(t) (sm,
+  // nibbles, spill piece, base byte), V rows qd + 4j (vs[j] sm, vn[j] nibbles, vh[j] spill, and
+  // the base words vb, base of row qd + 4j in byte 2 (qd & 1) + half of word j).
   struct Page {
-    u32x4 ks0, ks1, kn, kh, vs0, vs1, vn, vh;
+    u32x4 ks0, ks1, kn, kh;
+    u32x4 vs01, vs23;
+    u32x2 vn01, vn23, vh01, vh23;
     uint32_t kb;
-    u32x2 vb;
+    u32x4 vb;
   };
 
   // page n from its slot and meta slot ms, plus the issue metadata of a later page from ms2
   __device__ __forceinline__ Page read(int lane, uint32_t slot, uint32_t ms, uint32_t ms2, Issue& next) const {
     const int t = lane & 15, qd = lane >> 4;
-    const int sk = (t >> 1) & 7;
+    const int kr = krow(t);
+    const int sk = (kr >> 1) & 7;
     Page p;
     asm volatile(
-        "ds_read_b128 %0, %14\n\t"
-        "ds_read_b128 %1, %15\n\t"
-        "ds_read_b128 %2, %16\n\t"
-        "ds_read_b128 %3, %17 offset:1024\n\t"
-        "ds_read_b128 %4, %18\n\t"
-        "ds_read_b128 %5, %18 offset:16\n\t"
-        "ds_read_b128 %6, %17\n\t"
-        "ds_read_b128 %7, %17 offset:2048\n\t"
-        "ds_read_u8 %8, %19\n\t"
-        "ds_read_b64 %9, %20\n\t"
-        "ds_read_b32 %10, %21\n\t"
-        "ds_read_b32 %11, %22\n\t"
-        "ds_read_b128 %12, %23 offset:128\n\t"
-        "ds_read_b128 %13, %23\n\t"
+        "ds_read_b128 %0, %13\n\t"
+        "ds_read_b128 %1, %14\n\t"
+        "ds_read_b128 %2, %15\n\t"
+        "ds_read_b128 %3, %16\n\t"
+        "ds_read2st64_b64 %4, %17 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b64 %5, %17 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %6, %18 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %7, %18 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %8, %18 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b32 %9, %18 offset0:6 offset1:7\n\t"
+        "ds_read_u8 %10, %19\n\t"
+        "ds_read_b128 %11, %20\n\t"
+        "ds_read_b64 %12, %21\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(p.ks0), "=&v"(p.ks1), "=&v"(p.kn), "=&v"(p.kh), "=&v"(p.vs0), "=&v"(p.vs1),
-          "=&v"(p.vn), "=&v"(p.vh), "=&v"(p.kb), "=&v"(p.vb),
-          "=&v"(next.fk), "=&v"(next.sk), "=&v"(next.fv), "=&v"(next.sv)
-        : "v"(slot + t * 128 + ((2 * qd) ^ sk) * 16), "v"(slot + t * 128 + ((2 * qd + 1) ^ sk) * 16),
-          "v"(slot + 4096 + t * 64 + (qd ^ ((t >> 2) & 3)) * 16), "v"(slot + 5120 + lane * 16),
-          "v"(slot + 2048 + lane * 32), "v"(ms + 128 + 2 * t + (qd >> 1)), "v"(ms + 160 + 8 * qd),
-          "v"(ms2 + 4 * t), "v"(ms2 + 64 + 4 * (4 * (t & 3) + (t >> 2))), "v"(ms2 + 64 + 16 * (lane & 3))
+        : "=&v"(p.ks0), "=&v"(p.ks1), "=&v"(p.kn), "=&v"(p.kh), "=&v"(p.vs01), "=&v"(p.vs23),
+          "=&v"(p.vn01), "=&v"(p.vn23), "=&v"(p.vh01), "=&v"(p.vh23), "=&v"(p.kb), "=&v"(p.vb),
+          "=&v"(next.fs)
+        : "v"(slot + kr * 128 + ((2 * qd) ^ sk) * 16), "v"(slot + kr * 128 + ((2 * qd + 1) ^ sk) * 16),
+          "v"(slot + 4096 + kr * 64 + (qd ^ ((kr >> 2) & 3)) * 16),
+          "v"(slot + 7168 + kr * 64 + (qd ^ ((kr >> 2) & 3)) * 16),
+          "v"(slot + 2048 + qd * 128 + t * 8), "v"(slot + 5120 + qd * 64 + t * 4),
+          "v"(ms + 128 + 2 * kr + (qd >> 1)), "v"(ms + 160 + 16 * (qd >> 1)), "v"(ms2 + 8 * (lane >> 2))
         : "memory");
     return p;
   }
@@ -290,19 +280,21 @@ struct PackedLoader {
     }
   }
 
-  // V is rebuilt in groups of two token rows: group (q, hh) takes dims 4hh..4hh+3 of rows 2q
-  // and 2q + 1 as the 8 values of rebuild8 (row 2q first), so each rebuilt pair is already the
-  // (token, token + 1) pair the p.V operand wants.  The nibble and spill words of the two rows
-  // are joined by one byte permute; both rows' bases sit in one base word (bytes half and
-  // 2 + half), which one more permute spreads into the two halves.
+  // V is rebuilt in groups of two rows: group (q, hh) takes dims 4hh..4hh+3 of rows j = 2q and
+  // 2q + 1 (tokens qd + 8q and qd + 8q + 4) as the 8 values of rebuild8, so each rebuilt pair
+  // is already the token pair the p.V operand wants.  The nibble and spill words of the two rows
+  // are joined by one byte permute, and so are their base bytes.
   __device__ __forceinline__ void rebuild_v(const Page& p, int, int lane, uint32_t (&vt)[16]) const {
-    const uint32_t half = (uint32_t)((lane & 15) >> 3);
-    const uint32_t bsel = 0x0C000C00u | ((2u + half) << 16) | half;
-    const uint32_t vsw[8] = {p.vs0.x, p.vs0.y, p.vs0.z, p.vs0.w, p.vs1.x, p.vs1.y, p.vs1.z, p.vs1.w};
-    const uint32_t vna[4] = {p.vn.x, p.vn.y, p.vn.z, p.vn.w}, vha[4] = {p.vh.x, p.vh.y, p.vh.z, p.vh.w};
+    const uint32_t t = (uint32_t)(lane & 15), qd = (uint32_t)(lane >> 4);
+    const uint32_t by = 2u * (qd & 1u) + (t >> 3);  // base byte of the lane's rows in vb
+    const uint32_t bsel = 0x0C000C00u | ((4u + by) << 16) | by;
+    const uint32_t vsw[8] = {p.vs01.x, p.vs01.y, p.vs01.z, p.vs01.w, p.vs23.x, p.vs23.y, p.vs23.z, p.vs23.w};
+    const uint32_t vna[4] = {p.vn01.x, p.vn01.y, p.vn23.x, p.vn23.y};
+    const uint32_t vha[4] = {p.vh01.x, p.vh01.y, p.vh23.x, p.vh23.y};
+    const uint32_t vbw[4] = {p.vb.x, p.vb.y, p.vb.z, p.vb.w};
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t b16 = __builtin_amdgcn_perm(0u, q ? p.vb.y : p.vb.x, bsel);
+      const uint32_t b16 = __builtin_amdgcn_perm(vbw[2 * q + 1], vbw[2 * q], bsel);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
@@ -342,8 +334,10 @@ struct RawLoader {
     u32x4 k[4], v[4];
   };
 
+  // K row krow(t) (quarter qd), V rows qd + 4j (head_dim 8t..8t+7)
   __device__ __forceinline__ Page read(int lane, uint32_t slot, uint32_t, uint32_t, Issue&) const {
     const int t = lane & 15, qd = lane >> 4;
+    const int kr = krow(t);
     Page p;
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
@@ -351,15 +345,15 @@ struct RawLoader {
         "ds_read_b128 %2, %10\n\t"
         "ds_read_b128 %3, %11\n\t"
         "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %12 offset:256\n\t"
-        "ds_read_b128 %6, %12 offset:512\n\t"
-        "ds_read_b128 %7, %12 offset:768\n\t"
+        "ds_read_b128 %5, %12 offset:1024\n\t"
+        "ds_read_b128 %6, %12 offset:2048\n\t"
+        "ds_read_b128 %7, %12 offset:3072\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(p.k[0]), "=&v"(p.k[1]), "=&v"(p.k[2]), "=&v"(p.k[3]), "=&v"(p.v[0]), "=&v"(p.v[1]),
           "=&v"(p.v[2]), "=&v"(p.v[3])
-        : "v"(slot + t * 256 + ((4 * qd + 0) ^ t) * 16), "v"(slot + t * 256 + ((4 * qd + 1) ^ t) * 16),
-          "v"(slot + t * 256 + ((4 * qd + 2) ^ t) * 16), "v"(slot + t * 256 + ((4 * qd + 3) ^ t) * 16),
-          "v"(slot + 4096 + qd * 1024 + t * 16)
+        : "v"(slot + kr * 256 + ((4 * qd + 0) ^ kr) * 16), "v"(slot + kr * 256 + ((4 * qd + 1) ^ kr) * 16),
+          "v"(slot + kr * 256 + ((4 * qd + 2) ^ kr) * 16), "v"(slot + kr * 256 + ((4 * qd + 3) ^ kr) * 16),
+          "v"(slot + 4096 + qd * 256 + t * 16)
         : "memory");
     return p;
   }
@@ -526,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   __syncthreads();
 
   double m = -INFINITY;  // running max of head `head`'s unscaled scores (fp64)
-  double l = 0.0;        // this lane's share of head `head`'s weight sum (tokens 4qd..4qd+3)
+  double l = 0.0;        // this lane's share of head `head`'s weight sum (tokens qd + 4i)
   // p.V output: lane (t, qd) receives rows 4qd..4qd+3 = the hi, mid, lo parts (and an empty
   // fourth row) of head qd at head_dim vdim(n, t).  The parts of each page's MFMA (which
   // starts from zero) are summed here in fp64: with outlier values the running sum reaches
@@ -566,10 +560,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       const bf16x8 ka = __builtin_bit_cast(bf16x8, (u32x4){kp[4 * c], kp[4 * c + 1], kp[4 * c + 2], kp[4 * c + 3]});
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c], sc, 0, 0, 0);
     }
-    // sc[i]: token 4qd + i, head `head`; tokens past the end of the page count as -inf
+    // sc[i]: token qd + 4i, head `head`; tokens past the end of the page count as -inf
     if (ntok < kT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = 4 * qd + i < ntok ? sc[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) sc[i] = qd + 4 * i < ntok ? sc[i] : -INFINITY;
     }
     const float pm32 = rows_max(max_f32(max3_f32(sc[0], sc[1], sc[2]), sc[3]));
     // A score needs the exact path when it is large (one fp32 ulp of it is then a visible
@@ -581,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     for (int i = 0; i < 4; ++i) big |= fabsf(sc[i]) > kBigScore && sc[i] > floor32;
     double sd[4], pm;
     if (__any(big)) {
-      // exact fp64 scores: lane (t, qd) sums its 32 dims of token t for the 4 heads, the four
+      // exact fp64 scores: lane (t, qd) sums its 32 dims of token krow(t) for the 4 heads, the four
       // quarters are added, and each lane then fetches its own (token, head) entries
       double pd[kG] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -599,7 +593,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       for (int i = 0; i < kG; ++i) {
         pd[i] = rows_sum_d(pd[i]);
       }
-      // lane (t', qd') offers head qd' of token t'; lane (t, qd) reads token 4qd + i, head t >> 2
+      // lane (t', qd') offers head qd' of token krow(t'); lane (t, qd) reads token qd + 4i =
+      // krow(4qd + i), head t >> 2
       const double offer = qd == 0 ? pd[0] : qd == 1 ? pd[1] : qd == 2 ? pd[2] : pd[3];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -616,6 +611,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     // V is rebuilt here, where its independent work can fill the latency of the maxima
     uint32_t vt[16];
     ld.rebuild_v(pg, h, lane, vt);
+    // tokens past the end of the page: their weights are zero, but their rows hold whatever
+    // the memory holds, and 0 * Inf or NaN would not be zero
+    if (ntok < kT) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t keep = (qd + 8 * q < ntok ? 0x0000FFFFu : 0u) | (qd + 8 * q + 4 < ntok ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) vt[2 * nn + q] &= keep;
+      }
+    }
     if (__any(pm > m)) {
       const double mn = fmax(m, pm);
       const double alpha = exp2((m - mn) * c2);

@@ -145,8 +145,9 @@ def test_attention_maxcap_64_steps_sampled():
     assert np.array_equal(host(s.seqs.seq_lens), lens)
 
 
-@pytest.mark.parametrize("lens", [[0, 1, 2], [15, 16, 17], [31, 32, 33, 64], [1, 200, 0, 129, 16]])
-def test_edge_lengths(lens):
+def edge_instance(lens, fill=0):
+    """SMALL-shaped pages for exactly these lengths, physically shuffled, every slot that is
+    not a token row set to the u16 `fill`."""
     w = SMALL.replace(batch=len(lens), ctx_min=1, ctx_max=1, extra_tokens=0, seed=31)
     inst = synth.make(w, fill=False)
     inst.seq_lens[:] = lens
@@ -162,11 +163,16 @@ def test_edge_lengths(lens):
         n = -(-L // T)
         pt[b, :n] = perm[nxt:nxt + n]
         nxt += n
-    raw = np.zeros((npages, w.num_kv_heads, 2, T, w.head_dim), np.uint16)
+    raw = np.full((npages, w.num_kv_heads, 2, T, w.head_dim), fill, np.uint16)
     synth.fill_pages(w, inst.seq_lens, pt, raw, 0, max(lens))
-    inst = synth.Instance(w, inst.seq_lens, pt, npages, raw)
+    return synth.Instance(w, inst.seq_lens, pt, npages, raw)
+
+
+@pytest.mark.parametrize("lens", [[0, 1, 2], [15, 16, 17], [31, 32, 33, 64], [1, 200, 0, 129, 16]])
+def test_edge_lengths(lens):
+    inst = edge_instance(lens)
     s = Setup(inst)
-    q = synth.query(w, 0)
+    q = synth.query(inst.w, 0)
     out = s.attention(q)
     assert s.status() == 0
     check(out, inst, inst.seq_lens, q, what=f"lens {lens}")
@@ -174,6 +180,27 @@ def test_edge_lengths(lens):
     for b, L in enumerate(lens):
         if L == 0:
             assert not g[b].any()
+    assert torch.equal(out, s.attention(q, packed=False))
+
+
+@pytest.mark.parametrize("lens", [[15, 17, 1, 31], [16, 33, 250, 0]])
+def test_rows_past_the_end_are_never_data(lens):
+    """Slots at or past seq_lens hold whatever memory holds (the format leaves them undefined).
+    Here every such byte is all ones: NaN bf16 in the twin's pages; sm 0xFF, nibble 15, base
+    255, every block flagged raw with first spill slot 2^32 - 1, spill bytes 0xFF in the packed
+    cache (the rows below seq_lens are encoded over it).  Their weights are zero, and the
+    outputs must still be the oracle's and the twin's."""
+    inst = edge_instance(lens, fill=0xFFFF)
+    s = Setup(inst, encode=False)
+    for a in (s.cache.sm, s.cache.nib, s.cache.base, s.cache.row_flags, s.cache.row_spill,
+              s.cache.spill):
+        a.fill_(-1 if a.dtype == torch.int32 else 255)
+    zf.zf_encode_kv(s.cache, s.seqs, s.raw, zf.encode_workspace(s.seqs))
+    q = synth.query(inst.w, 0)
+    out = s.attention(q)
+    assert s.status() == 0
+    assert torch.isfinite(out).all()
+    check(out, inst, inst.seq_lens, q, what=f"poisoned tail, lens {lens}")
     assert torch.equal(out, s.attention(q, packed=False))
 
 
