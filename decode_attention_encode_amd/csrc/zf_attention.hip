@@ -49,6 +49,10 @@ constexpr int kD = 128, kT = 16, kG = 4, kWaves = 8, kThreads = 64 * kWaves;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr float kBigScore = 64.f;  // |q.k| above which a score may need the fp64 path
 constexpr double kNegligible = 16.0;  // weights below 2^-16 of the largest never need it
+// The hi row of p.V (below) sums this many pages in the MFMA's fp32 accumulator before it is
+// added in fp64: each MFMA rounds to a few fp32 ulps of its largest term, so a few pages of
+// weights <= 1 keep the row within ~2^-19 of its value.
+constexpr int kFlushPages = 4;
 constexpr int kMaxPagesPerSplit = kWaves * 64;
 constexpr uint32_t kXcds = 8;  // MI355X: workgroups are dispatched round-robin over 8 XCDs  // each wave keeps its page ids in one register
 // One split's partial, in doubles: acc[kG][kD], l[kG], m[kG].
@@ -181,7 +185,8 @@ struct PackedLoader {
   // blocks carry base 0.  The rebuild then needs no raw flag at all.
   __device__ __forceinline__ uint32_t spill_off(uint32_t flags, uint32_t first, int j, uint32_t piece) const {
     const uint32_t slot = (uint32_t)__popc(flags & ((1u << j) - 1u)) + first;
-    return ((flags >> j) & 1u) ? slot * 32u + piece : 0xFFFFFFFFu;
+    const uint32_t raw = (uint32_t)__builtin_amdgcn_sbfe((int)flags, j, 1);  // all ones iff raw
+    return bitselect(raw, slot * 32u + piece, 0xFFFFFFFFu);
   }
 
   // The row metadata issue_page needs, read from a meta slot ahead of time: flags and first
@@ -533,6 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     cacc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const double c2 = a.scale_log2e;
+  const float c2f = (float)c2;
   double mc2 = 0.0;        // m * c2 once m is finite
   float m32 = -INFINITY;   // m in fp32, for the exact-path test
   const float negl32 = (float)(kNegligible / c2);
@@ -574,37 +580,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) big |= fabsf(sc[i]) > kBigScore && sc[i] > floor32;
     double sd[4], pm;
-    if (__any(big)) {
-      // exact fp64 scores: lane (t, qd) sums its 32 dims of token krow(t) for the 4 heads, the four
-      // quarters are added, and each lane then fetches its own (token, head) entries
-      double pd[kG] = {0.0, 0.0, 0.0, 0.0};
+    const bool exact = __any(big);
+    if (exact) {
+      // exact fp64 scores for the heads that hold such a score (a page usually has one or two):
+      // lane (t, qd) sums its 32 dims of token krow(t) for each of them, the four quarters are
+      // added, and each lane then fetches its own (token, head) entries.  Heads without one keep
+      // their fp32 scores.
+      const uint64_t bm = __ballot(big);  // bit 16 qd + t: head t >> 2
+      const uint32_t cols = (uint32_t)(bm | (bm >> 16) | (bm >> 32) | (bm >> 48)) & 0xFFFFu;
+      float klo[16], khi[16];  // this lane's K values, exact in fp32
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const double klo = (double)__uint_as_float(kp[k] << 16);
-        const double khi = (double)__uint_as_float(kp[k] & 0xFFFF0000u);
-#pragma unroll
-        for (int i = 0; i < kG; ++i) {
-          const double2 qq = s_q64[i][qd][k];
-          pd[i] = fma(qq.x, klo, pd[i]);
-          pd[i] = fma(qq.y, khi, pd[i]);
-        }
+        klo[k] = __uint_as_float(kp[k] << 16);
+        khi[k] = __uint_as_float(kp[k] & 0xFFFF0000u);
       }
+      double pd[kG];
 #pragma unroll
       for (int i = 0; i < kG; ++i) {
-        pd[i] = rows_sum_d(pd[i]);
+        pd[i] = 0.0;
+        if ((cols >> (4 * i)) & 0xFu) {  // wave-uniform
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const double2 qq = s_q64[i][qd][k];
+            pd[i] = fma(qq.x, (double)klo[k], pd[i]);
+            pd[i] = fma(qq.y, (double)khi[k], pd[i]);
+          }
+          pd[i] = rows_sum_d(pd[i]);
+        }
       }
       // lane (t', qd') offers head qd' of token krow(t'); lane (t, qd) reads token qd + 4i =
       // krow(4qd + i), head t >> 2
       const double offer = qd == 0 ? pd[0] : qd == 1 ? pd[1] : qd == 2 ? pd[2] : pd[3];
+      const bool mine = (cols >> (4 * head)) & 0xFu;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const double x = __shfl(offer, head * 16 + 4 * qd + i, 64);
-        sd[i] = sc[i] == -INFINITY ? -INFINITY : x;  // keeps the tokens past the end out
+        // tokens past the end stay out; heads without a big score keep the fp32 one
+        sd[i] = sc[i] == -INFINITY ? -INFINITY : mine ? x : (double)sc[i];
       }
       pm = rows_max_d(max_f64(max_f64(sd[0], sd[1]), max_f64(sd[2], sd[3])));
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sd[i] = (double)sc[i];
       pm = (double)pm32;  // the same maximum
     }
 
@@ -633,17 +648,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) {
         acc[nn] *= al;
+        cacc[nn][0] *= alf;
         cacc[nn][1] *= alf;
         cacc[nn][2] *= alf;
       }
     }
-    // weights 2^((s - m) c2); a page seen before any finite score leaves m = -inf and mc2 = 0
+    // weights 2^((s - m) c2); a page seen before any finite score leaves m = -inf and mc2 = 0.
+    // Off the exact path every score that can matter has |s| <= kBigScore, so the running
+    // maximum is below kBigScore + kNegligible / c2 and the exponent, formed in fp32, is off by
+    // a few 1e-7 at most (an fp64 exponent is rounded to fp32 for the exp anyway).
     float p[4];
+    if (exact) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f((float)fma(sd[i], c2, -mc2));
-      l += p[i];
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f((float)fma(sd[i], c2, -mc2));
+    } else {
+      const float mc2f = (float)mc2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2f, -mc2f));
     }
+    l += (double)((p[0] + p[1]) + (p[2] + p[3]));  // 4 values <= 1: fp32 to a few 1e-7
     // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo, all
     // three by truncation: hi = the top 8 significant bits of p, mid those of x1 = p - hi,
     // lo = x1 - mid (at most 8 bits left).  The differences are exact, so the three parts
@@ -658,15 +681,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     // the high halves (the truncated bf16 parts) of two values per register
     const s16x4 pa = __builtin_bit_cast(s16x4, (u32x2){__builtin_amdgcn_perm(xb[1], xb[0], 0x07060302u),
                                                         __builtin_amdgcn_perm(xb[3], xb[2], 0x07060302u)});
-    // rows 4qd + (0, 1, 2): hi, mid, lo parts of head qd.  The hi row restarts from zero on
-    // every page and is added in fp64; mid and lo (below 2^-8 of it) accumulate in the MFMA.
+    // rows 4qd + (0, 1, 2): hi, mid, lo parts of head qd.  The hi row is moved to fp64 every
+    // kFlushPages pages; mid and lo (below 2^-8 of it) accumulate in the MFMA throughout.
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
       const s16x4 vb = __builtin_bit_cast(s16x4, (u32x2){vt[2 * nn], vt[2 * nn + 1]});
-      const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, cacc[nn], 0, 0, 0);
-      acc[nn] += (double)d[0];
-      cacc[nn] = d;
-      cacc[nn][0] = 0.f;
+      cacc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, cacc[nn], 0, 0, 0);
+    }
+    if ((n & (kFlushPages - 1)) == kFlushPages - 1) {
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) {
+        acc[nn] += (double)cacc[nn][0];
+        cacc[nn][0] = 0.f;
+      }
     }
   };
 
@@ -716,7 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   // ---- per-wave results to the wave's own LDS region: lane (t, qd) holds head qd at
   //      head_dim vdim(n, t)
 #pragma unroll
-  for (int nn = 0; nn < 8; ++nn) acc[nn] += (double)cacc[nn][1] + (double)cacc[nn][2];
+  for (int nn = 0; nn < 8; ++nn) acc[nn] += (double)cacc[nn][0] + (double)cacc[nn][1] + (double)cacc[nn][2];
   l = rows_sum_d(l);
   double* w_acc = reinterpret_cast<double*>(&s_ring[wave][0]);  // [kG][kD], then m[kG], l[kG]
 #pragma unroll
