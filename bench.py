@@ -248,8 +248,9 @@ def main():
 
 
 def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_bytes):
-    """Twin (uncompressed) attention over the same rotation of layer caches, the single-layer
-    warm-cache loop, and full-cache encode / decode rates."""
+    """Twin (uncompressed) attention over the same rotation of layer caches, the unfused
+    alternative (decode to bf16, then the twin), a plain streaming read over the same bytes,
+    the single-layer warm-cache loop, and full-cache encode / decode rates."""
     res = {}
     stream = torch.cuda.current_stream()
     NL = len(layers)
@@ -280,6 +281,24 @@ def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_byte
     res["attention_packed_us"] = round(t_pack * 1e6, 2)
     res["attention_twin_uncompressed_us"] = round(t_twin * 1e6, 2)
     res["speedup_vs_uncompressed_twin"] = round(t_twin / t_pack, 3)
+    # the unfused alternative: decode the layer's cache to bf16 pages, then the raw kernel
+    scratch = torch.empty_like(raw)
+
+    def unfused(i):
+        cache, seqs = layers[i % NL]
+        zf.zf_decode_kv(cache, seqs, scratch)
+        zf.zf_decode_attention_raw(scratch, seqs, q, scale, out, ws, status)
+    t_unf = timeit(unfused)
+    res["unfused_decode_then_twin_us"] = round(t_unf * 1e6, 2)
+    res["speedup_vs_unfused"] = round(t_unf / t_pack, 3)
+    del scratch
+    # a plain stream over the same rotation of (uncompressed) buffers: the read rate this GPU
+    # achieves at all, context for the attention kernel's
+    sink = torch.empty(zf.ZF_PROBE_BLOCKS, dtype=torch.int32, device=raw.device)
+    t_rd = timeit(lambda i: zf.zf_stream_read_probe(twins[i % NL], sink))
+    rd_bytes = twins[0].numel() * twins[0].element_size()
+    res["stream_read_probe_GBps"] = round(rd_bytes / t_rd / 1e9, 1)
+    res["stream_read_probe_bytes"] = rd_bytes
     res["attention_single_layer_warm_us"] = round(t_warm * 1e6, 2)
     res["attention_single_layer_warm_GBps"] = round(attn_bytes / t_warm / 1e9, 1)
     # full-cache encode and decode of one layer (the lengths as they are now)

@@ -22,7 +22,8 @@ ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN = 1, 2, 4
 EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_append_kv",
            "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_raw",
            "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
-           "zf_get_status", "zf_status_str")
+           "zf_stream_read_probe", "zf_get_status", "zf_status_str")
+ZF_PROBE_BLOCKS = 4096
 
 
 class ZfError(RuntimeError):
@@ -72,6 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "zf_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "zf_attention_workspace_init": (ctypes.c_int, [vp, sz, vp]),
         "zf_time_next_attention": (ctypes.c_int, [vp, vp]),
+        "zf_stream_read_probe": (ctypes.c_int, [vp, sz, vp, vp]),
         "zf_get_status": (ctypes.c_int, [vp, vp, vp]),
         "zf_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -215,6 +217,13 @@ def zf_time_next_attention(start: "torch.cuda.Event | None", stop: "torch.cuda.E
     a = None if start is None else start.cuda_event
     b = None if stop is None else stop.cuda_event
     _check(load().zf_time_next_attention(a, b), "zf_time_next_attention")
+
+
+def zf_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Reads all of `buf` once with the library's plain streaming kernel; `sink` holds
+    ZF_PROBE_BLOCKS u32 checksums afterwards."""
+    _check(load().zf_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                       _stream(stream)), "zf_stream_read_probe")
 
 
 def zf_get_status(status: torch.Tensor, stream=None) -> int:

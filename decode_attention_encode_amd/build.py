@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzf.so")
-SOURCES = ["zf_api.hip", "zf_codec.hip", "zf_attention.hip"]
+SOURCES = ["zf_api.hip", "zf_codec.hip", "zf_attention.hip", "zf_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # packed fp32 ops (v_pk_*_f32) stay off: ordinary float code only

@@ -1,0 +1,55 @@
+// zf_probe.hip - a plain streaming read of device memory (gfx950), the practically achievable
+// HBM read rate against which the attention kernel's bandwidth is read.  Measurement aid,
+// outside the method.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/zf.h"
+
+namespace zf {
+
+constexpr int kProbeThreads = 512;
+constexpr int kProbeUnroll = 4;
+
+// Block b reads its contiguous share of the buffer, 4 x 16 bytes per thread in flight, and
+// leaves the XOR of everything it read in sink[b] (so no load can be dropped).
+__global__ __launch_bounds__(kProbeThreads) void stream_read_k(const uint4* __restrict__ p, uint64_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const uint64_t b0 = (uint64_t)blockIdx.x * per, b1 = min(n16, b0 + per);
+  uint32_t x = 0;
+  for (uint64_t i = b0 + threadIdx.x; i < b1; i += kProbeUnroll * kProbeThreads) {
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const uint64_t j = i + (uint64_t)u * kProbeThreads;
+      if (j < b1) {
+        const uint4 v = p[j];
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+      }
+    }
+  }
+  // XOR over the block: wave, then waves through LDS
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
+  __shared__ uint32_t s_x[kProbeThreads / 64];
+  if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+    for (int w = 0; w < kProbeThreads / 64; ++w) y ^= s_x[w];
+    sink[blockIdx.x] = y;
+  }
+}
+
+}  // namespace zf
+
+extern "C" zf_status zf_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, zf_stream_t stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || (uintptr_t)buf % 16 != 0) return ZF_EINVAL;
+  const uint64_t n16 = bytes / 16;
+  const uint64_t per_block = (uint64_t)zf::kProbeThreads * zf::kProbeUnroll;
+  const uint32_t blocks = (uint32_t)std::min<uint64_t>(ZF_PROBE_BLOCKS, (n16 + per_block - 1) / per_block);
+  hipLaunchKernelGGL(zf::stream_read_k, dim3(blocks), dim3(zf::kProbeThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(buf), n16, sink);
+  return hipGetLastError() == hipSuccess ? ZF_OK : ZF_EHIP;
+}

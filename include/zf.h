@@ -158,6 +158,14 @@ zf_status zf_attention_workspace_init(void* workspace, size_t workspace_bytes,
  * timing-enabled hipEvent_t handles, or both NULL (clears).  ZF_EINVAL if exactly one is NULL. */
 zf_status zf_time_next_attention(void* start_event, void* stop_event);
 
+/* Measurement aid, outside the method: reads `bytes` of device memory at `buf` once, with
+ * 16-byte loads spread over up to ZF_PROBE_BLOCKS workgroups (a plain stream: the practically
+ * achievable HBM read rate, context for the attention kernel's).  sink: device u32
+ * [ZF_PROBE_BLOCKS], receives a checksum per workgroup.  bytes > 0, a multiple of 16, and buf
+ * 16-byte aligned, else ZF_EINVAL.  One kernel launch. */
+#define ZF_PROBE_BLOCKS 4096
+zf_status zf_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, zf_stream_t stream);
+
 /* Copies the sticky status word to *host_status (synchronizes `stream`). */
 zf_status zf_get_status(const uint32_t* status, uint32_t* host_status, zf_stream_t stream);
 const char* zf_status_str(zf_status s);

@@ -124,6 +124,16 @@ def test_time_next_attention_arguments():
     assert lib.zf_time_next_attention(None, 4096) == zf.ZF_EINVAL
 
 
+def test_stream_read_probe_arguments():
+    lib = zf.load()
+    # rejected on the host, nothing launched: null buffer or sink, zero or ragged sizes, misalignment
+    assert lib.zf_stream_read_probe(None, 4096, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_read_probe(4096, 4096, None, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_read_probe(4096, 0, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_read_probe(4096, 4100, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_read_probe(4104, 4096, 4096, None) == zf.ZF_EINVAL
+
+
 def test_attention_rejects_spill_pool_beyond_32bit_offsets():
     lib = zf.load()
     s = zf.zf_seqs(1, 1, 4096, 4096, 16)
