@@ -53,6 +53,13 @@ constexpr double kNegligible = 16.0;  // weights below 2^-16 of the largest neve
 // added in fp64: each MFMA rounds to a few fp32 ulps of its largest term, so a few pages of
 // weights <= 1 keep the row within ~2^-19 of its value.
 constexpr int kFlushPages = 4;
+// The exact-path test takes the largest score that the waves of the workgroup had seen
+// kShareLag steps earlier as a lower bound of the final maximum (it depends on the data only,
+// not on timing, so results stay bitwise repeatable).  A wave waits when it gets more than
+// kShareLag steps ahead of the slowest one; ring slots are reused after kShareRing steps.
+constexpr int kShareLag = 3;
+constexpr int kShareRing = 8;  // > 2 * kShareLag: no slot is rewritten while it may be read
+constexpr uint32_t kDone = 0x7FFFFFFFu;  // progress of a wave that has finished its pages
 constexpr int kMaxPagesPerSplit = kWaves * 64;
 constexpr uint32_t kXcds = 8;  // MI355X: workgroups are dispatched round-robin over 8 XCDs  // each wave keeps its page ids in one register
 // One split's partial, in doubles: acc[kG][kD], l[kG], m[kG].
@@ -106,6 +113,14 @@ __device__ __forceinline__ void lds_store_u32(uint32_t addr, uint32_t v) {
 __device__ __forceinline__ uint32_t lds_load_u32(uint32_t addr) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_max_f64(uint32_t addr, double v) {
+  asm volatile("ds_max_f64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ double lds_load_f64(uint32_t addr) {
+  double v;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
   return v;
 }
 template <int N>
@@ -477,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   if (s >= nsplit) return;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
-  __shared__ uint32_t s_prog[kWaves];  // pages finished by each wave
+  __shared__ uint32_t s_prog[kWaves];  // steps whose running maximum each wave has published
   const uint32_t ring = (uint32_t)(uintptr_t)&s_ring[wave][0];
   const uint32_t meta_ring = ring + 2 * kSlotBytes;
 
@@ -521,7 +536,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   // pin the q unpacking here: placed after the first page loads, its wait for q would also
   // wait for them
   asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
-  if (lane == 0) s_prog[wave] = 0u;
+  __shared__ double s_gmax[kShareRing][kG];  // per step: max over the waves' running maxima
+  if (tid < kShareRing * kG) s_gmax[tid / kG][tid % kG] = -INFINITY;
+  if (lane == 0) s_prog[wave] = nmine > 0 ? 0u : kDone;
   __syncthreads();
 
   double m = -INFINITY;  // running max of head `head`'s unscaled scores (fp64)
@@ -542,6 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   double mc2 = 0.0;        // m * c2 once m is finite
   float m32 = -INFINITY;   // m in fp32, for the exact-path test
   const float negl32 = (float)(kNegligible / c2);
+  float shared32 = -INFINITY;  // the workgroup's maximum kShareLag steps ago (fp32)
 
   // page n of this wave; indices past the end repeat the last page (their loads keep the
   // per-page load count fixed and are never used)
@@ -575,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     // A score needs the exact path when it is large (one fp32 ulp of it is then a visible
     // change of its weight) and its weight can matter: scores more than kNegligible / c2
     // below the running maximum get a weight under 2^-kNegligible of the largest one.
-    const float floor32 = max_f32(m32, pm32) - negl32;
+    const float floor32 = max_f32(max_f32(m32, pm32), shared32) - negl32;
     bool big = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) big |= fabsf(sc[i]) > kBigScore && sc[i] > floor32;
@@ -718,11 +736,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     // finishes well before w + 4, which then runs by itself at half occupancy.  Each step, the
     // wave of the pair that is behind raises its priority (the pages each wave takes are fixed,
     // so the results do not depend on this).
-    const uint32_t prog_me = (uint32_t)(uintptr_t)&s_prog[wave];
-    const uint32_t prog_other = (uint32_t)(uintptr_t)&s_prog[wave ^ 4];
+    const uint32_t prog_base = (uint32_t)(uintptr_t)&s_prog[0];
+    const uint32_t gmax_base = (uint32_t)(uintptr_t)&s_gmax[0][0];
+    auto gmax_at = [&](int step) -> uint32_t {
+      return gmax_base + (uint32_t)(((step & (kShareRing - 1)) * kG + head) * 8);
+    };
     for (int n = 0; n < nmine; ++n) {
-      lds_store_u32(prog_me, (uint32_t)n);
-      if (n > __builtin_amdgcn_readfirstlane(lds_load_u32(prog_other))) __builtin_amdgcn_s_setprio(0);
+      // step n's running maximum (pages before n) into the workgroup's maximum of step n
+      if (lane < 16 && part == 0) lds_max_f64(gmax_at(n), m);
+      lds_store_u32(prog_base + 4 * wave, (uint32_t)n + 1);
+      uint32_t prog = lds_load_u32(prog_base + 4 * (lane & (kWaves - 1)));
+      if (n >= kShareLag) {
+        const uint32_t need = (uint32_t)(n - kShareLag) + 1;  // every wave past step n - lag
+        while (!__all(prog >= need)) {
+          __builtin_amdgcn_s_sleep(1);
+          prog = lds_load_u32(prog_base + 4 * (lane & (kWaves - 1)));
+        }
+        shared32 = (float)lds_load_f64(gmax_at(n - kShareLag));
+      }
+      if ((uint32_t)n + 1 > __builtin_amdgcn_readlane(prog, wave ^ 4)) __builtin_amdgcn_s_setprio(0);
       else __builtin_amdgcn_s_setprio(2);
       // every load of step n - 2 and earlier has landed: page n, metas up to n + 4
       wait_vm<kP + kM>();
@@ -735,7 +767,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       compute(n, pg);
     }
     wait_vm<0>();  // the loads past the end still target this wave's LDS
-    lds_store_u32(prog_me, 0x7FFFFFFFu);  // done: never hold the partner back
+    if (lane < 16 && part == 0) lds_max_f64(gmax_at(nmine), m);  // the final maximum
+    lds_store_u32(prog_base + 4 * wave, kDone);  // done: never hold the others back
     __builtin_amdgcn_s_setprio(0);
   }
   if (err) set_status(a.status, err);
