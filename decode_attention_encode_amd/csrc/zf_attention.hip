@@ -481,21 +481,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const uint32_t mask1 = part == 0 ? 0u : part == 3 ? 0xFFFFFFFFu : 0xFFFF0000u;
   const uint32_t mask2 = part == 2 ? 0xFFFF0000u : 0u;
 
-  int32_t L = a.lens[b];
-  const int32_t cap = min(a.maxp * kT, a.max_seq_len);
-  if (L < 0 || L > cap) {
-    if (s == 0 && tid == 0) set_status(a.status, ZF_DEV_ELEN);
-    L = L < 0 ? 0 : cap;
-  }
-  const int npages = (L + kT - 1) / kT;
-  const int nsplit = max(1, (npages + a.pps - 1) / a.pps);
-  if (s >= nsplit) return;
-
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
-  __shared__ uint32_t s_prog[kWaves];  // steps whose running maximum each wave has published
-  const uint32_t ring = (uint32_t)(uintptr_t)&s_ring[wave][0];
-  const uint32_t meta_ring = ring + 2 * kSlotBytes;
-
+  // this wave's pages: p_first + 8n; lane n reads the page id of page n.  The table row and q
+  // are read together with the length, not after it (one memory round trip less before the
+  // first page); table entries past the sequence's end are never used.
+  const int p_first = s * a.pps + wave;
+  int32_t pt_lane = 0;
+  if (p_first + kWaves * lane < a.maxp) pt_lane = a.pt[(int64_t)b * a.maxp + p_first + kWaves * lane];
   // B operand of the score MFMA: column t is query head t >> 2 (each head four times),
   // head_dim 32*qd + 8c + (0,4,1,5,2,6,3,7)[k]
   bf16x8 qb[4];
@@ -510,6 +501,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       qb[c] = __builtin_bit_cast(bf16x8, (u32x4){p[0], p[1], p[2], p[3]});
     }
   }
+  int32_t L = a.lens[b];
+  const int32_t cap = min(a.maxp * kT, a.max_seq_len);
+  if (L < 0 || L > cap) {
+    if (s == 0 && tid == 0) set_status(a.status, ZF_DEV_ELEN);
+    L = L < 0 ? 0 : cap;
+  }
+  const int npages = (L + kT - 1) / kT;
+  const int nsplit = max(1, (npages + a.pps - 1) / a.pps);
+  if (s >= nsplit) return;
+
   // q in fp64, pair order, for the exact-score path: [head][quarter][pair] = (lo, hi) dims
   __shared__ double2 s_q64[kG][4][16];
   if (tid < kG * 64) {
@@ -520,14 +521,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
                                    (double)__uint_as_float((uint32_t)qrow[dlo + 4] << 16));
   }
 
-  // this wave's pages: p_first + 4n for n < nmine; lane n holds the page id of page n
-  const int p_first = s * a.pps + wave;
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
+  __shared__ uint32_t s_prog[kWaves];  // steps whose running maximum each wave has published
+  const uint32_t ring = (uint32_t)(uintptr_t)&s_ring[wave][0];
+  const uint32_t meta_ring = ring + 2 * kSlotBytes;
+
+  // lane n holds the page id of page n < nmine
   const int p_end = min(npages, (s + 1) * a.pps);
   const int nmine = p_first < p_end ? (p_end - p_first + kWaves - 1) / kWaves : 0;
   int32_t my_pid = 0;
   uint32_t err = 0;
   if (lane < nmine) {
-    my_pid = a.pt[(int64_t)b * a.maxp + p_first + kWaves * lane];
+    my_pid = pt_lane;
     if (my_pid < 0 || my_pid >= a.num_pages) {
       err = ZF_DEV_EPAGE;
       my_pid = -1;  // page skipped: read page 0, count no token
@@ -794,22 +799,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   double* part_out = a.part + (unit * a.nsplit_max + s) * kPartDoubles;
   __shared__ double s_f[kWaves][kG];
   __shared__ double s_lsum[kG];
-  if (tid < kG) {
+  if (tid < kG * kWaves) {  // thread (head i, wave w2), in wave 0: lanes 8i..8i+7 hold head i
+    const int i = tid >> 3, w2 = tid & (kWaves - 1);
     double mm = -INFINITY;
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) mm = fmax(mm, wres(w2)[kG * kD + tid]);
-    double lsum = 0.0;
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      const double mw = wres(w2)[kG * kD + tid];
-      const double f = mw == -INFINITY ? 0.0 : exp2((mw - mm) * c2);
-      s_f[w2][tid] = f;
-      lsum += f * wres(w2)[kG * kD + kG + tid];
-    }
-    s_lsum[tid] = lsum;
-    if (!a.direct) {
-      part_out[kG * kD + tid] = lsum;
-      part_out[kG * kD + kG + tid] = mm;
+    for (int w3 = 0; w3 < kWaves; ++w3) mm = fmax(mm, wres(w3)[kG * kD + i]);
+    const double mw = wres(w2)[kG * kD + i];
+    const double f = mw == -INFINITY ? 0.0 : exp2((mw - mm) * c2);
+    s_f[w2][i] = f;
+    double lsum = f * wres(w2)[kG * kD + kG + i];
+    lsum += __shfl_xor(lsum, 1, 64);
+    lsum += __shfl_xor(lsum, 2, 64);
+    lsum += __shfl_xor(lsum, 4, 64);
+    if (w2 == 0) {
+      s_lsum[i] = lsum;
+      if (!a.direct) {
+        part_out[kG * kD + i] = lsum;
+        part_out[kG * kD + kG + i] = mm;
+      }
     }
   }
   __syncthreads();
