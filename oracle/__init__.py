@@ -42,7 +42,8 @@ def _load():
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
             build()
         lib = ctypes.CDLL(_LIB)
-        for name in ("orc_encode_kv", "orc_append_kv", "orc_decode_kv", "orc_attention"):
+        for name in ("orc_encode_kv", "orc_append_kv", "orc_append_kv_n", "orc_decode_kv",
+                     "orc_attention"):
             getattr(lib, name).restype = ctypes.c_uint32
         lib.orc_block_encode.restype = ctypes.c_int
         _lib = lib
@@ -142,6 +143,21 @@ class Cache:
                                    ctypes.c_int32(pt.shape[1]),
                                    _p(np.ascontiguousarray(k_new, np.uint16)),
                                    _p(np.ascontiguousarray(v_new, np.uint16)))
+        self.spill_top = int(c.spill_top)
+        return int(st)
+
+    def append_n(self, seq_lens: np.ndarray, page_table, k_new, v_new) -> int:
+        """Appends n tokens per sequence (k_new, v_new u16[B][n][H][D]) at seq_lens[b];
+        advances ``seq_lens`` in place by n."""
+        assert seq_lens.dtype == np.int32 and seq_lens.flags.c_contiguous
+        k = np.ascontiguousarray(k_new, np.uint16)
+        assert k.ndim == 4 and k.shape[0] == len(seq_lens)
+        c = self._c()
+        pt = np.ascontiguousarray(page_table, np.int32)
+        st = _load().orc_append_kv_n(ctypes.byref(self._geom()), ctypes.byref(c),
+                                     ctypes.c_int32(len(seq_lens)), ctypes.c_int32(k.shape[1]),
+                                     _p(seq_lens), _p(pt), ctypes.c_int32(pt.shape[1]), _p(k),
+                                     _p(np.ascontiguousarray(v_new, np.uint16)))
         self.spill_top = int(c.spill_top)
         return int(st)
 

@@ -152,33 +152,43 @@ uint32_t orc_encode_kv(const orc_geom* g, orc_cache* c, int32_t batch, const int
   return ORC_OK;
 }
 
-uint32_t orc_append_kv(const orc_geom* g, orc_cache* c, int32_t batch, int32_t* seq_lens,
-                       const int32_t* page_table, int32_t max_pages, const uint16_t* k_new,
-                       const uint16_t* v_new) {
-  uint32_t st = check_rows(g, batch, seq_lens, page_table, max_pages, 1);
+uint32_t orc_append_kv_n(const orc_geom* g, orc_cache* c, int32_t batch, int32_t n_new,
+                         int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                         const uint16_t* k_new, const uint16_t* v_new) {
+  if (n_new < 0) return ORC_ELEN;
+  if (n_new == 0) return ORC_OK;
+  uint32_t st = check_rows(g, batch, seq_lens, page_table, max_pages, n_new);
   if (st) return st;
   const int H = g->num_kv_heads, D = g->head_dim, T = g->page_size;
   const uint16_t** src = (const uint16_t**)malloc(sizeof(uint16_t*) * 2 * (size_t)H);
+  /* pass 0 counts the spill slots (all or nothing), pass 1 writes */
   for (int pass = 0; pass < 2; ++pass) {
     uint64_t next = c->spill_top;
-    for (int b = 0; b < batch; ++b) { /* rows in batch order */
-      int t = seq_lens[b];
-      int64_t page = page_table[(int64_t)b * max_pages + t / T];
-      for (int h = 0; h < H; ++h) {
-        src[h * 2 + 0] = k_new + ((int64_t)b * H + h) * D;
-        src[h * 2 + 1] = v_new + ((int64_t)b * H + h) * D;
+    for (int b = 0; b < batch; ++b)     /* rows in (sequence, token) order, like an encode */
+      for (int j = 0; j < n_new; ++j) {
+        int t = seq_lens[b] + j;
+        int64_t page = page_table[(int64_t)b * max_pages + t / T];
+        for (int h = 0; h < H; ++h) {
+          src[h * 2 + 0] = k_new + (((int64_t)b * n_new + j) * H + h) * D;
+          src[h * 2 + 1] = v_new + (((int64_t)b * n_new + j) * H + h) * D;
+        }
+        next += (uint64_t)encode_row(g, c, page, t % T, src, next, pass == 1);
       }
-      next += (uint64_t)encode_row(g, c, page, t % T, src, next, pass == 1);
-    }
     if (pass == 0) {
       if (next - c->spill_top > c->spill_slots - c->spill_top) { free(src); return ORC_ESPILL; }
     } else {
       c->spill_top = next;
     }
   }
-  for (int b = 0; b < batch; ++b) seq_lens[b] += 1;
+  for (int b = 0; b < batch; ++b) seq_lens[b] += n_new;
   free(src);
   return ORC_OK;
+}
+
+uint32_t orc_append_kv(const orc_geom* g, orc_cache* c, int32_t batch, int32_t* seq_lens,
+                       const int32_t* page_table, int32_t max_pages, const uint16_t* k_new,
+                       const uint16_t* v_new) {
+  return orc_append_kv_n(g, c, batch, 1, seq_lens, page_table, max_pages, k_new, v_new);
 }
 
 uint32_t orc_decode_kv(const orc_geom* g, const orc_cache* c, int32_t batch,

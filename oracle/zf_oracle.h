@@ -73,6 +73,12 @@ uint32_t orc_encode_kv(const orc_geom* g, orc_cache* c, int32_t batch, const int
 uint32_t orc_append_kv(const orc_geom* g, orc_cache* c, int32_t batch, int32_t* seq_lens,
                        const int32_t* page_table, int32_t max_pages, const uint16_t* k_new,
                        const uint16_t* v_new);
+/* Encode n_new tokens per sequence (k_new, v_new u16[B][n_new][H][D]) at positions
+ * seq_lens[b] .. seq_lens[b] + n_new - 1, spill slots taken in (sequence, token) order; on
+ * success every seq_lens[b] grows by n_new.  All or nothing.  n_new = 1 is orc_append_kv. */
+uint32_t orc_append_kv_n(const orc_geom* g, orc_cache* c, int32_t batch, int32_t n_new,
+                         int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                         const uint16_t* k_new, const uint16_t* v_new);
 /* Rebuild tokens [0, seq_lens[b]) into raw pages u16[P][H][2][T][D]. */
 uint32_t orc_decode_kv(const orc_geom* g, const orc_cache* c, int32_t batch,
                        const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,

@@ -397,3 +397,115 @@ def test_bad_page_and_length_are_reported():
     lens[0] = pt.shape[1] * 16 + 1
     st, _ = _encode(synth.Instance(inst.w, lens, inst.page_table, inst.num_pages, inst.raw_pages))
     assert st & oracle.ELEN
+
+
+# ---------------------------------------------------------------- multi-token append
+
+def _tokens_of(inst, b, t0, n):
+    """K, V rows of tokens t0..t0+n-1 of sequence b from the raw pages: two u16[n][H][D]."""
+    T = inst.w.page_size
+    ks, vs = [], []
+    for t in range(t0, t0 + n):
+        page = inst.page_table[b, t // T]
+        ks.append(inst.raw_pages[page, :, 0, t % T])
+        vs.append(inst.raw_pages[page, :, 1, t % T])
+    return np.stack(ks), np.stack(vs)
+
+
+def _chunk(inst, lens, n):
+    k = np.stack([_tokens_of(inst, b, int(lens[b]), n)[0] for b in range(inst.w.batch)])
+    v = np.stack([_tokens_of(inst, b, int(lens[b]), n)[1] for b in range(inst.w.batch)])
+    return k, v
+
+
+def test_append_n_from_empty_is_an_encode():
+    """All tokens of equal-length sequences appended in one call land exactly as a full encode
+    lays them out: same fields, same spill slots ((sequence, token) order in both)."""
+    w = _small(seed=17, ctx_min=45, ctx_max=45)
+    inst = synth.make(w)
+    _, full = _encode(inst)
+    c = oracle.Cache(inst.num_pages, w.page_size, w.num_kv_heads, w.head_dim, spill_slots=1 << 20)
+    lens = np.zeros(w.batch, np.int32)
+    k, v = _chunk(inst, lens, 45)
+    assert c.append_n(lens, inst.page_table, k, v) == oracle.OK
+    assert (lens == 45).all()
+    rows = _valid_rows(inst)
+    for name in ("row_flags", "row_spill"):
+        assert np.array_equal(getattr(c, name)[rows], getattr(full, name)[rows]), name
+    for name in ("sm", "nib", "base"):
+        m = _valid_mask(inst, getattr(c, name).shape)
+        assert np.array_equal(getattr(c, name)[m], getattr(full, name)[m]), name
+    assert c.spill_top == full.spill_top
+    assert np.array_equal(c.spill[:c.spill_top], full.spill[:full.spill_top])
+
+
+def test_append_n_chunks_roundtrip_and_slot_order():
+    """Chunks of 5, 1, 16, 9 and 2 tokens, crossing page boundaries: lossless, and within each
+    call the first spill slot of row (b, j) counts the raw blocks of all rows before it in
+    (sequence, token) order, counted from the row flags independently of the oracle."""
+    w = _small(seed=18, ctx_min=33, ctx_max=33)
+    inst = synth.make(w)
+    c = oracle.Cache(inst.num_pages, w.page_size, w.num_kv_heads, w.head_dim, spill_slots=1 << 20)
+    lens = np.zeros(w.batch, np.int32)
+    T = w.page_size
+    for n in (5, 1, 16, 9, 2):
+        k, v = _chunk(inst, lens, n)
+        pos = lens.copy()
+        top = c.spill_top
+        assert c.append_n(lens, inst.page_table, k, v) == oracle.OK
+        assert np.array_equal(lens, pos + n)
+        nxt = top
+        for b in range(w.batch):
+            for j in range(n):
+                t = int(pos[b]) + j
+                page, slot = inst.page_table[b, t // T], t % T
+                assert c.row_spill[page, slot] == nxt
+                nxt += bin(int(c.row_flags[page, slot])).count("1")
+        assert c.spill_top == nxt
+    st, dec = c.decode(lens, inst.page_table)
+    assert st == oracle.OK
+    mask = _valid_mask(inst, dec.shape)
+    assert np.array_equal(dec[mask], inst.raw_pages[mask])
+
+
+def test_append_n_one_token_is_append_and_zero_is_a_no_op():
+    w = _small(seed=19, extra_tokens=1)
+    inst = synth.make(w)
+    _, a = _encode(inst)
+    _, b = _encode(inst)
+    la, lb = inst.seq_lens.copy(), inst.seq_lens.copy()
+    k, v = synth.tokens(w, la)
+    assert a.append(la, inst.page_table, k, v) == oracle.OK
+    assert b.append_n(lb, inst.page_table, k[:, None], v[:, None]) == oracle.OK
+    assert np.array_equal(la, lb) and a.spill_top == b.spill_top
+    for name in ("sm", "nib", "base", "row_flags", "row_spill", "spill"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    before = b.spill.copy()
+    empty = np.zeros((w.batch, 0, w.num_kv_heads, w.head_dim), np.uint16)
+    assert b.append_n(lb, inst.page_table, empty, empty) == oracle.OK
+    assert np.array_equal(lb, la) and np.array_equal(before, b.spill)
+
+
+def test_append_n_errors_change_nothing():
+    w = _small(seed=20, ctx_min=20, ctx_max=20)
+    inst = synth.make(w)
+    lens = np.full(w.batch, 3, np.int32)
+    k, v = _chunk(inst, lens, 6)
+    k[:, :, :, 0] = 0  # every row gets raw blocks
+    need_c = oracle.Cache(inst.num_pages, w.page_size, w.num_kv_heads, w.head_dim, spill_slots=1 << 20)
+    l2 = lens.copy()
+    assert need_c.append_n(l2, inst.page_table, k, v) == oracle.OK
+    need = need_c.spill_top
+    c = oracle.Cache(inst.num_pages, w.page_size, w.num_kv_heads, w.head_dim, spill_slots=need - 1)
+    l3 = lens.copy()
+    assert c.append_n(l3, inst.page_table, k, v) == oracle.ESPILL
+    assert np.array_equal(l3, lens) and c.spill_top == 0 and not c.spill.any()
+    # a chunk running past the page table, and a bad page id on the way
+    big = oracle.Cache(inst.num_pages, w.page_size, w.num_kv_heads, w.head_dim, spill_slots=1 << 20)
+    l4 = np.full(w.batch, inst.page_table.shape[1] * w.page_size - 2, np.int32)
+    assert big.append_n(l4, inst.page_table, k, v) & oracle.ELEN
+    pt = inst.page_table.copy()
+    pt[0, 0] = -1
+    l5 = lens.copy()
+    assert big.append_n(l5, pt, k, v) & oracle.EPAGE
+    assert np.array_equal(l5, lens) and big.spill_top == 0
