@@ -320,6 +320,28 @@ def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_byte
     res["encode_GBps_read_plus_written"] = round((raw_bytes + packed_bytes) / t_enc / 1e9, 1)
     res["decode_GBps_read_plus_written"] = round((raw_bytes + packed_bytes) / t_dec / 1e9, 1)
     res["encode_us"] = round(t_enc * 1e6, 1)
+    # multi-token append: up to 16 new tokens per sequence in one call, written over layer 0's
+    # rows at the initial lengths (lengths and spill_top restored after each call); last
+    # extra, since it rewrites those rows
+    n_new = min(16, inst.w.extra_tokens)
+    H, D = inst.w.num_kv_heads, inst.w.head_dim
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    k16 = torch.randint(0x3C00, 0x4000, (inst.w.batch, n_new, H, D), generator=gen,
+                        dtype=torch.int16).to(raw.device)
+    v16 = k16.flip(1).contiguous()
+    lens_at = torch.from_numpy(inst.seq_lens.copy()).to(raw.device)
+    seqs_at = zf.Seqs(seqs.page_table, lens_at.clone(), seqs.max_seq_len)
+    top_dev = cache.spill_top.clone()
+
+    def app(i):
+        zf.zf_append_kv_n(cache, seqs_at, k16, v16)
+        seqs_at.seq_lens.copy_(lens_at)
+        cache.spill_top.copy_(top_dev)
+    t_app = timeit(app, n=10)
+    assert zf.zf_get_status(cache.status) == 0
+    res["append_n_tokens_per_seq"] = n_new
+    res["append_n_us"] = round(t_app * 1e6, 1)
+    res["append_n_rows_per_s"] = round(inst.w.batch * n_new / t_app, 1)
     res["decode_us"] = round(t_dec * 1e6, 1)
     return res
 

@@ -20,6 +20,7 @@ ZF_OK, ZF_EINVAL, ZF_EUNSUPPORTED, ZF_EHIP, ZF_EWORKSPACE = 0, 1, 2, 3, 4
 ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN = 1, 2, 4
 
 EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_append_kv",
+           "zf_append_kv_n",
            "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_raw",
            "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
            "zf_stream_read_probe", "zf_get_status", "zf_status_str")
@@ -66,6 +67,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "zf_encode_kv": (ctypes.c_int, [pc, ps, vp, vp, sz, vp]),
         "zf_encode_workspace_bytes": (sz, [ps]),
         "zf_append_kv": (ctypes.c_int, [pc, ps, vp, vp, vp]),
+        "zf_append_kv_n": (ctypes.c_int, [pc, ps, i32, vp, vp, vp]),
         "zf_decode_kv": (ctypes.c_int, [pc, ps, vp, vp]),
         "zf_decode_attention": (ctypes.c_int, [pc, ps, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
         "zf_decode_attention_raw": (ctypes.c_int, [vp, i32, i32, i32, i32, ps, vp, i32,
@@ -174,6 +176,15 @@ def zf_append_kv(cache: PackedCache, seqs: Seqs, k_new: torch.Tensor, v_new: tor
                  stream=None) -> None:
     _check(load().zf_append_kv(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(k_new),
                                _ptr(v_new), _stream(stream)), "zf_append_kv")
+
+
+def zf_append_kv_n(cache: PackedCache, seqs: Seqs, k_new: torch.Tensor, v_new: torch.Tensor,
+                   stream=None) -> None:
+    """k_new, v_new: bf16 bits [batch][n][H][D]; n tokens per sequence."""
+    if k_new.dim() != 4 or k_new.shape != v_new.shape:
+        raise ZfError("zf_append_kv_n: k_new and v_new must both be [batch][n][H][D]")
+    _check(load().zf_append_kv_n(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), k_new.shape[1],
+                                 _ptr(k_new), _ptr(v_new), _stream(stream)), "zf_append_kv_n")
 
 
 def zf_decode_kv(cache: PackedCache, seqs: Seqs, raw_out: torch.Tensor, stream=None) -> None:

@@ -7,8 +7,8 @@ namespace zf {
 hipError_t launch_encode(const Geom&, const zf_cache*, const zf_seqs*, const uint16_t*, uint32_t*,
                          hipStream_t);
 size_t encode_workspace_bytes(const zf_seqs*);
-int append_max_batch();
-hipError_t launch_append(const Geom&, const zf_cache*, const zf_seqs*, const uint16_t*,
+int append_max_rows();
+hipError_t launch_append(const Geom&, const zf_cache*, const zf_seqs*, int32_t, const uint16_t*,
                          const uint16_t*, hipStream_t);
 hipError_t launch_decode(const Geom&, const zf_cache*, const zf_seqs*, uint16_t*, hipStream_t);
 hipError_t launch_attention_packed(const zf_cache*, const zf_seqs*, const uint16_t*, float,
@@ -106,18 +106,24 @@ zf_status zf_encode_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_
                                       static_cast<hipStream_t>(stream)));
 }
 
-zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
-                       const uint16_t* v_new, zf_stream_t stream) {
+zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_new,
+                         const uint16_t* k_new, const uint16_t* v_new, zf_stream_t stream) {
   zf_status s = check_cache(cache);
   if (s != ZF_OK) return s;
   if ((s = check_seqs(seqs, cache->page_size)) != ZF_OK) return s;
-  if (seqs->batch == 0) return ZF_OK;
-  if (seqs->batch > zf::append_max_batch()) return ZF_EUNSUPPORTED;
+  if (n_new < 0) return ZF_EINVAL;
+  if (seqs->batch == 0 || n_new == 0) return ZF_OK;
+  if ((int64_t)seqs->batch * n_new > zf::append_max_rows()) return ZF_EUNSUPPORTED;
   if (!k_new || !v_new || (reinterpret_cast<uintptr_t>(k_new) & 15u) ||
       (reinterpret_cast<uintptr_t>(v_new) & 15u))
     return ZF_EINVAL;
-  return hip_status(zf::launch_append(geom_of(cache), cache, seqs, k_new, v_new,
+  return hip_status(zf::launch_append(geom_of(cache), cache, seqs, n_new, k_new, v_new,
                                       static_cast<hipStream_t>(stream)));
+}
+
+zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
+                       const uint16_t* v_new, zf_stream_t stream) {
+  return zf_append_kv_n(cache, seqs, 1, k_new, v_new, stream);
 }
 
 zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw_pages_out,

@@ -252,37 +252,42 @@ __global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint
 
 // ------------------------------------------------------------------------------ append
 
-// Append runs as two kernels.  append_pack_k: one workgroup per new row classifies its 32
-// blocks and writes their sm/nib/base bytes and the row's flag word into the row's slot,
-// which is not yet part of the sequence.  append_commit_k: one workgroup validates every row,
-// scans the rows' raw counts in batch order, and only if the whole batch fits in the spill
-// pool writes the spill slots and row_spill and advances seq_lens and spill_top.  So a failed
-// append changes no defined state: only the slots at position seq_lens[b] may be touched.
+// Append of n tokens per sequence runs as two kernels; new row r = b * n + j is token j of
+// sequence b, at position seq_lens[b] + j.  append_pack_k: one workgroup per new row
+// classifies its 32 blocks and writes their sm/nib/base bytes and the row's flag word into the
+// row's slot, which is not yet part of the sequence.  append_commit_k: one workgroup validates
+// every row, scans the rows' raw counts in row order ((sequence, token) order), and only if all
+// of them fit in the spill pool writes the spill slots and row_spill and advances seq_lens and
+// spill_top.  So a failed append changes no defined state: only slots at positions seq_lens[b]
+// and later may be touched.
 constexpr int kAppendThreads = 1024;
-constexpr int kAppendMaxBatch = 4096;  // two u32 per row in LDS
+constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS
 
-// Row of the new token of sequence b, or -1 (with the error bit) when it cannot be appended.
-__device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, int b, uint32_t* err) {
+// Row of new token j of sequence b (n per sequence), or -1 (with the error bit) when the
+// sequence cannot take them.
+__device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, int b, int j, int n,
+                                              uint32_t* err) {
   const int32_t L = s.lens[b];
-  if (L < 0 || (int64_t)L + 1 > (int64_t)s.maxp * g.T || L + 1 > s.max_seq_len) {
+  if (L < 0 || (int64_t)L + n > (int64_t)s.maxp * g.T || (int64_t)L + n > s.max_seq_len) {
     *err = ZF_DEV_ELEN;
     return -1;
   }
-  const int32_t pid = s.pt[(int64_t)b * s.maxp + L / g.T];
+  const int32_t t = L + j;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + t / g.T];
   if (pid < 0 || pid >= g.P) {
     *err = ZF_DEV_EPAGE;
     return -1;
   }
   *err = 0;
-  return (int64_t)pid * g.T + L % g.T;
+  return (int64_t)pid * g.T + t % g.T;
 }
 
-__global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, const uint16_t* __restrict__ k_new,
+__global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, uint8_t* sm,
                                                      uint8_t* nib, uint8_t* base, uint32_t* row_flags) {
-  const int b = blockIdx.x, tid = threadIdx.x, lane8 = tid & 7;
+  const int r = blockIdx.x, b = r / n, tid = threadIdx.x, lane8 = tid & 7;
   uint32_t err;
-  const int64_t row = append_row(g, s, b, &err);
+  const int64_t row = append_row(g, s, b, r - b * n, n, &err);
   if (row < 0) return;  // reported by append_commit_k
   const int64_t pid = row / g.T, slot = row % g.T;
   __shared__ uint32_t s_f;
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, const ui
   const int nb = g.nb(), D = g.D, H = g.H, rb = 2 * H * nb;
   for (int j = tid >> 3; j < rb; j += blockDim.x >> 3) {
     const int half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
-    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)b * H + h) * D +
+    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)r * H + h) * D +
                                                      half * kBlock + lane8 * 8);
     const uint32_t w[4] = {in.x, in.y, in.z, in.w};
     Window win = window8(w);
@@ -317,42 +322,43 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, const ui
   if (tid == 0) row_flags[row] = s_f;
 }
 
-__global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqView s,
+__global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqView s, int n,
                                                                   const uint16_t* __restrict__ k_new,
                                                                   const uint16_t* __restrict__ v_new,
                                                                   const uint32_t* row_flags, uint32_t* row_spill,
                                                                   uint8_t* spill, uint64_t* spill_top,
                                                                   uint64_t spill_slots, uint32_t* status) {
-  extern __shared__ uint32_t s_flags[];  // [B] row flags, then [B] exclusive prefixes
-  uint32_t* s_pref = s_flags + s.B;
+  const int R = s.B * n;                 // new rows
+  extern __shared__ uint32_t s_flags[];  // [R] row flags, then [R] exclusive prefixes
+  uint32_t* s_pref = s_flags + R;
   __shared__ uint32_t s_err, s_total;
   const int tid = threadIdx.x;
   if (tid == 0) s_err = 0u;
   __syncthreads();
-  for (int b = tid; b < s.B; b += kAppendThreads) {
+  for (int r = tid; r < R; r += kAppendThreads) {
     uint32_t e;
-    const int64_t row = append_row(g, s, b, &e);
+    const int64_t row = append_row(g, s, r / n, r % n, n, &e);
     if (e) atomicOr(&s_err, e);
-    else s_flags[b] = row_flags[row];
+    else s_flags[r] = row_flags[row];
   }
   __syncthreads();
   if (s_err) {
     if (tid == 0) set_status(status, s_err);
     return;
   }
-  // exclusive scan of raw counts in batch order (one wave)
+  // exclusive scan of raw counts in row order (one wave)
   if (tid < 64) {
     uint32_t carry = 0;
-    for (int b0 = 0; b0 < s.B; b0 += 64) {
-      const int b = b0 + tid;
-      const uint32_t c = b < s.B ? __popc(s_flags[b]) : 0u;
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int r = r0 + tid;
+      const uint32_t c = r < R ? __popc(s_flags[r]) : 0u;
       uint32_t incl = c;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const uint32_t up = __shfl_up((int)incl, o, 64);
         if (tid >= o) incl += up;
       }
-      if (b < s.B) s_pref[b] = carry + incl - c;
+      if (r < R) s_pref[r] = carry + incl - c;
       carry += __shfl((int)incl, 63, 64);
     }
     if (tid == 0) s_total = carry;
@@ -366,30 +372,30 @@ __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqVie
   }
   // spill slots of the raw blocks: 8 lanes per block, blocks walked in (row, block) order
   const int nb = g.nb(), D = g.D, H = g.H;
-  const uint32_t rb = 2u * H * nb, nblk = (uint32_t)s.B * rb;
+  const uint32_t rb = 2u * H * nb, nblk = (uint32_t)R * rb;
   const int lane8 = tid & 7;
 #pragma unroll 4
   for (uint32_t m = tid >> 3; m < nblk; m += kAppendThreads >> 3) {
-    const uint32_t b = m / rb, j = m - b * rb;
-    const uint32_t f = s_flags[b];
+    const uint32_t r = m / rb, j = m - r * rb;
+    const uint32_t f = s_flags[r];
     if (!((f >> j) & 1u)) continue;
     const uint32_t hk = j / nb, half = j - hk * nb, h = hk >> 1, kv = hk & 1;
-    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)b * H + h) * D +
+    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)r * H + h) * D +
                                                      half * kBlock + lane8 * 8);
     const uint32_t w[4] = {in.x, in.y, in.z, in.w};
     uint32_t hi = 0u;
 #pragma unroll
     for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
-    const uint64_t idx = top + s_pref[b] + __popc(f & ((1u << j) - 1u));
+    const uint64_t idx = top + s_pref[r] + __popc(f & ((1u << j) - 1u));
     *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
   }
-  for (int b = tid; b < s.B; b += kAppendThreads) {
+  for (int r = tid; r < R; r += kAppendThreads) {
     uint32_t e;
-    const int64_t row = append_row(g, s, b, &e);
-    row_spill[row] = (uint32_t)(top + s_pref[b]);
+    const int64_t row = append_row(g, s, r / n, r % n, n, &e);
+    row_spill[row] = (uint32_t)(top + s_pref[r]);
   }
   __syncthreads();  // every length has been read before any is advanced
-  for (int b = tid; b < s.B; b += kAppendThreads) s.lens[b] += 1;
+  for (int b = tid; b < s.B; b += kAppendThreads) s.lens[b] += n;
   if (tid == 0) *spill_top = top + total;
 }
 
@@ -472,15 +478,16 @@ size_t encode_lds_bytes(int32_t batch) {
   return ((size_t)batch + 1 + kScanThreads) * sizeof(uint32_t);
 }
 
-int append_max_batch() { return kAppendMaxBatch; }
+int append_max_rows() { return kAppendMaxRows; }
 
-hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, const uint16_t* k_new,
+hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int32_t n, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t st) {
   SeqView s = view(q);
-  hipLaunchKernelGGL(append_pack_k, dim3(q->batch), dim3(256), 0, st, g, s, k_new, v_new, c->sm, c->nib,
+  const int rows = q->batch * n;
+  hipLaunchKernelGGL(append_pack_k, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
                      c->base, c->row_flags);
-  size_t lds = 2 * (size_t)q->batch * sizeof(uint32_t);
-  hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, k_new, v_new,
+  size_t lds = 2 * (size_t)rows * sizeof(uint32_t);
+  hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, n, k_new, v_new,
                      c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
   return hipGetLastError();
 }

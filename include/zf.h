@@ -112,9 +112,19 @@ size_t zf_encode_workspace_bytes(const zf_seqs* seqs);
  * (ZF_DEV_*) seq_lens, spill_top, the spill pool and every row t < seq_lens[b] are left as
  * they were; only the slots at position seq_lens[b], which are not yet part of any sequence,
  * may have been overwritten.  seqs->max_seq_len bounds the lengths after the append.
- * Supports batch <= 4096.  Two kernel launches. */
+ * Supports batch <= 4096.  Two kernel launches (those of zf_append_kv_n with n_new = 1). */
 zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
                        const uint16_t* v_new, zf_stream_t stream);
+
+/* Multi-token append (speculative or chunked decode): encodes n_new tokens per sequence
+ * (k_new, v_new u16[batch][n_new][H][D]) into rows seq_lens[b] .. seq_lens[b] + n_new - 1,
+ * spill slots from *spill_top in (sequence, token) order, then seq_lens[b] += n_new for every
+ * b.  All or nothing, as zf_append_kv (only slots at positions seq_lens[b] and later may have
+ * been overwritten after a device error); seqs->max_seq_len bounds the grown lengths.
+ * n_new == 0 does nothing; n_new < 0 is ZF_EINVAL.  Supports batch * n_new <= 4096 (callers
+ * split longer chunks).  Two kernel launches.  zf_append_kv is the case n_new == 1. */
+zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_new,
+                         const uint16_t* k_new, const uint16_t* v_new, zf_stream_t stream);
 
 /* Inverse of the codec: writes rows t < seq_lens[b] as raw bf16 pages (lossless: the bits
  * that were encoded). */

@@ -77,6 +77,19 @@ def test_bad_cache_is_rejected_before_any_launch(kw, code):
     s = zf.zf_seqs(1, 1, 4096, 4096, 16)
     assert lib.zf_decode_kv(ctypes.byref(c), ctypes.byref(s), 2304, None) == code
     assert lib.zf_append_kv(ctypes.byref(c), ctypes.byref(s), 4096, 4096, None) == code
+    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 2, 4096, 4096, None) == code
+
+
+def test_append_n_arguments():
+    """Rejected (or, for no tokens, finished) on the host before any launch."""
+    lib = zf.load()
+    c = _cache()
+    s = zf.zf_seqs(64, 1, 4096, 4096, 16)
+    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), -1, 4096, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 0, None, None, None) == zf.ZF_OK
+    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 65, 4096, 4096, None) == zf.ZF_EUNSUPPORTED
+    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 64, 4096, 4104, None) == zf.ZF_EINVAL
+    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 64, None, 4096, None) == zf.ZF_EINVAL
 
 
 @pytest.mark.parametrize("seqs,code", [

@@ -1,4 +1,4 @@
-"""GPU parity for the codec: zf_encode_kv, zf_append_kv and zf_decode_kv through the C ABI,
+"""GPU parity for the codec: zf_encode_kv, zf_append_kv(_n) and zf_decode_kv through the C ABI,
 bit-exact against the CPU oracle on every workload (packed planes, base, row flags, row spill
 slots, spill bytes, spill_top), plus the device-side error rules.
 
@@ -112,6 +112,56 @@ def test_append_spill_exhaustion_changes_no_defined_state():
     torch.cuda.synchronize()
     assert s2.status() == 0
     compare_packed(s2.cache, orc2, valid_rows(inst, lens), "append after a failed one")
+
+
+def _chunk_tokens(w, lens, n):
+    """n new tokens per sequence at positions lens[b] .. lens[b] + n - 1: two u16[B][n][H][D]."""
+    ks, vs = zip(*(synth.tokens(w, lens + j) for j in range(n)))
+    return np.ascontiguousarray(np.stack(ks, 1)), np.ascontiguousarray(np.stack(vs, 1))
+
+
+@pytest.mark.parametrize("key,chunks", [("small", (5, 1, 3, 16)), (1, (16,)), (3, (64,)), (4, (17, 64, 1))])
+def test_append_n_bitexact(key, chunks):
+    """Multi-token appends (ragged lengths, chunks crossing pages, 4096 rows at the limit for
+    64 sequences x 64 tokens) equal the oracle bit for bit after every call."""
+    w = workload(key)
+    w = w.replace(extra_tokens=max(w.extra_tokens, sum(chunks)))
+    log(f"multi-token append parity: workload {w.name}, chunks {chunks}")
+    inst = synth.make(w)
+    s = Setup(inst)
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    lens = inst.seq_lens.copy()
+    for i, n in enumerate(chunks):
+        k, v = _chunk_tokens(w, lens, n)
+        zf.zf_append_kv_n(s.cache, s.seqs, dev(k), dev(v))
+        assert orc.append_n(lens, inst.page_table, k, v) == oracle.OK
+        torch.cuda.synchronize()
+        assert s.status() == 0
+        assert np.array_equal(host(s.seqs.seq_lens), lens)
+        compare_packed(s.cache, orc, valid_rows(inst, lens), f"{w.name} chunk {i} (n={n})")
+
+
+def test_append_n_spill_exhaustion_changes_no_defined_state():
+    inst = synth.make(SMALL.replace(extra_tokens=8))
+    orc = oracle_cache(inst, 1 << 20)
+    need = orc.spill_top
+    s = Setup(inst, spill_slots=need + 3)  # room for a few raw blocks only
+    rows = valid_rows(inst)
+    names = ("sm", "nib", "base", "row_flags", "row_spill")
+    before = {n: host(getattr(s.cache, n)).copy() for n in names}
+    spill_before = host(s.cache.spill).copy()
+    k, v = _chunk_tokens(inst.w, inst.seq_lens, 8)
+    k[:, :, :, 0] = 0  # every new row gets a raw block
+    zf.zf_append_kv_n(s.cache, s.seqs, dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert s.status() & zf.ZF_DEV_ESPILL
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == need
+    assert np.array_equal(host(s.cache.spill), spill_before)
+    for n in names:
+        a, b = host(getattr(s.cache, n)), before[n]
+        m = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
+        assert np.array_equal(a[m], b[m]), n
 
 
 def test_encode_spill_exhaustion_keeps_pool():
