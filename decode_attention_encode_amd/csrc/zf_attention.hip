@@ -99,8 +99,13 @@ constexpr int32_t kRawBufferWord3 = 0x00020000;  // 32-bit data format, no swizz
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
 }
+// Cache policy of a load: plain, or non-temporal (`nt`: the line is not kept for reuse).
+// Page planes are read once per launch, so they stream; spill lines and metadata are shared
+// by the kv heads of a sequence and stay cached.
+constexpr int kKeep = 0, kStream = 2;
+template <int Policy = kKeep>
 __device__ __forceinline__ void dmab16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds, 16, voff, soff, 0, Policy);
 }
 __device__ __forceinline__ void dmab4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds, 4, voff, soff, 0, 0);
@@ -216,32 +221,35 @@ struct PackedLoader {
     return r;
   }
 
-  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue& m) const {
+  // live = false: a step past the wave's last page; its loads still go out (the per-step load
+  // count is fixed) but through empty resources, which return zeros without touching memory.
+  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue& m,
+                                             bool live) const {
     // spill: lane l loads 16 bytes of row l >> 2, chunk l & 3 of the row's 64 bytes (K chunks
     // swizzled); the pool as a bounds-checked buffer, so offsets past its end read zeros
-    const __amdgpu_buffer_rsrc_t spr = buffer_of(spill, spill_bytes);
+    const __amdgpu_buffer_rsrc_t spr = buffer_of(spill, live ? spill_bytes : 0u);
     const int r = lane >> 2;
     const int ck = (lane & 3) ^ ((r >> 2) & 3), cv = lane & 3;
     dmab16(spr, slot + 7168, spill_off(m.fs.x, m.fs.y, (h * 2 + 0) * 2 + (ck >> 1), (ck & 1) * 16), 0);
     dmab16(spr, slot + 6144, spill_off(m.fs.x, m.fs.y, (h * 2 + 1) * 2 + (cv >> 1), (cv & 1) * 16), 0);
     // the planes of (page, h): sm of K rows then V rows (4 KB), nibbles likewise (2 KB)
     const int64_t row0 = ((pid * H + h) * 2) * kT;  // K row 0 of the page
-    const __amdgpu_buffer_rsrc_t smr = buffer_of(sm + row0 * kD, 2 * kT * kD);
-    const __amdgpu_buffer_rsrc_t nbr = buffer_of(nib + row0 * (kD / 2), 2 * kT * (kD / 2));
+    const __amdgpu_buffer_rsrc_t smr = buffer_of(sm + row0 * kD, live ? 2 * kT * kD : 0u);
+    const __amdgpu_buffer_rsrc_t nbr = buffer_of(nib + row0 * (kD / 2), live ? 2 * kT * (kD / 2) : 0u);
     {  // K sm: gather i, lane l -> LDS chunk 64i + l = row 8i + (l >> 3), position l & 7
       const int r0 = lane >> 3, c0 = (lane & 7) ^ ((r0 >> 1) & 7);
       const int r1 = 8 + (lane >> 3), c1 = (lane & 7) ^ ((r1 >> 1) & 7);
-      dmab16(smr, slot, (uint32_t)(r0 * 128 + c0 * 16), 0);
-      dmab16(smr, slot + 1024, (uint32_t)(r1 * 128 + c1 * 16), 0);
+      dmab16<kStream>(smr, slot, (uint32_t)(r0 * 128 + c0 * 16), 0);
+      dmab16<kStream>(smr, slot + 1024, (uint32_t)(r1 * 128 + c1 * 16), 0);
     }
     {  // K nibbles: lane l -> row l >> 2, position l & 3
       const int rn = lane >> 2, cn = (lane & 3) ^ ((rn >> 2) & 3);
-      dmab16(nbr, slot + 4096, (uint32_t)(rn * 64 + cn * 16), 0);
+      dmab16<kStream>(nbr, slot + 4096, (uint32_t)(rn * 64 + cn * 16), 0);
     }
     // V sm and nibbles as they are in memory
-    dmab16(smr, slot + 2048, (uint32_t)(lane * 16), 2048);
-    dmab16(smr, slot + 3072, (uint32_t)(lane * 16), 3072);
-    dmab16(nbr, slot + 5120, (uint32_t)(lane * 16), 1024);
+    dmab16<kStream>(smr, slot + 2048, (uint32_t)(lane * 16), 2048);
+    dmab16<kStream>(smr, slot + 3072, (uint32_t)(lane * 16), 3072);
+    dmab16<kStream>(nbr, slot + 5120, (uint32_t)(lane * 16), 1024);
   }
 
   // One page's bytes as this lane needs them (read from LDS in one go): K row krow(t) (sm,
@@ -339,15 +347,16 @@ struct RawLoader {
   __device__ __forceinline__ Issue read_issue(int, uint32_t) const { return Issue{}; }
   __device__ __forceinline__ void issue_meta(int64_t, int, int, int, uint32_t) const {}
 
-  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue&) const {
-    const __amdgpu_buffer_rsrc_t pr = buffer_of(pages + ((pid * H + h) * 2) * kT * kD, 2 * kT * kD * 2);
+  __device__ __forceinline__ void issue_page(int64_t pid, int H, int h, int lane, uint32_t slot, const Issue&,
+                                             bool live) const {
+    const __amdgpu_buffer_rsrc_t pr = buffer_of(pages + ((pid * H + h) * 2) * kT * kD, live ? 2 * kT * kD * 2 : 0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // gather i, lane l -> row 4i + (l >> 4), position l & 15
       const int r = 4 * i + (lane >> 4), c = (lane & 15) ^ r;
-      dmab16(pr, slot + i * 1024, (uint32_t)(r * 256 + c * 16), 0);
+      dmab16<kStream>(pr, slot + i * 1024, (uint32_t)(r * 256 + c * 16), 0);
     }
 #pragma unroll
-    for (int i = 4; i < 8; ++i) dmab16(pr, slot + i * 1024, (uint32_t)(lane * 16), i * 1024);
+    for (int i = 4; i < 8; ++i) dmab16<kStream>(pr, slot + i * 1024, (uint32_t)(lane * 16), i * 1024);
   }
 
   struct Page {
@@ -566,8 +575,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const float negl32 = (float)(kNegligible / c2);
   float shared32 = -INFINITY;  // the workgroup's maximum kShareLag steps ago (fp32)
 
-  // page n of this wave; indices past the end repeat the last page (their loads keep the
-  // per-page load count fixed and are never used)
+  // page n of this wave; indices past the end repeat the last page (their metadata loads keep
+  // the per-step load count fixed and are never used; their page loads read nothing)
   auto pid_at = [&](int n) -> int64_t {
     const int32_t v = __builtin_amdgcn_readlane(my_pid, min(n, nmine - 1));
     return v < 0 ? 0 : v;
@@ -731,10 +740,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) ld.issue_meta(pid_at(k), a.H, h, lane, meta_of(k));
     wait_vm<3 * kM>();
-    ld.issue_page(pid_at(0), a.H, h, lane, slot_of(0), ld.read_issue(lane, meta_of(0)));
+    ld.issue_page(pid_at(0), a.H, h, lane, slot_of(0), ld.read_issue(lane, meta_of(0)), true);
     ld.issue_meta(pid_at(4), a.H, h, lane, meta_of(4));
     wait_vm<kP + 2 * kM>();
-    ld.issue_page(pid_at(1), a.H, h, lane, slot_of(1), ld.read_issue(lane, meta_of(1)));
+    ld.issue_page(pid_at(1), a.H, h, lane, slot_of(1), ld.read_issue(lane, meta_of(1)), nmine > 1);
     typename Loader::Issue next = ld.read_issue(lane, meta_of(2));
     ld.issue_meta(pid_at(5), a.H, h, lane, meta_of(5));
     // Waves w and w + 4 share a SIMD, and the SIMD issues the older one first: left alone, w
@@ -767,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       // page n + 2's loads then go into the freed slot and the rebuild runs while they fly
       const typename Loader::Issue cur = next;
       const typename Loader::Page pg = ld.read(lane, slot_of(n), meta_of(n), meta_of(n + 3), next);
-      ld.issue_page(pid_at(n + 2), a.H, h, lane, slot_of(n), cur);
+      ld.issue_page(pid_at(n + 2), a.H, h, lane, slot_of(n), cur, n + 2 < nmine);
       ld.issue_meta(pid_at(n + 6), a.H, h, lane, meta_of(n + 6));
       compute(n, pg);
     }

@@ -13,7 +13,8 @@ namespace zf {
 constexpr int kProbeThreads = 512;
 constexpr int kProbeUnroll = 4;
 
-// Block b reads its contiguous share of the buffer, 4 x 16 bytes per thread in flight, and
+// Block b reads its contiguous share of the buffer, 4 x 16 bytes per thread in flight with the
+// non-temporal hint (the fastest plain read measured on gfx950), and
 // leaves the XOR of everything it read in sink[b] (so no load can be dropped).
 __global__ __launch_bounds__(kProbeThreads) void stream_read_k(const uint4* __restrict__ p, uint64_t n16,
                                                                uint32_t* __restrict__ sink) {
@@ -25,7 +26,8 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_k(const uint4* __re
     for (int u = 0; u < kProbeUnroll; ++u) {
       const uint64_t j = i + (uint64_t)u * kProbeThreads;
       if (j < b1) {
-        const uint4 v = p[j];
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + j);  // streamed
         x ^= v.x ^ v.y ^ v.z ^ v.w;
       }
     }
