@@ -60,6 +60,7 @@ constexpr int kFlushPages = 4;
 constexpr int kShareLag = 3;
 constexpr int kShareRing = 8;  // > 2 * kShareLag: no slot is rewritten while it may be read
 constexpr uint32_t kDone = 0x7FFFFFFFu;  // progress of a wave that has finished its pages
+constexpr int kOrderMaxBatch = 256;  // longest-first group order up to this batch (LDS scratch)
 constexpr int kMaxPagesPerSplit = kWaves * 64;
 constexpr uint32_t kXcds = 8;  // MI355X: workgroups are dispatched round-robin over 8 XCDs  // each wave keeps its page ids in one register
 // One split's partial, in doubles: acc[kG][kD], l[kG], m[kG].
@@ -68,6 +69,7 @@ constexpr int kPartDoubles = kG * kD + 2 * kG;
 struct AttnArgs {
   int32_t B, H, maxp, max_seq_len, pps, nsplit_max, num_pages;
   int32_t direct;  // one split per sequence: attn_k writes the output itself
+  int32_t order;   // number the (sequence, split) groups longest sequence first
   const int32_t* pt;
   const int32_t* lens;
   const uint16_t* q;
@@ -468,18 +470,22 @@ __device__ __forceinline__ float rows_max(float v) {
 // own region once its loads have drained.
 constexpr uint32_t kWaveLds = 2 * kSlotBytes + kMetaRing * kMetaBytes;
 static_assert(kG * kD * sizeof(double) + 2 * kG * sizeof(double) <= kWaveLds, "results fit");
+static_assert(2 * kOrderMaxBatch * sizeof(int32_t) <= kWaveLds, "order scratch fits");
 
 template <class Loader>
 __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
-  // Workgroup ids go round-robin over the 8 XCDs; each XCD takes a contiguous run of units
-  // (split fastest, then kv head, then sequence), so the kv heads of a sequence share one L2
-  // for the page metadata and spill lines they all read.
+  // The job: a (sequence b, split s, kv head h).  Workgroup ids go round-robin over the 8
+  // XCDs; in the plain order each XCD takes a contiguous run of jobs (split fastest, then kv
+  // head, then sequence), so the kv heads of a sequence share one L2 for the page metadata and
+  // spill lines they all read.
   const uint32_t per_xcd = gridDim.x / kXcds;
-  const uint32_t job = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (job >= (uint32_t)a.nsplit_max * (uint32_t)a.H * (uint32_t)a.B) return;  // <= maxp * B < 2^31
-  const int s = (int)(job % (uint32_t)a.nsplit_max);
-  const int h = (int)((job / (uint32_t)a.nsplit_max) % (uint32_t)a.H);
-  const int b = (int)(job / ((uint32_t)a.nsplit_max * (uint32_t)a.H));
+  const uint32_t xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const uint32_t job = xcd * per_xcd + local;
+  const uint32_t units = (uint32_t)a.nsplit_max * (uint32_t)a.H * (uint32_t)a.B;  // <= maxp * B < 2^31
+  if (!a.order && job >= units) return;
+  int s = (int)(job % (uint32_t)a.nsplit_max);
+  int h = (int)((job / (uint32_t)a.nsplit_max) % (uint32_t)a.H);
+  int b = (int)(job / ((uint32_t)a.nsplit_max * (uint32_t)a.H));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 15, qd = lane >> 4;
@@ -489,6 +495,63 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   // row 3 p - p = 0
   const uint32_t mask1 = part == 0 ? 0u : part == 3 ? 0xFFFFFFFFu : 0xFFFF0000u;
   const uint32_t mask2 = part == 2 ? 0xFFFF0000u : 0u;
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
+  const int32_t cap = min(a.maxp * kT, a.max_seq_len);
+  auto splits_of = [&](int32_t len) {  // splits of a sequence of `len` tokens (len clamped)
+    len = len < 0 ? 0 : min(len, cap);
+    return max(1, ((len + kT - 1) / kT + a.pps - 1) / a.pps);
+  };
+  if (a.order) {
+    // More workgroups than CUs: when the lengths differ, the (sequence, split) groups are
+    // dispatched longest sequence first (ties: lower index), group g with all its kv heads on
+    // XCD g % 8, so that long jobs start first and short ones fill the end.  Each wave finds
+    // the same job on its own, with its LDS region as scratch (no pages are in flight yet).
+    int32_t* wl = reinterpret_cast<int32_t*>(&s_ring[wave][0]);  // [B] lengths, [B] splits
+    int32_t lmin = 0x7FFFFFFF, lmax = -1;
+    for (int i = lane; i < a.B; i += 64) {
+      const int32_t li = max(0, min(a.lens[i], cap));
+      wl[i] = li;
+      wl[kOrderMaxBatch + i] = splits_of(li);
+      lmin = min(lmin, li);
+      lmax = max(lmax, li);
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");  // the wave's stores above before its loads below
+    for (int o = 32; o > 0; o >>= 1) {
+      lmin = min(lmin, __shfl_xor(lmin, o, 64));
+      lmax = max(lmax, __shfl_xor(lmax, o, 64));
+    }
+    if (lmin != lmax) {
+      const uint32_t g = (local / (uint32_t)a.H) * kXcds + xcd;
+      int mb = -1, ms = 0;
+      for (int i = lane; i < a.B; i += 64) {
+        const int32_t li = wl[i];
+        uint32_t first = 0;  // groups of the sequences ranked before i
+        for (int k = 0; k < a.B; ++k) {
+          const int32_t lk = wl[k];
+          if (lk > li || (lk == li && k < i)) first += (uint32_t)wl[kOrderMaxBatch + k];
+        }
+        if (g >= first && g < first + (uint32_t)wl[kOrderMaxBatch + i]) {
+          mb = i;
+          ms = (int)(g - first);
+        }
+      }
+      const uint64_t found = __ballot(mb >= 0);
+      if (!found) return;  // past the last group (every wave of the workgroup)
+      const int src = __builtin_ffsll((long long)found) - 1;
+      b = __builtin_amdgcn_readfirstlane(__shfl(mb, src, 64));
+      s = __builtin_amdgcn_readfirstlane(__shfl(ms, src, 64));
+      h = (int)(local % (uint32_t)a.H);
+    } else if (job >= units) {
+      return;
+    }
+  }
+
+  // the job is the same for every lane: keep it in scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  s = __builtin_amdgcn_readfirstlane(s);
+  h = __builtin_amdgcn_readfirstlane(h);
 
   // this wave's pages: p_first + 8n; lane n reads the page id of page n.  The table row and q
   // are read together with the length, not after it (one memory round trip less before the
@@ -511,7 +574,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     }
   }
   int32_t L = a.lens[b];
-  const int32_t cap = min(a.maxp * kT, a.max_seq_len);
   if (L < 0 || L > cap) {
     if (s == 0 && tid == 0) set_status(a.status, ZF_DEV_ELEN);
     L = L < 0 ? 0 : cap;
@@ -530,7 +592,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
                                    (double)__uint_as_float((uint32_t)qrow[dlo + 4] << 16));
   }
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
   __shared__ uint32_t s_prog[kWaves];  // steps whose running maximum each wave has published
   const uint32_t ring = (uint32_t)(uintptr_t)&s_ring[wave][0];
   const uint32_t meta_ring = ring + 2 * kSlotBytes;
@@ -669,14 +730,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       }
     }
     if (__any(pm > m)) {
+      // rescale by alpha = 2^((m - mn) c2), one fp32 factor for all of this head's sums (fp64
+      // and MFMA ones alike): where alpha is not negligible its exponent is small, so fp32 is
+      // accurate to ~1e-6 there, and a common factor cancels in acc / l anyway
       const double mn = fmax(m, pm);
-      const double alpha = exp2((m - mn) * c2);
+      const float alpha = __builtin_amdgcn_exp2f((float)((m - mn) * c2));
       m = mn;
       m32 = (float)m;
       mc2 = m * c2;
-      l *= alpha;
-      const double al = __shfl(alpha, 4 * qd, 64);  // acc holds head qd; lane 4qd has head qd
-      const float alf = (float)al;
+      l *= (double)alpha;
+      const float alf = __shfl(alpha, 4 * qd, 64);  // acc holds head qd; lane 4qd has head qd
+      const double al = (double)alf;
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) {
         acc[nn] *= al;
@@ -953,6 +1017,9 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   a.nsplit_max = pl.nsplit_max;
   a.num_pages = num_pages;
   a.direct = pl.nsplit_max == 1;
+  int dev = 0, cus = 0;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   a.pt = q->page_table;
   a.lens = q->seq_lens;
   a.q = qv;
@@ -961,8 +1028,11 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   size_t cnt = (size_t)q->batch * H * sizeof(uint32_t);
   a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + 256 + ((cnt + 255) / 256) * 256);
   a.status = status;
-  const uint32_t units = (uint32_t)pl.nsplit_max * (uint32_t)H * (uint32_t)q->batch;
-  dim3 grid((units + kXcds - 1) / kXcds * kXcds);
+  // groups (sequence, split) rounded up to a multiple of the XCD count, times the kv heads
+  const uint32_t groups = (uint32_t)pl.nsplit_max * (uint32_t)q->batch;
+  dim3 grid((groups + kXcds - 1) / kXcds * kXcds * (uint32_t)H);
+  // the dispatch order only matters with more workgroups than CUs
+  a.order = q->batch > 1 && q->batch <= kOrderMaxBatch && grid.x > (uint32_t)cus;
   if (t_timing.start) {  // one-shot device timestamps of this kernel (profiling aid)
     const TimingEvents ev = t_timing;
     t_timing = TimingEvents{};
