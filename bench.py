@@ -14,8 +14,9 @@ Prints one JSON line.  `value` = tokens/s of the whole job (sequences x steps / 
 layer.  `roofline` prices the attention kernel (the dominant one) against HBM: algorithmic
 bytes per launch (packed planes of the attended rows, spill slots of their raw blocks, q, out,
 page table and lengths) / its mean duration from HIP events on the launch stream, stamped at
-the kernel's own start and end (zf_time_next_attention: the interval a kernel trace reports);
-the call time with dispatch overhead is reported beside it.
+the kernel's own start and end (zf_time_next_attention: the interval a kernel trace reports) on
+every 4th timed step (a stamped launch pays ~8 us more dispatch, so `value` would be understated
+if every step carried the stamps); the call time with dispatch overhead is reported beside it.
 `cpu_baseline` times the CPU oracle (plain C, one thread) on a bounded sample of the same
 steps.
 """
@@ -49,6 +50,9 @@ def attn_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+STAMP_EVERY = 4  # timed steps per kernel-stamped step
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,6 +67,9 @@ def parse():
                     help="also time the raw twin, a cache-flushed attention, encode and decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--per-config", default="",
+                    help="only time the attention call on these workloads (e.g. 1,2,3,4: the "
+                         "parity configurations), one JSON line each, and exit")
     return ap.parse_args()
 
 
@@ -92,6 +99,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "launches": 3}))
+        return
+    if args.per_config:
+        for wi in [int(x) for x in args.per_config.split(",")]:
+            print(json.dumps(per_config(torch, zf, synth, wi, dev)), flush=True)
         return
 
     W, K = args.warmup, args.steps
@@ -149,15 +160,18 @@ def main():
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
-    # per timed step: kernel start / end (device timestamps of the dispatch) and call start / end
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(K)]
+    # every STAMP_EVERY-th timed step: kernel start / end (device timestamps of the dispatch)
+    # and call start / end.  A stamped launch costs ~8 us of dispatch, so only a sample of the
+    # timed steps carries the stamps.
+    sampled = [i for i in range(K) if i % STAMP_EVERY == 0]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in sampled]
     for ev in evs:
         for e in ev:
             e.record(stream)  # creates the events on the device
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
-        step(W + i, evs[i])
+        step(W + i, evs[i // STAMP_EVERY] if i % STAMP_EVERY == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     for cache, _ in layers:
@@ -190,7 +204,7 @@ def main():
         attn_bytes.append(nbytes)
     attn_bytes = np.array(attn_bytes, np.float64)
     mean_attn_s = attn_ms.mean() / 1e3
-    achieved = attn_bytes.mean() / mean_attn_s / 1e9
+    achieved = attn_bytes[sampled].mean() / mean_attn_s / 1e9  # bytes of the stamped launches
     uncompressed_eq = tokens_attended / K * H * 2 * D * 2 / mean_attn_s / 1e9
     packed_valid = rows0 * row_bytes + 32 * top0
     ratio = packed_valid / (rows0 * H * 2 * D * 2)
@@ -204,6 +218,7 @@ def main():
     extra = {
         "layers_rotated": NL,
         "attention_kernel_us_mean": round(attn_ms.mean() * 1e3, 2),
+        "attention_launches_stamped": len(sampled),
         "attention_kernel_us_min": round(attn_ms.min() * 1e3, 2),
         "attention_call_us_mean": round(call_ms.mean() * 1e3, 2),
         "attention_bytes_per_launch": int(attn_bytes.mean()),
@@ -344,6 +359,76 @@ def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_byte
     res["append_n_rows_per_s"] = round(inst.w.batch * n_new / t_app, 1)
     res["decode_us"] = round(t_dec * 1e6, 1)
     return res
+
+
+def per_config(torch, zf, synth, wi, dev):
+    """Attention alone on one workload (no append): the packed call and its split kernel, and
+    the twin, rotating over layer caches well beyond the last-level cache."""
+    w = synth.WORKLOADS[wi].replace(extra_tokens=0)
+    inst = synth.make(w)
+    to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    T, H, D, Hq = w.page_size, w.num_kv_heads, w.head_dim, w.num_q_heads
+    raw = to(inst.raw_pages)
+    NL = max(2, -(-1200_000_000 // (int(inst.seq_lens.sum()) * 3404)))  # >= 1.2 GB of caches
+    layers = []
+    for _ in range(NL):
+        cache = zf.PackedCache.empty(inst.num_pages, T, H, D, int(inst.seq_lens.sum()) * 2 * H * (D // 64),
+                                     device=dev)
+        seqs = zf.Seqs(to(inst.page_table), to(inst.seq_lens.copy()), int(inst.seq_lens.max()))
+        zf.zf_encode_kv(cache, seqs, raw, zf.encode_workspace(seqs))
+        layers.append((cache, seqs))
+    torch.cuda.synchronize()
+    top = int(layers[0][0].spill_top.item())
+    rows = int(inst.seq_lens.sum())
+    pt_bytes = sum(-(-int(L) // T) for L in inst.seq_lens) * 4
+    attn_bytes = rows * 3112 + 32 * top + w.batch * Hq * D * (2 + 4) + pt_bytes + 4 * w.batch
+    q = to(synth.query(w, 0))
+    out = torch.empty((w.batch, Hq, D), dtype=torch.float32, device=dev)
+    ws = zf.attention_workspace(w.batch, H, Hq, D, layers[0][1].max_seq_len, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    N = 30
+
+    def run(fn, stamps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N)]
+        for e in ev:
+            for x in e:
+                x.record(stream)
+        torch.cuda.synchronize()
+        for i in range(N):
+            ev[i][0].record(stream)
+            if stamps:
+                zf.zf_time_next_attention(ev[i][2], ev[i][3])
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        call = np.array([e[0].elapsed_time(e[1]) for e in ev[5:]]) * 1e3
+        kern = np.array([e[2].elapsed_time(e[3]) for e in ev[5:]]) * 1e3 if stamps else None
+        return call, kern
+    packed = lambda i: zf.zf_decode_attention(layers[i % NL][0], layers[i % NL][1], q, scale, out, ws)
+    call, _ = run(packed, False)   # plain launches, as the twin's below
+    _, kern = run(packed, True)    # stamped launches (slower dispatch) for the kernel's own time
+    twins = []
+    for cache, seqs in layers[:2]:
+        d = torch.zeros_like(raw)
+        zf.zf_decode_kv(cache, seqs, d)
+        twins.append(d)
+    del raw
+    tcall, _ = run(lambda i: zf.zf_decode_attention_raw(twins[i % 2], layers[i % 2][1], q, scale, out, ws,
+                                                        status), False)
+    for cache, _ in layers:
+        assert zf.zf_get_status(cache.status) == 0
+    return {"workload": w.name, "batch": w.batch, "tokens": rows, "q_heads": Hq, "kv_heads": H,
+            "layers_rotated": NL, "attention_bytes": attn_bytes,
+            "call_us_mean": round(float(call.mean()), 2),
+            "kernel_us_mean": round(float(kern.mean()), 2), "kernel_us_min": round(float(kern.min()), 2),
+            "call_GBps": round(attn_bytes / call.mean() / 1e3, 1),
+            "call_frac_of_8TBps": round(attn_bytes / call.mean() / 1e3 / 8000, 4),
+            "tokens_per_s": round(w.batch / call.mean() * 1e6, 1),
+            "twin_call_us_mean": round(float(tcall.mean()), 2),
+            "speedup_vs_twin": round(float(tcall.mean() / call.mean()), 3),
+            "note": "call = split kernel + merge when the plan splits sequences; back to back"}
 
 
 def cpu_baseline(w, inst, lens0, ks, vs, qs, budget_s, row_bytes):
