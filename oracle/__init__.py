@@ -43,8 +43,10 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB)
         for name in ("orc_encode_kv", "orc_append_kv", "orc_append_kv_n", "orc_decode_kv",
-                     "orc_attention"):
+                     "orc_compact_spill", "orc_attention"):
             getattr(lib, name).restype = ctypes.c_uint32
+        lib.orc_max_sequences.restype = ctypes.c_int64
+        lib.orc_max_sequences.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 5 + [ctypes.c_double]
         lib.orc_block_encode.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -161,6 +163,18 @@ class Cache:
         self.spill_top = int(c.spill_top)
         return int(st)
 
+    def compact(self, seq_lens, page_table) -> int:
+        """Rewrites the spill pool for the listed sequences only (slots from 0 in (sequence,
+        token) order); the other sequences' slots are given up."""
+        c = self._c()
+        lens = np.ascontiguousarray(seq_lens, np.int32)
+        pt = np.ascontiguousarray(page_table, np.int32)
+        st = _load().orc_compact_spill(ctypes.byref(self._geom()), ctypes.byref(c),
+                                       ctypes.c_int32(len(lens)), _p(lens), _p(pt),
+                                       ctypes.c_int32(pt.shape[1]))
+        self.spill_top = int(c.spill_top)
+        return int(st)
+
     def decode(self, seq_lens, page_table, out: np.ndarray | None = None):
         if out is None:
             out = np.zeros((self.num_pages, self.num_kv_heads, 2, self.page_size,
@@ -171,6 +185,15 @@ class Cache:
                                    ctypes.c_int32(len(lens)), _p(lens), _p(pt),
                                    ctypes.c_int32(pt.shape[1]), _p(out))
         return int(st), out
+
+
+def max_sequences(kv_budget: int, layers: int, context: int, page_size: int, num_kv_heads: int,
+                  head_dim: int, raw_blocks_per_row: float | None) -> int:
+    """Sequences of ``context`` tokens whose caches fit in ``kv_budget`` bytes over ``layers``
+    layers; ``raw_blocks_per_row`` None = uncompressed bf16 pages."""
+    r = -1.0 if raw_blocks_per_row is None else float(raw_blocks_per_row)
+    return int(_load().orc_max_sequences(kv_budget, layers, context, page_size, num_kv_heads,
+                                         head_dim, r))
 
 
 def attention(raw_pages: np.ndarray, seq_lens, page_table, q: np.ndarray,

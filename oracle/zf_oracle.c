@@ -221,6 +221,53 @@ uint32_t orc_decode_kv(const orc_geom* g, const orc_cache* c, int32_t batch,
   return ORC_OK;
 }
 
+uint32_t orc_compact_spill(const orc_geom* g, orc_cache* c, int32_t batch,
+                           const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages) {
+  uint32_t st = check_rows(g, batch, seq_lens, page_table, max_pages, 0);
+  if (st) return st;
+  const int T = g->page_size;
+  /* Pass 1: every listed row's slots must be live ones; count them. */
+  uint64_t total = 0;
+  for (int b = 0; b < batch; ++b)
+    for (int t = 0; t < seq_lens[b]; ++t) {
+      int64_t row = (int64_t)page_table[(int64_t)b * max_pages + t / T] * T + t % T;
+      uint64_t n = (uint64_t)popcount32(c->row_flags[row]);
+      if (n > 0 && (uint64_t)c->row_spill[row] + n > c->spill_top) return ORC_ESPILL;
+      total += n;
+    }
+  /* Pass 2: copy the slots out in the new order, then write them back from slot 0. */
+  uint8_t* fresh = (uint8_t*)malloc(total * 32u + 1u);
+  uint64_t next = 0;
+  for (int b = 0; b < batch; ++b)
+    for (int t = 0; t < seq_lens[b]; ++t) {
+      int64_t row = (int64_t)page_table[(int64_t)b * max_pages + t / T] * T + t % T;
+      uint64_t n = (uint64_t)popcount32(c->row_flags[row]);
+      if (n > 0) memcpy(fresh + next * 32u, c->spill + (uint64_t)c->row_spill[row] * 32u, n * 32u);
+      c->row_spill[row] = (uint32_t)next;
+      next += n;
+    }
+  memcpy(c->spill, fresh, total * 32u);
+  free(fresh);
+  c->spill_top = total;
+  return ORC_OK;
+}
+
+int64_t orc_max_sequences(int64_t kv_budget, int32_t layers, int32_t context, int32_t page_size,
+                          int32_t num_kv_heads, int32_t head_dim, double raw_blocks_per_row) {
+  if (kv_budget <= 0 || layers <= 0 || context <= 0) return 0;
+  int64_t rows = (int64_t)(context + page_size - 1) / page_size * page_size;
+  int64_t vectors = (int64_t)num_kv_heads * 2;
+  int64_t per_layer;
+  if (raw_blocks_per_row < 0) {
+    per_layer = rows * vectors * head_dim * 2;
+  } else {
+    int64_t row_bytes = vectors * (head_dim + head_dim / 2 + head_dim / 64) + 4 + 4;
+    int64_t slots = (int64_t)ceil(raw_blocks_per_row * (double)context);
+    per_layer = rows * row_bytes + slots * 32;
+  }
+  return kv_budget / (per_layer * layers);
+}
+
 static double bf16_value(uint16_t x) {
   uint32_t u = (uint32_t)x << 16;
   float f;

@@ -19,6 +19,14 @@
  *      nibbles (exponent >> 4), packed the same way, in a 32-byte spill slot.
  *  - Spill slots: a token row's raw blocks take consecutive slots in block order; rows are
  *    numbered (sequence, token) ascending for a full encode and in batch order for an append.
+ *  - Spill lifecycle: pages come and go with their sequences (paged cache: page "Open
+ *    Weights: from files to tokens / second", section "09 / The optimization stack"), but the
+ *    spill pool only grows; compaction rewrites it for the sequences still live, as if they had
+ *    been encoded into an empty pool: slots from 0 in (sequence, token) order.
+ *  - Capacity (same page, step "Spend the memory dividend" of its deployment checklist, and
+ *    section "05 / Memory is the admission ticket"): the device memory left after the weights
+ *    (parameters x bits / 8) and a reserve goes to the paged KV cache, and the number of
+ *    sequences that fit is that budget over one sequence's cache across all layers.
  *  - Attention (page "Open Weights: from files to tokens / second", section
  *    "03 / The inference loop"): one query token per sequence attends over every cached token of its
  *    sequence; grouped-query heads share a KV head (q head -> q / (Hq / Hkv)); scaled dot
@@ -83,6 +91,21 @@ uint32_t orc_append_kv_n(const orc_geom* g, orc_cache* c, int32_t batch, int32_t
 uint32_t orc_decode_kv(const orc_geom* g, const orc_cache* c, int32_t batch,
                        const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
                        uint16_t* raw_out);
+/* Compaction of the spill pool for the listed sequences: the raw blocks of their rows
+ * [0, seq_lens[b]) move to slots 0, 1, ... in (sequence, token) order, row_spill of those rows
+ * follows, spill_top becomes their count.  Rows of other sequences are not touched (their
+ * slots are given up).  All or nothing: a listed row whose slots are not inside
+ * [0, spill_top) fails the call with ORC_ESPILL before anything is written. */
+uint32_t orc_compact_spill(const orc_geom* g, orc_cache* c, int32_t batch,
+                           const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages);
+/* Capacity model: how many sequences of `context` tokens fit in `kv_budget` bytes of
+ * device memory across `layers` layers.  Per sequence and layer: ceil(context / T) pages of
+ * T token rows.  Uncompressed (raw_blocks_per_row < 0): a row is H x 2 x D bf16 values.
+ * Packed: a row is its planes (sm D bytes, offsets D/2 bytes, one base byte per 64 values,
+ * for H x 2 vectors) plus a flag word and a spill index (4 bytes each), and the sequence adds
+ * ceil(raw_blocks_per_row x context) spill slots of 32 bytes. */
+int64_t orc_max_sequences(int64_t kv_budget, int32_t layers, int32_t context, int32_t page_size,
+                          int32_t num_kv_heads, int32_t head_dim, double raw_blocks_per_row);
 /* fp64 decode attention over raw bf16 pages; q u16[B][Hq][D]; out f64[B][Hq][D].
  * `want` (u8[B][Hq], may be NULL = all) selects which (sequence, q head) rows to compute. */
 uint32_t orc_attention(const orc_geom* g, int32_t batch, int32_t num_q_heads,
