@@ -265,7 +265,8 @@ def main():
 def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_bytes):
     """Twin (uncompressed) attention over the same rotation of layer caches, the unfused
     alternative (decode to bf16, then the twin), a plain streaming read over the same bytes,
-    the single-layer warm-cache loop, and full-cache encode / decode rates."""
+    the single-layer warm-cache loop, full-cache encode / decode rates, multi-token append,
+    spill compaction, and the capacity model at a fixed HBM budget."""
     res = {}
     stream = torch.cuda.current_stream()
     NL = len(layers)
@@ -358,6 +359,32 @@ def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_byte
     res["append_n_us"] = round(t_app * 1e6, 1)
     res["append_n_rows_per_s"] = round(inst.w.batch * n_new / t_app, 1)
     res["decode_us"] = round(t_dec * 1e6, 1)
+    # spill compaction (sequence free): layer 1 with every sequence live (its slots are
+    # interleaved by the appends), then layer 2 with every other sequence freed
+    for name, lay, live in (("all_live", 1, slice(None)), ("half_freed", 2, slice(0, None, 2))):
+        cache, seqs = layers[lay]
+        sub = zf.Seqs(seqs.page_table[live].contiguous(), seqs.seq_lens[live].contiguous(),
+                      seqs.max_seq_len)
+        cws = zf.compact_workspace(cache, sub)
+        top_in = int(cache.spill_top.item())
+        t_cmp = timeit(lambda i: zf.zf_compact_spill(cache, sub, cws), n=10)
+        assert zf.zf_get_status(cache.status) == 0
+        moved = int(cache.spill_top.item())
+        res[f"compact_{name}_us"] = round(t_cmp * 1e6, 1)
+        res[f"compact_{name}_slots"] = [top_in, moved]
+    # capacity at a fixed HBM budget, Llama-3.1-8B-shaped KV (32 layers, 8 kv heads, D 128):
+    # 288 GB of HBM less the bf16 weights (8.03e9 parameters x 16 bits / 8) and a 10 % reserve
+    w = inst.w
+    budget = int(288e9 - 8.03e9 * 16 / 8 - 0.1 * 288e9)
+    raw_per_row = top / rows
+    ctx = int(inst.seq_lens.max())
+    n_bf16 = zf.zf_max_sequences(budget, 32, ctx, w.page_size, w.num_kv_heads, w.head_dim, None)
+    n_pack = zf.zf_max_sequences(budget, 32, ctx, w.page_size, w.num_kv_heads, w.head_dim,
+                                 raw_per_row)
+    res["capacity"] = {"kv_budget_bytes": budget, "layers": 32, "context": ctx,
+                       "raw_blocks_per_row": round(raw_per_row, 3),
+                       "sequences_bf16": n_bf16, "sequences_packed": n_pack,
+                       "gain": round(n_pack / n_bf16, 3)}
     return res
 
 

@@ -20,7 +20,7 @@ ZF_OK, ZF_EINVAL, ZF_EUNSUPPORTED, ZF_EHIP, ZF_EWORKSPACE = 0, 1, 2, 3, 4
 ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN = 1, 2, 4
 
 EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_append_kv",
-           "zf_append_kv_n",
+           "zf_append_kv_n", "zf_compact_spill", "zf_compact_workspace_bytes", "zf_max_sequences",
            "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_raw",
            "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
            "zf_stream_read_probe", "zf_get_status", "zf_status_str")
@@ -68,6 +68,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "zf_encode_workspace_bytes": (sz, [ps]),
         "zf_append_kv": (ctypes.c_int, [pc, ps, vp, vp, vp]),
         "zf_append_kv_n": (ctypes.c_int, [pc, ps, i32, vp, vp, vp]),
+        "zf_compact_spill": (ctypes.c_int, [pc, ps, vp, sz, vp]),
+        "zf_compact_workspace_bytes": (sz, [pc, ps]),
+        "zf_max_sequences": (ctypes.c_int64, [ctypes.c_int64, i32, i32, i32, i32, i32,
+                                              ctypes.c_double]),
         "zf_decode_kv": (ctypes.c_int, [pc, ps, vp, vp]),
         "zf_decode_attention": (ctypes.c_int, [pc, ps, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
         "zf_decode_attention_raw": (ctypes.c_int, [vp, i32, i32, i32, i32, ps, vp, i32,
@@ -187,6 +191,26 @@ def zf_append_kv_n(cache: PackedCache, seqs: Seqs, k_new: torch.Tensor, v_new: t
                                  _ptr(k_new), _ptr(v_new), _stream(stream)), "zf_append_kv_n")
 
 
+def zf_compact_workspace_bytes(cache: PackedCache, seqs: Seqs) -> int:
+    return load().zf_compact_workspace_bytes(ctypes.byref(cache.c()), ctypes.byref(seqs.c()))
+
+
+def zf_compact_spill(cache: PackedCache, seqs: Seqs, workspace: torch.Tensor, stream=None) -> None:
+    """Moves the raw blocks of the sequences in `seqs` to the front of the spill pool (the
+    others' slots are given up)."""
+    _check(load().zf_compact_spill(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "zf_compact_spill")
+
+
+def zf_max_sequences(kv_budget_bytes: int, layers: int, context: int, page_size: int,
+                     num_kv_heads: int, head_dim: int, raw_blocks_per_row: float | None) -> int:
+    """Sequences of `context` tokens whose caches fit in the budget; None = bf16 pages."""
+    r = -1.0 if raw_blocks_per_row is None else float(raw_blocks_per_row)
+    return int(load().zf_max_sequences(kv_budget_bytes, layers, context, page_size, num_kv_heads,
+                                       head_dim, r))
+
+
 def zf_decode_kv(cache: PackedCache, seqs: Seqs, raw_out: torch.Tensor, stream=None) -> None:
     _check(load().zf_decode_kv(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(raw_out),
                                _stream(stream)), "zf_decode_kv")
@@ -252,6 +276,10 @@ def attention_workspace(batch, num_kv_heads, num_q_heads, head_dim, max_seq_len,
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     zf_attention_workspace_init(ws)
     return ws
+
+
+def compact_workspace(cache: PackedCache, seqs: Seqs, device="cuda") -> torch.Tensor:
+    return torch.empty(zf_compact_workspace_bytes(cache, seqs), dtype=torch.uint8, device=device)
 
 
 def encode_workspace(seqs: Seqs, device="cuda") -> torch.Tensor:

@@ -1,4 +1,5 @@
 // zf_api.hip - the C ABI: argument checks, workspace sizing, kernel launches.
+#include <math.h>
 #include <string.h>
 
 #include "zf_internal.h"
@@ -11,6 +12,8 @@ int append_max_rows();
 hipError_t launch_append(const Geom&, const zf_cache*, const zf_seqs*, int32_t, const uint16_t*,
                          const uint16_t*, hipStream_t);
 hipError_t launch_decode(const Geom&, const zf_cache*, const zf_seqs*, uint16_t*, hipStream_t);
+size_t compact_workspace_bytes(const zf_cache*, const zf_seqs*);
+hipError_t launch_compact(const Geom&, const zf_cache*, const zf_seqs*, void*, size_t, hipStream_t);
 hipError_t launch_attention_packed(const zf_cache*, const zf_seqs*, const uint16_t*, float,
                                    float*, void*, hipStream_t);
 hipError_t launch_attention_raw(const uint16_t*, int32_t, int32_t, const zf_seqs*,
@@ -124,6 +127,47 @@ zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_n
 zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
                        const uint16_t* v_new, zf_stream_t stream) {
   return zf_append_kv_n(cache, seqs, 1, k_new, v_new, stream);
+}
+
+size_t zf_compact_workspace_bytes(const zf_cache* cache, const zf_seqs* seqs) {
+  if (check_cache(cache) != ZF_OK || check_seqs(seqs, cache->page_size) != ZF_OK) return 0;
+  return zf::compact_workspace_bytes(cache, seqs);
+}
+
+zf_status zf_compact_spill(const zf_cache* cache, const zf_seqs* seqs, void* workspace,
+                           size_t workspace_bytes, zf_stream_t stream) {
+  zf_status s = check_cache(cache);
+  if (s != ZF_OK) return s;
+  if ((s = check_seqs(seqs, cache->page_size)) != ZF_OK) return s;
+  if (seqs->batch > kMaxEncodeBatch) return ZF_EUNSUPPORTED;
+  // the header and the page counts at least; the staging area behind them may be smaller
+  // than the pool (the device then checks that it holds the live slots)
+  zf_cache head_only = *cache;
+  head_only.spill_slots = 0;
+  if (!aligned(workspace) || workspace_bytes < zf::compact_workspace_bytes(&head_only, seqs))
+    return ZF_EWORKSPACE;
+  return hip_status(zf::launch_compact(geom_of(cache), cache, seqs, workspace, workspace_bytes,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int64_t zf_max_sequences(int64_t kv_budget_bytes, int32_t layers, int32_t context,
+                         int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                         double raw_blocks_per_row) {
+  if (kv_budget_bytes <= 0 || layers <= 0 || context <= 0) return 0;
+  if (check_geom(1, page_size, num_kv_heads, head_dim) != ZF_OK) return -1;
+  const int64_t pages = ((int64_t)context + page_size - 1) / page_size;
+  const int64_t values = (int64_t)num_kv_heads * 2 * head_dim;  // per token row
+  int64_t page_bytes, spill_bytes = 0;
+  if (raw_blocks_per_row < 0) {
+    page_bytes = (int64_t)page_size * values * 2;
+  } else {
+    const int64_t blocks = values / 64;
+    if (raw_blocks_per_row > (double)blocks) return -1;
+    page_bytes = (int64_t)zf_cache_bytes(1, page_size, num_kv_heads, head_dim);
+    spill_bytes = 32 * (int64_t)ceil(raw_blocks_per_row * (double)context);
+  }
+  const int64_t per_seq = ((int64_t)pages * page_bytes + spill_bytes) * layers;
+  return kv_budget_bytes / per_seq;
 }
 
 zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw_pages_out,

@@ -15,6 +15,8 @@
 
 namespace zf {
 
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
 struct SeqView {
   int32_t B, maxp, max_seq_len;
   const int32_t* pt;
@@ -98,8 +100,9 @@ __global__ __launch_bounds__(256) void enc_pack_k(Geom g, SeqView s, const uint1
 
 // ------------------------------------------------------------------------------ encode: scan
 
-// One workgroup.  Turns per-page raw counts into exclusive prefixes (offset by *spill_top) in
-// (sequence, page) order; flags the call as failed when the pool is too small.
+// One workgroup.  Turns per-page raw counts into exclusive prefixes (offset by *top_in) in
+// (sequence, page) order and stores the end in *top_out; flags the call as failed when the
+// `spill_slots` slots of the target do not hold them.
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 8;
 
@@ -122,8 +125,9 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* 
 
 __global__ __launch_bounds__(kScanThreads) void enc_scan_k(Geom g, SeqView s,
                                                            uint32_t* __restrict__ page_count,
-                                                           uint64_t* spill_top, uint64_t spill_slots,
-                                                           uint32_t* ws_flag, uint32_t* status) {
+                                                           const uint64_t* top_in, uint64_t* top_out,
+                                                           uint64_t spill_slots, uint32_t* ws_flag,
+                                                           uint32_t* status) {
   extern __shared__ uint32_t s_off[];  // [B + 1] page offsets, then kScanThreads scratch
   uint32_t* s_tmp = s_off + s.B + 1;
   __shared__ uint32_t s_total;
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan_k(Geom g, SeqView s,
   if (tid == 0) s_off[s.B] = carry;
   __syncthreads();
   const uint32_t nchunks = s_off[s.B];
-  const uint64_t top = *spill_top;
+  const uint64_t top = *top_in;
 
   // two passes: total, then prefixes (only if the pool holds them)
   for (int pass = 0; pass < 2; ++pass) {
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan_k(Geom g, SeqView s,
       }
       if (tid == 0) {
         *ws_flag = 0u;
-        *spill_top = top + run;
+        *top_out = top + run;
       }
     }
   }
@@ -448,6 +452,120 @@ __global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t
   if (err) set_status(status, err);
 }
 
+// ------------------------------------------------------------------------------ compaction
+
+// Spill compaction for the sequences passed in: their raw blocks move to slots 0, 1, ... in
+// (sequence, token) order, the order an encode into an empty pool takes (page "Open Weights:
+// from files to tokens / second", section "09 / The optimization stack": pages return to the
+// pool with their sequences; the spill pool is this format's own overflow area).  Runs as
+// count -> scan -> gather -> copy back, through a staging area in the workspace, so the slots
+// read and the slots written never overlap within a kernel.  All or nothing: the count pass
+// checks every row (page id, length, slots inside [0, spill_top)) and the scan checks that the
+// staging area holds the result; on any failure the gather and copy passes write nothing.
+//
+// Workspace header (256 bytes): word 0 scan failure, word 1 row failure, bytes 16..23 a zero
+// u64 (the scan's start), bytes 24..31 the new spill_top.
+struct CompactWs {
+  uint32_t* scan_flag;
+  uint32_t* row_err;
+  const uint64_t* zero;
+  uint64_t* new_top;
+  uint32_t* page_count;
+  uint8_t* staging;
+  uint64_t staging_slots;
+};
+
+__global__ __launch_bounds__(64) void compact_count_k(Geom g, SeqView s, const uint32_t* __restrict__ row_flags,
+                                                      const uint32_t* __restrict__ row_spill,
+                                                      const uint64_t* spill_top, uint64_t spill_slots,
+                                                      CompactWs w, uint32_t* status) {
+  const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int32_t L;
+  const int rows = rows_in_page(s, g, b, p, &L);
+  if (rows < 0) {
+    if (p == 0 && tid == 0) {
+      set_status(status, ZF_DEV_ELEN);
+      atomicOr(w.row_err, ZF_DEV_ELEN);
+    }
+    return;
+  }
+  if (rows == 0) return;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
+  if (pid < 0 || pid >= g.P) {
+    if (tid == 0) {
+      set_status(status, ZF_DEV_EPAGE);
+      atomicOr(w.row_err, ZF_DEV_EPAGE);
+      w.page_count[(int64_t)b * s.maxp + p] = 0u;
+    }
+    return;
+  }
+  const uint64_t top = min(*spill_top, spill_slots);  // the slots that hold data
+  uint32_t n = 0u;
+  bool bad = false;
+  if (tid < rows) {
+    const int64_t row = (int64_t)pid * g.T + tid;
+    n = __popc(row_flags[row]);
+    bad = n > 0u && (uint64_t)row_spill[row] + n > top;
+  }
+  if (__any(bad) && tid == 0) {
+    set_status(status, ZF_DEV_ESPILL);
+    atomicOr(w.row_err, ZF_DEV_ESPILL);
+  }
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
+  if (tid == 0) w.page_count[(int64_t)b * s.maxp + p] = n;
+}
+
+__global__ __launch_bounds__(256) void compact_gather_k(Geom g, SeqView s, const uint32_t* __restrict__ row_flags,
+                                                        uint32_t* __restrict__ row_spill,
+                                                        const uint8_t* __restrict__ spill, CompactWs w) {
+  if (*w.scan_flag != 0u || *w.row_err != 0u) return;
+  const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int32_t L;
+  const int rows = rows_in_page(s, g, b, p, &L);
+  if (rows <= 0) return;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + p];  // checked by the count pass
+  __shared__ uint32_t s_n[64], s_old[64], s_new[64];
+  if (tid < 64) {
+    const int64_t row = (int64_t)pid * g.T + tid;
+    const uint32_t n = tid < rows ? (uint32_t)__popc(row_flags[row]) : 0u;
+    uint32_t incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t up = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += up;
+    }
+    const uint32_t first = w.page_count[(int64_t)b * s.maxp + p] + (incl - n);
+    s_n[tid] = n;
+    s_new[tid] = first;
+    if (tid < rows) {
+      s_old[tid] = row_spill[row];  // this lane reads the row's old index, then replaces it
+      row_spill[row] = first;
+    }
+  }
+  __syncthreads();
+  // 16-byte halves of the moved slots: row r, slot i, half k
+  for (int m = tid; m < rows * 64; m += blockDim.x) {
+    const int r = m >> 6, i = (m & 63) >> 1, k = m & 1;
+    if ((uint32_t)i >= s_n[r]) continue;
+    const uint64_t from = ((uint64_t)s_old[r] + i) * 32u + k * 16u;
+    const uint64_t to = ((uint64_t)s_new[r] + i) * 32u + k * 16u;
+    *reinterpret_cast<uint4*>(w.staging + to) = *reinterpret_cast<const uint4*>(spill + from);
+  }
+}
+
+constexpr int kCopyBlocks = 1024;
+
+__global__ __launch_bounds__(256) void compact_copy_k(CompactWs w, uint8_t* __restrict__ spill,
+                                                      uint64_t* spill_top) {
+  if (*w.scan_flag != 0u || *w.row_err != 0u) return;
+  const uint64_t total = *w.new_top;
+  const uint64_t n16 = total * 2u;  // 16-byte pieces
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    reinterpret_cast<uint4*>(spill)[i] = reinterpret_cast<const uint4*>(w.staging)[i];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *spill_top = total;
+}
+
 // ------------------------------------------------------------------------------ host launchers
 
 static SeqView view(const zf_seqs* q) {
@@ -464,7 +582,7 @@ hipError_t launch_encode(const Geom& g, const zf_cache* c, const zf_seqs* q, con
                      c->row_flags, page_count, c->status);
   size_t lds = ((size_t)q->batch + 1 + kScanThreads) * sizeof(uint32_t);
   hipLaunchKernelGGL(enc_scan_k, dim3(1), dim3(kScanThreads), lds, st, g, s, page_count,
-                     c->spill_top, c->spill_slots, ws_flag, c->status);
+                     c->spill_top, c->spill_top, c->spill_slots, ws_flag, c->status);
   hipLaunchKernelGGL(enc_spill_k, grid, dim3(256), 0, st, g, s, raw, c->row_flags, c->row_spill,
                      c->spill, page_count, ws_flag, c->spill_slots);
   return hipGetLastError();
@@ -489,6 +607,46 @@ hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int
   size_t lds = 2 * (size_t)rows * sizeof(uint32_t);
   hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, n, k_new, v_new,
                      c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
+  return hipGetLastError();
+}
+
+static size_t compact_head_bytes(const zf_seqs* q) {
+  const size_t counts = (size_t)q->batch * (size_t)q->max_pages_per_seq * sizeof(uint32_t);
+  return 256 + (counts + 255) / 256 * 256;
+}
+
+size_t compact_workspace_bytes(const zf_cache* c, const zf_seqs* q) {
+  return compact_head_bytes(q) + (size_t)c->spill_slots * 32u;
+}
+
+hipError_t launch_compact(const Geom& g, const zf_cache* c, const zf_seqs* q, void* ws, size_t ws_bytes,
+                          hipStream_t st) {
+  SeqView s = view(q);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const size_t head = compact_head_bytes(q);
+  CompactWs w;
+  w.scan_flag = reinterpret_cast<uint32_t*>(base);
+  w.row_err = reinterpret_cast<uint32_t*>(base) + 1;
+  w.zero = reinterpret_cast<const uint64_t*>(base + 16);
+  w.new_top = reinterpret_cast<uint64_t*>(base + 24);
+  w.page_count = reinterpret_cast<uint32_t*>(base + 256);
+  w.staging = base + head;
+  // the live blocks must fit both the staging area and the pool (rows that alias each other's
+  // slots could otherwise count more blocks than the pool has)
+  w.staging_slots = std::min<uint64_t>((ws_bytes - head) / 32u, c->spill_slots);
+  hipError_t e = launch_fill_zero(base, 256, st);
+  if (e != hipSuccess) return e;
+  dim3 grid(q->max_pages_per_seq, q->batch);
+  if (q->batch > 0)
+    hipLaunchKernelGGL(compact_count_k, grid, dim3(64), 0, st, g, s, c->row_flags, c->row_spill,
+                       c->spill_top, c->spill_slots, w, c->status);
+  size_t lds = ((size_t)q->batch + 1 + kScanThreads) * sizeof(uint32_t);
+  hipLaunchKernelGGL(enc_scan_k, dim3(1), dim3(kScanThreads), lds, st, g, s, w.page_count, w.zero,
+                     w.new_top, w.staging_slots, w.scan_flag, c->status);
+  if (q->batch > 0)
+    hipLaunchKernelGGL(compact_gather_k, grid, dim3(256), 0, st, g, s, c->row_flags, c->row_spill,
+                       c->spill, w);
+  hipLaunchKernelGGL(compact_copy_k, dim3(kCopyBlocks), dim3(256), 0, st, w, c->spill, c->spill_top);
   return hipGetLastError();
 }
 

@@ -126,6 +126,42 @@ zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_
 zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_new,
                          const uint16_t* k_new, const uint16_t* v_new, zf_stream_t stream);
 
+/* Spill lifecycle (pages come and go with their sequences: page "Open Weights: from files to
+ * tokens / second", section "09 / The optimization stack"; the spill pool is this format's
+ * overflow area for raw blocks, and encode and append only ever grow it).  `seqs` lists the
+ * sequences still live; a sequence that ended is freed by leaving it out.  Their raw blocks
+ * move to spill slots 0, 1, ... in (sequence, token) order, the row spill index of each of
+ * their rows follows (rows without raw blocks get the running count, as encode writes it), and
+ * *spill_top becomes the number of those blocks: the layout an encode of just these sequences
+ * into an empty pool produces.  Rows of other sequences are not touched; their slots are
+ * given up.  Planes, bases and row flags are not touched.  The listed sequences must not share
+ * pages (as for encode).  batch == 0 empties the pool.
+ * All or nothing: if a listed row's page id or length is invalid (ZF_DEV_EPAGE, ZF_DEV_ELEN),
+ * a listed row's raw blocks are not inside [0, min(spill_top, spill_slots)) (ZF_DEV_ESPILL),
+ * or the live blocks outnumber the staging area's slots or the pool's (ZF_DEV_ESPILL; rows
+ * that alias each other's slots can do that), the status word says so
+ * and nothing else changes.  Workspace: device memory, any contents; a 256-byte header, the
+ * page counts, then a staging area of 32 bytes per slot.  zf_compact_workspace_bytes gives
+ * room for every slot of the pool; a smaller workspace (at least the header and counts) works
+ * when its staging area holds the live blocks.  Five kernel launches, none allocates.
+ * Supports batch <= 8192. */
+zf_status zf_compact_spill(const zf_cache* cache, const zf_seqs* seqs, void* workspace,
+                           size_t workspace_bytes, zf_stream_t stream);
+size_t zf_compact_workspace_bytes(const zf_cache* cache, const zf_seqs* seqs);
+
+/* Capacity model (page "Open Weights: from files to tokens / second": the memory left after
+ * the weights, parameters x bits / 8, and a runtime reserve goes to the paged KV cache, and
+ * more cache pages admit more concurrent sequences; the ZipFusion video summary puts most of
+ * its gain there).  Returns how many sequences of `context` tokens fit in `kv_budget_bytes`
+ * across `layers` layers: each sequence and layer holds ceil(context / page_size) pages;
+ * raw_blocks_per_row < 0 prices them as bf16 pages (H x 2 x D values of 2 bytes per row),
+ * otherwise as packed pages (zf_cache_bytes per page) plus ceil(raw_blocks_per_row x context)
+ * spill slots of 32 bytes.  0 for a non-positive budget, layer count or context; -1 for an
+ * unsupported geometry or more raw blocks per row than a row has.  Host only. */
+int64_t zf_max_sequences(int64_t kv_budget_bytes, int32_t layers, int32_t context,
+                         int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                         double raw_blocks_per_row);
+
 /* Inverse of the codec: writes rows t < seq_lens[b] as raw bf16 pages (lossless: the bits
  * that were encoded). */
 zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw_pages_out,

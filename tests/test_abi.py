@@ -78,6 +78,39 @@ def test_bad_cache_is_rejected_before_any_launch(kw, code):
     assert lib.zf_decode_kv(ctypes.byref(c), ctypes.byref(s), 2304, None) == code
     assert lib.zf_append_kv(ctypes.byref(c), ctypes.byref(s), 4096, 4096, None) == code
     assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 2, 4096, 4096, None) == code
+    assert lib.zf_compact_spill(ctypes.byref(c), ctypes.byref(s), 4096, 1 << 20, None) == code
+    assert lib.zf_compact_workspace_bytes(ctypes.byref(c), ctypes.byref(s)) == 0
+
+
+def test_compact_workspace_and_arguments():
+    lib = zf.load()
+    c = _cache(spill_slots=100)
+    s = zf.zf_seqs(3, 5, 4096, 4096, 80)
+    # 256-byte header, page counts rounded to 256 bytes, then 32 bytes per pool slot
+    assert lib.zf_compact_workspace_bytes(ctypes.byref(c), ctypes.byref(s)) == 256 + 256 + 3200
+    head = 512
+    assert lib.zf_compact_spill(ctypes.byref(c), ctypes.byref(s), 4096, head - 1, None) == zf.ZF_EWORKSPACE
+    assert lib.zf_compact_spill(ctypes.byref(c), ctypes.byref(s), 4100, 1 << 20, None) == zf.ZF_EWORKSPACE
+    assert lib.zf_compact_spill(ctypes.byref(c), ctypes.byref(s), None, 1 << 20, None) == zf.ZF_EWORKSPACE
+    big = zf.zf_seqs(8193, 1, 4096, 4096, 16)
+    assert lib.zf_compact_spill(ctypes.byref(c), ctypes.byref(big), 4096, 1 << 30, None) == zf.ZF_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("budget,layers,ctx,raw", [
+    (80 << 30, 32, 4096, None), (80 << 30, 32, 4096, 0.0), (80 << 30, 32, 4096, 9.08),
+    (288 << 30, 32, 4097, 32.0), (272 << 30, 32, 131072, 7.5), (1 << 20, 1, 1, 1.0),
+    (0, 32, 4096, None), (1 << 30, 0, 4096, 1.0), (1 << 30, 32, 0, 1.0),
+])
+def test_max_sequences_matches_the_oracle(budget, layers, ctx, raw):
+    """A host-only function: the library and the oracle's capacity model agree."""
+    import oracle
+    got = zf.zf_max_sequences(budget, layers, ctx, 16, 8, 128, raw)
+    assert got == oracle.max_sequences(budget, layers, ctx, 16, 8, 128, raw)
+
+
+def test_max_sequences_rejects_bad_geometry():
+    assert zf.zf_max_sequences(1 << 30, 32, 4096, 16, 8, 100, 0.0) == -1
+    assert zf.zf_max_sequences(1 << 30, 32, 4096, 16, 8, 128, 33.0) == -1  # a row has 32 blocks
 
 
 def test_append_n_arguments():
