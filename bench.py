@@ -56,8 +56,10 @@ STAMP_EVERY = 4  # timed steps per kernel-stamped step
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=150)
+    ap.add_argument("--warmup", type=int, default=150,
+                    help="untimed steps first: an idle MI355X needs ~10 ms of load to reach "
+                         "its working clock (the first ms run ~15 %% slower)")
     ap.add_argument("--layers", type=int, default=3,
                     help="layer caches the steps rotate over (1.35 GB at 3, beyond the 256 MB "
                          "last-level cache, as in a multi-layer model)")
@@ -418,6 +420,8 @@ def per_config(torch, zf, synth, wi, dev):
     N = 30
 
     def run(fn, stamps):
+        for i in range(3 * N):  # untimed: bring the GPU to its working clock
+            fn(i)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N)]
         for e in ev:
             for x in e:

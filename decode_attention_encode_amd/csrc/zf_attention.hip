@@ -504,15 +504,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   };
   if (a.order) {
     // More workgroups than CUs: when the lengths differ, the (sequence, split) groups are
-    // dispatched longest sequence first (ties: lower index), group g with all its kv heads on
-    // XCD g % 8, so that long jobs start first and short ones fill the end.  Each wave finds
-    // the same job on its own, with its LDS region as scratch (no pages are in flight yet).
-    int32_t* wl = reinterpret_cast<int32_t*>(&s_ring[wave][0]);  // [B] lengths, [B] splits
+    // dispatched largest first (longest-processing-time-first list scheduling), group g with
+    // all its kv heads on XCD g % 8, so that long jobs start first and short ones fill the end.
+    // A sequence's splits hold a.pps pages each except its last, which holds the rest: the
+    // full splits come first in (sequence, split) order, then the partial last splits by size
+    // (ties: lower sequence).  Each wave finds the same job on its own, with its LDS region as
+    // scratch (no pages are in flight yet).
+    int32_t* wl = reinterpret_cast<int32_t*>(&s_ring[wave][0]);  // [B] full splits, [B] rest
     int32_t lmin = 0x7FFFFFFF, lmax = -1;
     for (int i = lane; i < a.B; i += 64) {
       const int32_t li = max(0, min(a.lens[i], cap));
-      wl[i] = li;
-      wl[kOrderMaxBatch + i] = splits_of(li);
+      const int32_t pages = (li + kT - 1) / kT;
+      const int32_t full = pages / a.pps;
+      // pages of the partial last split, -1 when there is none (an empty sequence still has
+      // one split, of 0 pages)
+      wl[i] = full;
+      wl[kOrderMaxBatch + i] = full == splits_of(li) ? -1 : pages - full * a.pps;
       lmin = min(lmin, li);
       lmax = max(lmax, li);
     }
@@ -525,16 +532,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     if (lmin != lmax) {
       const uint32_t g = (local / (uint32_t)a.H) * kXcds + xcd;
       int mb = -1, ms = 0;
+      uint32_t nfull = 0;  // full splits of all sequences
+      for (int k = 0; k < a.B; ++k) nfull += (uint32_t)wl[k];
       for (int i = lane; i < a.B; i += 64) {
-        const int32_t li = wl[i];
-        uint32_t first = 0;  // groups of the sequences ranked before i
+        const int32_t ri = wl[kOrderMaxBatch + i];
+        uint32_t first = 0, before = 0;  // full splits of sequences < i; partials ranked before i's
         for (int k = 0; k < a.B; ++k) {
-          const int32_t lk = wl[k];
-          if (lk > li || (lk == li && k < i)) first += (uint32_t)wl[kOrderMaxBatch + k];
+          const int32_t rk = wl[kOrderMaxBatch + k];
+          if (k < i) first += (uint32_t)wl[k];
+          if (rk > ri || (rk == ri && k < i)) before += 1u;
         }
-        if (g >= first && g < first + (uint32_t)wl[kOrderMaxBatch + i]) {
+        if (g >= first && g < first + (uint32_t)wl[i]) {
           mb = i;
           ms = (int)(g - first);
+        } else if (ri >= 0 && g == nfull + before) {
+          mb = i;
+          ms = wl[i];
         }
       }
       const uint64_t found = __ballot(mb >= 0);
