@@ -14,11 +14,12 @@ hipError_t launch_append(const Geom&, const zf_cache*, const zf_seqs*, int32_t, 
 hipError_t launch_decode(const Geom&, const zf_cache*, const zf_seqs*, uint16_t*, hipStream_t);
 size_t compact_workspace_bytes(const zf_cache*, const zf_seqs*);
 hipError_t launch_compact(const Geom&, const zf_cache*, const zf_seqs*, void*, size_t, hipStream_t);
-hipError_t launch_attention_packed(const zf_cache*, const zf_seqs*, const uint16_t*, float,
-                                   float*, void*, hipStream_t);
+hipError_t launch_attention_packed(const zf_cache*, const zf_seqs*, const uint16_t*, int32_t,
+                                   float, float*, void*, hipStream_t);
 hipError_t launch_attention_raw(const uint16_t*, int32_t, int32_t, const zf_seqs*,
-                                const uint16_t*, float, float*, void*, uint32_t*, hipStream_t);
-size_t attention_workspace_bytes(int32_t, int32_t, int32_t);
+                                const uint16_t*, int32_t, float, float*, void*, uint32_t*,
+                                hipStream_t);
+size_t attention_workspace_bytes(int32_t, int32_t, int32_t, int32_t);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
 void set_attention_timing(hipEvent_t, hipEvent_t);
 }  // namespace zf
@@ -68,10 +69,11 @@ zf::Geom geom_of(const zf_cache* c) {
 
 zf_status hip_status(hipError_t e) { return e == hipSuccess ? ZF_OK : ZF_EHIP; }
 
-// The attention kernels are written for one shape.
+// The attention kernels are written for head_dim 128, 16-token pages and 4 or 8 query heads
+// per kv head.
 zf_status check_attention_shape(int32_t T, int32_t H, int32_t D, int32_t Hq) {
   if (Hq <= 0) return ZF_EINVAL;
-  if (D != 128 || T != 16 || Hq != 4 * H) return ZF_EUNSUPPORTED;
+  if (D != 128 || T != 16 || (Hq != 4 * H && Hq != 8 * H)) return ZF_EUNSUPPORTED;
   return ZF_OK;
 }
 
@@ -185,7 +187,7 @@ size_t zf_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t
                                     int32_t head_dim, int32_t max_seq_len) {
   if (batch < 0 || num_kv_heads <= 0 || max_seq_len < 0 || max_seq_len > kMaxAttentionLen) return 0;
   if (check_attention_shape(16, num_kv_heads, head_dim, num_q_heads) != ZF_OK) return 0;
-  return zf::attention_workspace_bytes(batch, num_kv_heads, max_seq_len);
+  return zf::attention_workspace_bytes(batch, num_kv_heads, num_q_heads / num_kv_heads, max_seq_len);
 }
 
 zf_status zf_attention_workspace_init(void* workspace, size_t workspace_bytes,
@@ -200,10 +202,10 @@ static zf_status check_attention_io(const zf_seqs* seqs, int32_t num_kv_heads, i
   if (!aligned(q) || !aligned(out)) return ZF_EINVAL;
   if (seqs->max_seq_len > kMaxAttentionLen) return ZF_EUNSUPPORTED;
   if (!aligned(workspace) ||
-      workspace_bytes < zf::attention_workspace_bytes(seqs->batch, num_kv_heads, seqs->max_seq_len))
+      workspace_bytes < zf::attention_workspace_bytes(seqs->batch, num_kv_heads,
+                                                      num_q_heads / num_kv_heads, seqs->max_seq_len))
     return ZF_EWORKSPACE;
   (void)head_dim;
-  (void)num_q_heads;
   return ZF_OK;
 }
 
@@ -222,7 +224,7 @@ zf_status zf_decode_attention(const zf_cache* cache, const zf_seqs* seqs, const 
   if ((s = check_attention_io(seqs, cache->num_kv_heads, cache->head_dim, q, num_q_heads, out,
                               workspace, workspace_bytes)) != ZF_OK)
     return s;
-  return hip_status(zf::launch_attention_packed(cache, seqs, q, scale, out, workspace,
+  return hip_status(zf::launch_attention_packed(cache, seqs, q, num_q_heads, scale, out, workspace,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -240,7 +242,7 @@ zf_status zf_decode_attention_raw(const uint16_t* raw_pages, int32_t num_pages,
   if ((s = check_attention_io(seqs, num_kv_heads, head_dim, q, num_q_heads, out, workspace,
                               workspace_bytes)) != ZF_OK)
     return s;
-  return hip_status(zf::launch_attention_raw(raw_pages, num_pages, num_kv_heads, seqs, q, scale,
+  return hip_status(zf::launch_attention_raw(raw_pages, num_pages, num_kv_heads, seqs, q, num_q_heads, scale,
                                              out, workspace, status,
                                              static_cast<hipStream_t>(stream)));
 }

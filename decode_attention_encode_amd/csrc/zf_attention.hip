@@ -8,7 +8,8 @@
 // second", section "03 / The inference loop": one new token per sequence attends over its
 // KV cache).
 //
-// Mapping (head_dim 128, 16-token pages, 4 query heads per kv head):
+// Mapping (head_dim 128, 16-token pages, G = 4 query heads per kv head; G = 8 differs only in
+// the number of weight parts, see attn_k):
 //   one workgroup of 8 waves per (split, kv head, sequence); wave w takes pages w, w+8, ...
 //   of its split, one page per step of a software pipeline: row metadata (flags, first spill
 //   slots, bases) six pages ahead, planes and spill slots two pages ahead, all staged in LDS by
@@ -45,7 +46,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // One workgroup of 8 waves per CU (two per SIMD): with two smaller workgroups sharing a CU, the
 // older one is issued first and the younger one then finishes alone at half occupancy.
-constexpr int kD = 128, kT = 16, kG = 4, kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kD = 128, kT = 16, kWaves = 8, kThreads = 64 * kWaves;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr float kBigScore = 64.f;  // |q.k| above which a score may need the fp64 path
 constexpr double kNegligible = 16.0;  // weights below 2^-16 of the largest never need it
@@ -63,8 +64,8 @@ constexpr uint32_t kDone = 0x7FFFFFFFu;  // progress of a wave that has finished
 constexpr int kOrderMaxBatch = 256;  // longest-first group order up to this batch (LDS scratch)
 constexpr int kMaxPagesPerSplit = kWaves * 64;
 constexpr uint32_t kXcds = 8;  // MI355X: workgroups are dispatched round-robin over 8 XCDs  // each wave keeps its page ids in one register
-// One split's partial, in doubles: acc[kG][kD], l[kG], m[kG].
-constexpr int kPartDoubles = kG * kD + 2 * kG;
+// One split's partial for G query heads per kv head, in doubles: acc[G][kD], l[G], m[G].
+__host__ __device__ constexpr int part_doubles(int G) { return G * kD + 2 * G; }
 
 struct AttnArgs {
   int32_t B, H, maxp, max_seq_len, pps, nsplit_max, num_pages;
@@ -75,7 +76,7 @@ struct AttnArgs {
   const uint16_t* q;
   double scale_log2e;
   float* out;
-  double* part;  // [B][H][nsplit_max][kPartDoubles]
+  double* part;  // [B][H][nsplit_max][part_doubles(G)]
   uint32_t* status;
 };
 
@@ -469,11 +470,19 @@ __device__ __forceinline__ float rows_max(float v) {
 // LDS per wave: two page slots and the meta ring; the end-of-split results reuse the wave's
 // own region once its loads have drained.
 constexpr uint32_t kWaveLds = 2 * kSlotBytes + kMetaRing * kMetaBytes;
-static_assert(kG * kD * sizeof(double) + 2 * kG * sizeof(double) <= kWaveLds, "results fit");
+static_assert(8 * kD * sizeof(double) + 2 * 8 * sizeof(double) <= kWaveLds, "results fit");
 static_assert(2 * kOrderMaxBatch * sizeof(int32_t) <= kWaveLds, "order scratch fits");
 
-template <class Loader>
+// G query heads per kv head: 4 (Llama-3.1-8B) or 8 (Llama-3.1-70B).  The score MFMA's 16
+// columns hold each head kParts = 16 / G times, and the p.V MFMA's 16 A rows hold kParts bf16
+// parts of each head's weights: hi, mid, lo (exact, row 3 empty) for G = 4; hi and a rounded
+// second part (within 2^-16 of p) for G = 8.
+template <class Loader, int G>
 __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
+  static_assert(G == 4 || G == 8, "4 or 8 query heads per kv head");
+  constexpr int kParts = 16 / G;           // score columns (and p.V rows) per head
+  constexpr int kHeadsPerLane = G / 4;     // p.V output heads per lane
+  constexpr uint32_t kColMask = (1u << kParts) - 1u;
   // The job: a (sequence b, split s, kv head h).  Workgroup ids go round-robin over the 8
   // XCDs; in the plain order each XCD takes a contiguous run of jobs (split fastest, then kv
   // head, then sequence), so the kv heads of a sequence share one L2 for the page metadata and
@@ -489,12 +498,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 15, qd = lane >> 4;
-  const int head = t >> 2;  // query head of this lane's scores (and of its p.V A-operand row)
-  const int part = t & 3;   // which bf16 part of the weights this lane's A row carries
+  const int head = t / kParts;  // query head of this lane's scores (and of its p.V A-operand row)
+  const int part = t % kParts;  // which bf16 part of the weights this lane's A row carries
   // masks of the weight split below: row 0 keeps p, row 1 takes p - hi, row 2 (p - hi) - mid,
-  // row 3 p - p = 0
-  const uint32_t mask1 = part == 0 ? 0u : part == 3 ? 0xFFFFFFFFu : 0xFFFF0000u;
-  const uint32_t mask2 = part == 2 ? 0xFFFF0000u : 0u;
+  // row 3 p - p = 0; with two parts, row 1 keeps p - hi and rounds it (rnd)
+  const uint32_t mask1 = part == 0 ? 0u : (G == 4 && part == 3) ? 0xFFFFFFFFu : 0xFFFF0000u;
+  const uint32_t mask2 = (G == 4 && part == 2) ? 0xFFFF0000u : 0u;
+  const bool rnd = G == 8 && part == 1;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kWaveLds];
   const int32_t cap = min(a.maxp * kT, a.max_seq_len);
@@ -572,11 +582,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const int p_first = s * a.pps + wave;
   int32_t pt_lane = 0;
   if (p_first + kWaves * lane < a.maxp) pt_lane = a.pt[(int64_t)b * a.maxp + p_first + kWaves * lane];
-  // B operand of the score MFMA: column t is query head t >> 2 (each head four times),
+  // B operand of the score MFMA: column t is query head t / kParts (each head kParts times),
   // head_dim 32*qd + 8c + (0,4,1,5,2,6,3,7)[k]
   bf16x8 qb[4];
   {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.H * kG + h * kG + head) * kD + qd * 32;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.H * G + h * G + head) * kD + qd * 32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 x = *reinterpret_cast<const uint4*>(qrow + 8 * c);
@@ -596,11 +606,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   if (s >= nsplit) return;
 
   // q in fp64, pair order, for the exact-score path: [head][quarter][pair] = (lo, hi) dims
-  __shared__ double2 s_q64[kG][4][16];
-  if (tid < kG * 64) {
+  __shared__ double2 s_q64[G][4][16];
+  if (tid < G * 64) {
     const int i = tid >> 6, qq = (tid >> 4) & 3, k = tid & 15;
     const int dlo = 32 * qq + 8 * (k >> 2) + (k & 3);
-    const uint16_t* qrow = a.q + ((int64_t)b * a.H * kG + h * kG + i) * kD;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.H * G + h * G + i) * kD;
     s_q64[i][qq][k] = make_double2((double)__uint_as_float((uint32_t)qrow[dlo] << 16),
                                    (double)__uint_as_float((uint32_t)qrow[dlo + 4] << 16));
   }
@@ -624,22 +634,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   // pin the q unpacking here: placed after the first page loads, its wait for q would also
   // wait for them
   asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
-  __shared__ double s_gmax[kShareRing][kG];  // per step: max over the waves' running maxima
-  if (tid < kShareRing * kG) s_gmax[tid / kG][tid % kG] = -INFINITY;
+  __shared__ double s_gmax[kShareRing][G];  // per step: max over the waves' running maxima
+  if (tid < kShareRing * G) s_gmax[tid / G][tid % G] = -INFINITY;
   if (lane == 0) s_prog[wave] = nmine > 0 ? 0u : kDone;
   __syncthreads();
 
   double m = -INFINITY;  // running max of head `head`'s unscaled scores (fp64)
   double l = 0.0;        // this lane's share of head `head`'s weight sum (tokens qd + 4i)
-  // p.V output: lane (t, qd) receives rows 4qd..4qd+3 = the hi, mid, lo parts (and an empty
-  // fourth row) of head qd at head_dim vdim(n, t).  The parts of each page's MFMA (which
-  // starts from zero) are summed here in fp64: with outlier values the running sum reaches
-  // 1e4, where one fp32 rounding is already 5e-4.
-  double acc[8];
-  f32x4 cacc[8];  // the MFMA accumulators: rows 4qd + 1, 4qd + 2 carry mid and lo
+  // p.V output: lane (t, qd) receives rows 4qd..4qd+3 at head_dim vdim(n, t): for G = 4 the
+  // hi, mid, lo parts (and an empty fourth row) of head qd; for G = 8 the hi and second parts
+  // of heads 2qd and 2qd + 1.  The hi rows are summed here in fp64: with outlier values the
+  // running sum reaches 1e4, where one fp32 rounding is already 5e-4.
+  double acc[kHeadsPerLane][8];
+  f32x4 cacc[8];  // the MFMA accumulators: rows 4qd + j kParts + r, part r of head slot j
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    acc[n] = 0.0;
+#pragma unroll
+    for (int j = 0; j < kHeadsPerLane; ++j) acc[j][n] = 0.0;
     cacc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const double c2 = a.scale_log2e;
@@ -692,7 +703,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       // lane (t, qd) sums its 32 dims of token krow(t) for each of them, the four quarters are
       // added, and each lane then fetches its own (token, head) entries.  Heads without one keep
       // their fp32 scores.
-      const uint64_t bm = __ballot(big);  // bit 16 qd + t: head t >> 2
+      const uint64_t bm = __ballot(big);  // bit 16 qd + t: head t / kParts
       const uint32_t cols = (uint32_t)(bm | (bm >> 16) | (bm >> 32) | (bm >> 48)) & 0xFFFFu;
       float klo[16], khi[16];  // this lane's K values, exact in fp32
 #pragma unroll
@@ -700,11 +711,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
         klo[k] = __uint_as_float(kp[k] << 16);
         khi[k] = __uint_as_float(kp[k] & 0xFFFF0000u);
       }
-      double pd[kG];
+      double pd[G];
 #pragma unroll
-      for (int i = 0; i < kG; ++i) {
+      for (int i = 0; i < G; ++i) {
         pd[i] = 0.0;
-        if ((cols >> (4 * i)) & 0xFu) {  // wave-uniform
+        if ((cols >> (kParts * i)) & kColMask) {  // wave-uniform
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             const double2 qq = s_q64[i][qd][k];
@@ -714,13 +725,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
           pd[i] = rows_sum_d(pd[i]);
         }
       }
-      // lane (t', qd') offers head qd' of token krow(t'); lane (t, qd) reads token qd + 4i =
-      // krow(4qd + i), head t >> 2
+      // lane (t', qd') offers heads qd' (and qd' + 4) of token krow(t'); lane (t, qd) reads
+      // token qd + 4i = krow(4qd + i), head t / kParts
       const double offer = qd == 0 ? pd[0] : qd == 1 ? pd[1] : qd == 2 ? pd[2] : pd[3];
-      const bool mine = (cols >> (4 * head)) & 0xFu;
+      double offer2 = 0.0;
+      if constexpr (G == 8) offer2 = qd == 0 ? pd[4] : qd == 1 ? pd[5] : qd == 2 ? pd[6] : pd[7];
+      const bool mine = (cols >> (kParts * head)) & kColMask;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const double x = __shfl(offer, head * 16 + 4 * qd + i, 64);
+        double x = __shfl(offer, (head & 3) * 16 + 4 * qd + i, 64);
+        if constexpr (G == 8) {
+          const double x2 = __shfl(offer2, (head & 3) * 16 + 4 * qd + i, 64);
+          x = head >= 4 ? x2 : x;
+        }
         // tokens past the end stay out; heads without a big score keep the fp32 one
         sd[i] = sc[i] == -INFINITY ? -INFINITY : mine ? x : (double)sc[i];
       }
@@ -752,14 +769,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       m32 = (float)m;
       mc2 = m * c2;
       l *= (double)alpha;
-      const float alf = __shfl(alpha, 4 * qd, 64);  // acc holds head qd; lane 4qd has head qd
-      const double al = (double)alf;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-        acc[nn] *= al;
-        cacc[nn][0] *= alf;
-        cacc[nn][1] *= alf;
-        cacc[nn][2] *= alf;
+      for (int j = 0; j < kHeadsPerLane; ++j) {
+        // acc slot j holds head kHeadsPerLane qd + j; lane head * kParts has that head's alpha
+        const float alf = __shfl(alpha, (kHeadsPerLane * qd + j) * kParts, 64);
+        const double al = (double)alf;
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) {
+          acc[j][nn] *= al;
+          cacc[nn][j * kParts] *= alf;
+          cacc[nn][j * kParts + 1] *= alf;
+          if constexpr (G == 4) cacc[nn][2] *= alf;
+        }
       }
     }
     // weights 2^((s - m) c2); a page seen before any finite score leaves m = -inf and mc2 = 0.
@@ -786,12 +807,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     for (int i = 0; i < 4; ++i) {
       const float x1 = p[i] - __uint_as_float(__float_as_uint(p[i]) & mask1);
       xb[i] = __float_as_uint(x1 - __uint_as_float(__float_as_uint(x1) & mask2));
+      // two parts: the second one rounds to nearest even instead of truncating
+      if constexpr (G == 8) xb[i] += rnd ? 0x7FFFu + ((xb[i] >> 16) & 1u) : 0u;
     }
     // the high halves (the truncated bf16 parts) of two values per register
     const s16x4 pa = __builtin_bit_cast(s16x4, (u32x2){__builtin_amdgcn_perm(xb[1], xb[0], 0x07060302u),
                                                         __builtin_amdgcn_perm(xb[3], xb[2], 0x07060302u)});
-    // rows 4qd + (0, 1, 2): hi, mid, lo parts of head qd.  The hi row is moved to fp64 every
-    // kFlushPages pages; mid and lo (below 2^-8 of it) accumulate in the MFMA throughout.
+    // rows 4qd + j kParts + r: part r of head kHeadsPerLane qd + j.  The hi rows are moved to
+    // fp64 every kFlushPages pages; the other parts (below 2^-8 of hi) accumulate in the MFMA
+    // throughout.
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
       const s16x4 vb = __builtin_bit_cast(s16x4, (u32x2){vt[2 * nn], vt[2 * nn + 1]});
@@ -800,8 +824,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     if ((n & (kFlushPages - 1)) == kFlushPages - 1) {
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) {
-        acc[nn] += (double)cacc[nn][0];
-        cacc[nn][0] = 0.f;
+#pragma unroll
+        for (int j = 0; j < kHeadsPerLane; ++j) {
+          acc[j][nn] += (double)cacc[nn][j * kParts];
+          cacc[nn][j * kParts] = 0.f;
+        }
       }
     }
   };
@@ -830,7 +857,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     const uint32_t prog_base = (uint32_t)(uintptr_t)&s_prog[0];
     const uint32_t gmax_base = (uint32_t)(uintptr_t)&s_gmax[0][0];
     auto gmax_at = [&](int step) -> uint32_t {
-      return gmax_base + (uint32_t)(((step & (kShareRing - 1)) * kG + head) * 8);
+      return gmax_base + (uint32_t)(((step & (kShareRing - 1)) * G + head) * 8);
     };
     for (int n = 0; n < nmine; ++n) {
       // step n's running maximum (pages before n) into the workgroup's maximum of step n
@@ -867,52 +894,62 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   // ---- per-wave results to the wave's own LDS region: lane (t, qd) holds head qd at
   //      head_dim vdim(n, t)
 #pragma unroll
-  for (int nn = 0; nn < 8; ++nn) acc[nn] += (double)cacc[nn][0] + (double)cacc[nn][1] + (double)cacc[nn][2];
+  for (int nn = 0; nn < 8; ++nn) {
+    if constexpr (G == 4) {
+      acc[0][nn] += (double)cacc[nn][0] + (double)cacc[nn][1] + (double)cacc[nn][2];
+    } else {
+      acc[0][nn] += (double)cacc[nn][0] + (double)cacc[nn][1];
+      acc[1][nn] += (double)cacc[nn][2] + (double)cacc[nn][3];
+    }
+  }
   l = rows_sum_d(l);
-  double* w_acc = reinterpret_cast<double*>(&s_ring[wave][0]);  // [kG][kD], then m[kG], l[kG]
+  double* w_acc = reinterpret_cast<double*>(&s_ring[wave][0]);  // [G][kD], then m[G], l[G]
 #pragma unroll
-  for (int nn = 0; nn < 8; ++nn) w_acc[qd * kD + vdim(nn, t)] = acc[nn];
-  if (lane < 16 && part == 0) {  // lane 4i holds head i
-    w_acc[kG * kD + head] = m;
-    w_acc[kG * kD + kG + head] = l;
+  for (int nn = 0; nn < 8; ++nn) {
+#pragma unroll
+    for (int j = 0; j < kHeadsPerLane; ++j) w_acc[(kHeadsPerLane * qd + j) * kD + vdim(nn, t)] = acc[j][nn];
+  }
+  if (lane < 16 && part == 0) {  // lane i kParts holds head i
+    w_acc[G * kD + head] = m;
+    w_acc[G * kD + G + head] = l;
   }
   __syncthreads();
 
-  // ---- merge the waves (fp64) into this split's partial acc[kG][kD], l[kG], m[kG], or with
+  // ---- merge the waves (fp64) into this split's partial acc[G][kD], l[G], m[G], or with
   //      a single split straight into the output
   auto wres = [&](int w2) { return reinterpret_cast<const double*>(&s_ring[w2][0]); };
   const int64_t unit = (int64_t)b * a.H + h;
-  double* part_out = a.part + (unit * a.nsplit_max + s) * kPartDoubles;
-  __shared__ double s_f[kWaves][kG];
-  __shared__ double s_lsum[kG];
-  if (tid < kG * kWaves) {  // thread (head i, wave w2), in wave 0: lanes 8i..8i+7 hold head i
+  double* part_out = a.part + (unit * a.nsplit_max + s) * part_doubles(G);
+  __shared__ double s_f[kWaves][G];
+  __shared__ double s_lsum[G];
+  if (tid < G * kWaves) {  // thread (head i, wave w2), in wave 0: lanes 8i..8i+7 hold head i
     const int i = tid >> 3, w2 = tid & (kWaves - 1);
     double mm = -INFINITY;
 #pragma unroll
-    for (int w3 = 0; w3 < kWaves; ++w3) mm = fmax(mm, wres(w3)[kG * kD + i]);
-    const double mw = wres(w2)[kG * kD + i];
+    for (int w3 = 0; w3 < kWaves; ++w3) mm = fmax(mm, wres(w3)[G * kD + i]);
+    const double mw = wres(w2)[G * kD + i];
     const double f = mw == -INFINITY ? 0.0 : exp2((mw - mm) * c2);
     s_f[w2][i] = f;
-    double lsum = f * wres(w2)[kG * kD + kG + i];
+    double lsum = f * wres(w2)[G * kD + G + i];
     lsum += __shfl_xor(lsum, 1, 64);
     lsum += __shfl_xor(lsum, 2, 64);
     lsum += __shfl_xor(lsum, 4, 64);
     if (w2 == 0) {
       s_lsum[i] = lsum;
       if (!a.direct) {
-        part_out[kG * kD + i] = lsum;
-        part_out[kG * kD + kG + i] = mm;
+        part_out[G * kD + i] = lsum;
+        part_out[G * kD + G + i] = mm;
       }
     }
   }
   __syncthreads();
-  for (int e = tid; e < kG * kD; e += kThreads) {
+  for (int e = tid; e < G * kD; e += kThreads) {
     double sum = 0.0;
 #pragma unroll
     for (int w2 = 0; w2 < kWaves; ++w2) sum += s_f[w2][e / kD] * wres(w2)[e];
     if (a.direct) {
       const double lsum = s_lsum[e / kD];
-      a.out[((int64_t)b * a.H * kG + h * kG) * kD + e] = lsum > 0.0 ? (float)(sum / lsum) : 0.f;
+      a.out[((int64_t)b * a.H * G + h * G) * kD + e] = lsum > 0.0 ? (float)(sum / lsum) : 0.f;
     } else {
       part_out[e] = sum;
     }
@@ -925,7 +962,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
 // formed once, and every thread then reads its accumulator column with independent loads.
 constexpr int kMaxSplitsStaged = 256;
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void combine_k(AttnArgs a) {
+  constexpr int kPartDoubles = part_doubles(G);
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int32_t L = a.lens[b];
   const int32_t cap = min(a.maxp * kT, a.max_seq_len);
@@ -935,16 +974,16 @@ __global__ __launch_bounds__(kThreads) void combine_k(AttnArgs a) {
   const int64_t unit = (int64_t)b * a.H + h;
   const double* base = a.part + unit * a.nsplit_max * kPartDoubles;
   const double c2 = a.scale_log2e;
-  __shared__ double s_m[kMaxSplitsStaged][kG];
-  __shared__ double s_w[kMaxSplitsStaged][kG];
-  __shared__ double s_lsum[kG];
-  for (int e = tid; e < nsplit * kG; e += kThreads) {
-    const int x = e / kG, i = e % kG;
-    s_m[x][i] = base[x * kPartDoubles + kG * kD + kG + i];
-    s_w[x][i] = base[x * kPartDoubles + kG * kD + i];  // l, turned into weights below
+  __shared__ double s_m[kMaxSplitsStaged][G];
+  __shared__ double s_w[kMaxSplitsStaged][G];
+  __shared__ double s_lsum[G];
+  for (int e = tid; e < nsplit * G; e += kThreads) {
+    const int x = e / G, i = e % G;
+    s_m[x][i] = base[x * kPartDoubles + G * kD + G + i];
+    s_w[x][i] = base[x * kPartDoubles + G * kD + i];  // l, turned into weights below
   }
   __syncthreads();
-  if (tid < kG) {
+  if (tid < G) {
     const int i = tid;
     double mm = -INFINITY;
     for (int x = 0; x < nsplit; ++x) mm = fmax(mm, s_m[x][i]);
@@ -957,13 +996,13 @@ __global__ __launch_bounds__(kThreads) void combine_k(AttnArgs a) {
     s_lsum[i] = lsum;
   }
   __syncthreads();
-  for (int e = tid; e < kG * kD; e += kThreads) {
+  for (int e = tid; e < G * kD; e += kThreads) {
     const int i = e / kD, d = e % kD;
     double sum = 0.0;
 #pragma unroll 8
     for (int x = 0; x < nsplit; ++x) sum += s_w[x][i] * base[x * kPartDoubles + i * kD + d];
     const double lsum = s_lsum[i];
-    a.out[((int64_t)b * a.H * kG + h * kG + i) * kD + d] = lsum > 0.0 ? (float)(sum / lsum) : 0.f;
+    a.out[((int64_t)b * a.H * G + h * G + i) * kD + d] = lsum > 0.0 ? (float)(sum / lsum) : 0.f;
   }
 }
 
@@ -1002,9 +1041,9 @@ static Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len) {
   return Plan{pps, (maxpages + pps - 1) / pps};
 }
 
-size_t attention_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
+size_t attention_workspace_bytes(int32_t B, int32_t H, int32_t G, int32_t max_seq_len) {
   Plan pl = make_plan(B, H, max_seq_len);
-  size_t part = (size_t)B * H * pl.nsplit_max * kPartDoubles * sizeof(double);
+  size_t part = (size_t)B * H * pl.nsplit_max * part_doubles(G) * sizeof(double);
   size_t cnt = (size_t)B * H * sizeof(uint32_t);
   return 256 + ((cnt + 255) / 256) * 256 + part;
 }
@@ -1016,7 +1055,7 @@ static thread_local TimingEvents t_timing;
 
 void set_attention_timing(hipEvent_t start, hipEvent_t stop) { t_timing = TimingEvents{start, stop}; }
 
-template <class Loader>
+template <class Loader, int G>
 static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const zf_seqs* q,
                          const uint16_t* qv, float scale, float* out, void* ws, uint32_t* status,
                          hipStream_t st) {
@@ -1049,28 +1088,36 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   if (t_timing.start) {  // one-shot device timestamps of this kernel (profiling aid)
     const TimingEvents ev = t_timing;
     t_timing = TimingEvents{};
-    hipExtLaunchKernelGGL(attn_k<Loader>, grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0, a, ld);
+    hipExtLaunchKernelGGL((attn_k<Loader, G>), grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0, a, ld);
   } else {
-    hipLaunchKernelGGL(attn_k<Loader>, grid, dim3(kThreads), 0, st, a, ld);
+    hipLaunchKernelGGL((attn_k<Loader, G>), grid, dim3(kThreads), 0, st, a, ld);
   }
-  if (!a.direct) hipLaunchKernelGGL(combine_k, dim3(H, q->batch), dim3(kThreads), 0, st, a);
+  if (!a.direct) hipLaunchKernelGGL(combine_k<G>, dim3(H, q->batch), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
+template <class Loader>
+static hipError_t launch_g(const Loader& ld, int32_t num_pages, int32_t H, int32_t Hq,
+                           const zf_seqs* q, const uint16_t* qv, float scale, float* out, void* ws,
+                           uint32_t* status, hipStream_t st) {
+  if (Hq == 8 * H) return launch<Loader, 8>(ld, num_pages, H, q, qv, scale, out, ws, status, st);
+  return launch<Loader, 4>(ld, num_pages, H, q, qv, scale, out, ws, status, st);
+}
+
 hipError_t launch_attention_packed(const zf_cache* c, const zf_seqs* q, const uint16_t* qv,
-                                   float scale, float* out, void* ws, hipStream_t st) {
+                                   int32_t Hq, float scale, float* out, void* ws, hipStream_t st) {
   // the spill address of a compressed block is never used, but it must be readable
   const uint8_t* spill = c->spill_slots > 0 ? c->spill : c->sm;
   const uint32_t spill_bytes = (uint32_t)(c->spill_slots * 32);  // validated below 2^32
   PackedLoader ld{c->sm, c->nib, c->base, c->row_flags, c->row_spill, spill, spill_bytes};
-  return launch(ld, c->num_pages, c->num_kv_heads, q, qv, scale, out, ws, c->status, st);
+  return launch_g(ld, c->num_pages, c->num_kv_heads, Hq, q, qv, scale, out, ws, c->status, st);
 }
 
 hipError_t launch_attention_raw(const uint16_t* pages, int32_t num_pages, int32_t H,
-                                const zf_seqs* q, const uint16_t* qv, float scale, float* out,
-                                void* ws, uint32_t* status, hipStream_t st) {
+                                const zf_seqs* q, const uint16_t* qv, int32_t Hq, float scale,
+                                float* out, void* ws, uint32_t* status, hipStream_t st) {
   RawLoader ld{pages};
-  return launch(ld, num_pages, H, q, qv, scale, out, ws, status, st);
+  return launch_g(ld, num_pages, H, Hq, q, qv, scale, out, ws, status, st);
 }
 
 // ---------------------------------------------------------------- workspace fill

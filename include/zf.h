@@ -173,7 +173,9 @@ zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw
  * softmax(scale * q K^T) V over the sequence's tokens in logical order; zeros when
  * seq_lens[b] == 0.  Workspace: zf_attention_workspace_bytes(...) bytes of device memory, any
  * contents (it holds per-split partials); calls sharing one workspace must not overlap.
- * Requires D == 128, page_size == 16, num_q_heads == 4 * H, max_seq_len <= 2^20 and
+ * Requires D == 128, page_size == 16, num_q_heads == 4 * H or 8 * H (Llama-3.1-8B- and
+ * 70B-shaped groups; the 8-head kernel carries each weight as two bf16 parts, within 2^-16
+ * of it, where the 4-head one carries it exactly in three), max_seq_len <= 2^20 and
  * spill_slots < 2^27 (the pool is addressed with 32-bit byte offsets) in this
  * version (ZF_EUNSUPPORTED otherwise).  One kernel launch when max_seq_len fits one split per
  * (sequence, kv head), else two (split attention, split merge). */

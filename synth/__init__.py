@@ -90,7 +90,7 @@ class Workload:
                     self.pool_factor, self.seed)
 
 
-# The five workloads (sizes, value distributions and page-table structure).
+# The workloads (sizes, value distributions and page-table structure).
 WORKLOADS = {
     0: Workload("tiny_b1_ctx512", batch=1, ctx_min=512, ctx_max=512, seed=0),
     1: Workload("llama8b_b32_ctx4096", batch=32, ctx_min=4096, ctx_max=4096,
@@ -102,6 +102,10 @@ WORKLOADS = {
                 p_wide_block=0.05, pool_factor=1.25, seed=3),
     4: Workload("maxcap_b4_ctx131072", batch=4, ctx_min=131072, ctx_max=131072,
                 extra_tokens=64, seed=4),
+    # wider query groups: 64 query heads over 8 kv heads (a Llama-3.1-70B-shaped layer,
+    # whose bf16 weights fit one 288 GB GPU), otherwise the batch-32 decode above
+    5: Workload("gqa8_b32_ctx4096", batch=32, ctx_min=4096, ctx_max=4096, num_q_heads=64,
+                extra_tokens=1, seed=5),
 }
 
 

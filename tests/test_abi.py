@@ -147,13 +147,29 @@ def test_attention_shape_and_workspace_checks():
     # group of 3 query heads per kv head: unsupported
     assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s), 4096, 24, 0.1, 8192, 12288,
                                    1 << 20, None) == zf.ZF_EUNSUPPORTED
+    # 16 query heads per kv head: unsupported (4 and 8 are)
+    assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s), 4096, 128, 0.1, 8192, 12288,
+                                   1 << 20, None) == zf.ZF_EUNSUPPORTED
     # too small a workspace
     assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s), 4096, 32, 0.1, 8192, 12288,
+                                   16, None) == zf.ZF_EWORKSPACE
+    assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s), 4096, 64, 0.1, 8192, 12288,
                                    16, None) == zf.ZF_EWORKSPACE
     # empty batch: nothing to do
     s0 = zf.zf_seqs(0, 0, None, None, 0)
     assert lib.zf_decode_attention(ctypes.byref(c), ctypes.byref(s0), 4096, 32, 0.1, 8192, 12288,
                                    0, None) == zf.ZF_OK
+
+
+def test_attention_workspace_grows_with_the_query_group():
+    """Partials hold acc[G][128], l[G], m[G] doubles per split: 8 query heads per kv head need
+    twice the 4-head partial area (the counter header is the same)."""
+    B, H, L = 2, 8, 200000  # long enough to split
+    w4 = zf.zf_attention_workspace_bytes(B, H, 4 * H, 128, L)
+    w8 = zf.zf_attention_workspace_bytes(B, H, 8 * H, 128, L)
+    head = 256 + 256  # 256-byte header, B * H counters rounded to 256
+    assert w4 > head and w8 - head == 2 * (w4 - head)
+    assert zf.zf_attention_workspace_bytes(B, H, 16 * H, 128, L) == 0
 
 
 def test_status_strings():

@@ -39,8 +39,14 @@ SMALL = synth.WORKLOADS[0].replace(name="ragged_small", batch=5, ctx_min=1, ctx_
                                    extra_tokens=3, pool_factor=1.3, p_wide_block=0.05, seed=21)
 
 
+# 8 query heads per kv head (64 / 8): a ragged small batch, and long sequences that split
+SMALL8 = SMALL.replace(name="ragged_small_gqa8", num_q_heads=64, seed=22)
+SPLIT8 = synth.WORKLOADS[2].replace(name="long_b3_ctx24000_gqa8", batch=3, ctx_min=24000,
+                                    ctx_max=24000, num_q_heads=64, seed=23)
+
+
 def workload(key):
-    return SMALL if key == "small" else synth.WORKLOADS[key]
+    return {"small": SMALL, "small8": SMALL8, "split8": SPLIT8}.get(key) or synth.WORKLOADS[key]
 
 
 def put_tokens(inst, lens, k, v):
@@ -94,7 +100,7 @@ def sample_want(rng, B, Hq, n):
     return want
 
 
-@pytest.mark.parametrize("key", [0, "small", 1, 2])
+@pytest.mark.parametrize("key", [0, "small", 1, 2, "small8", 5, "split8"])
 def test_attention_full(key):
     w = workload(key)
     log(f"attention parity (all heads): workload {w.name}")
