@@ -426,24 +426,12 @@ __device__ __forceinline__ void pair_d(double v, double& a, double& b) {
   a = __longlong_as_double((int64_t)(((uint64_t)h[0] << 32) | l[0]));
   b = __longlong_as_double((int64_t)(((uint64_t)h[1] << 32) | l[1]));
 }
-// Maxima as single instructions.  fmax / fmaxf first quiet a possible signalling NaN in each
-// operand with an extra max; every operand here is the result of arithmetic or a copy of one,
-// never a signalling NaN, so the plain instruction gives the same result.
-__device__ __forceinline__ float max_f32(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float max3_f32(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ double max_f64(double a, double b) {
-  double r;
-  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+// Maxima in plain C, never inline asm: the scores come straight out of the matrix cores, and
+// a VALU read of an MFMA result needs wait states that the compiler inserts only for the
+// instructions it can see (an asm max read them stale on full pages under some schedules).
+__device__ __forceinline__ float max_f32(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float max3_f32(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ double max_f64(double a, double b) { return fmax(a, b); }
 // max / sum over the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48) of a double
 __device__ __forceinline__ double rows_max_d(double v) {
   double a, b;
