@@ -32,7 +32,6 @@
 // loaders hand the same bf16 pairs to the same arithmetic, so the outputs match bit for bit.
 #include <algorithm>
 #include <hip/hip_ext.h>
-#include <stdlib.h>
 
 #include "zf_internal.h"
 
@@ -1000,28 +999,15 @@ struct Plan {
   int pps, nsplit_max;
 };
 
-static int env_pps() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("ZF_PAGES_PER_SPLIT");
-    v = e ? atoi(e) : 0;
-    if (v < 0) v = 0;
-  }
-  return v;
-}
-
 // Pages per split: about one workgroup per CU (256), at least one page per wave, at most 64
 // per wave, and splits of one sequence as equal as the multiple of kWaves allows.
 static Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len) {
   const int maxpages = std::max(1, (max_seq_len + kT - 1) / kT);
-  int pps = env_pps();
-  if (pps == 0) {
-    const int64_t units = std::max<int64_t>((int64_t)B * H, 1);
-    int64_t splits = std::max<int64_t>(1, (256 + units - 1) / units);
-    splits = std::min<int64_t>(splits, (maxpages + kWaves - 1) / kWaves);
-    splits = std::max<int64_t>(splits, 1);
-    pps = (int)((maxpages + splits - 1) / splits);
-  }
+  const int64_t units = std::max<int64_t>((int64_t)B * H, 1);
+  int64_t splits = std::max<int64_t>(1, (256 + units - 1) / units);
+  splits = std::min<int64_t>(splits, (maxpages + kWaves - 1) / kWaves);
+  splits = std::max<int64_t>(splits, 1);
+  int pps = (int)((maxpages + splits - 1) / splits);
   pps = (pps + kWaves - 1) / kWaves * kWaves;
   pps = std::min(std::max(pps, kWaves), kMaxPagesPerSplit);
   if ((maxpages + pps - 1) / pps > kMaxSplitsStaged)  // very long sequences: fewer, longer splits
@@ -1029,11 +1015,10 @@ static Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len) {
   return Plan{pps, (maxpages + pps - 1) / pps};
 }
 
+// Workspace: a 256-byte header (unused, keeps the partials aligned), then the split partials.
 size_t attention_workspace_bytes(int32_t B, int32_t H, int32_t G, int32_t max_seq_len) {
   Plan pl = make_plan(B, H, max_seq_len);
-  size_t part = (size_t)B * H * pl.nsplit_max * part_doubles(G) * sizeof(double);
-  size_t cnt = (size_t)B * H * sizeof(uint32_t);
-  return 256 + ((cnt + 255) / 256) * 256 + part;
+  return 256 + (size_t)B * H * pl.nsplit_max * part_doubles(G) * sizeof(double);
 }
 
 struct TimingEvents {
@@ -1065,8 +1050,7 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   a.q = qv;
   a.scale_log2e = (double)scale * kLog2e;
   a.out = out;
-  size_t cnt = (size_t)q->batch * H * sizeof(uint32_t);
-  a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + 256 + ((cnt + 255) / 256) * 256);
+  a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + 256);
   a.status = status;
   // groups (sequence, split) rounded up to a multiple of the XCD count, times the kv heads
   const uint32_t groups = (uint32_t)pl.nsplit_max * (uint32_t)q->batch;

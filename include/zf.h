@@ -25,8 +25,9 @@
  * word, and 32 spill bytes holding e >> 4 of each value (packed like the nibbles).
  * Rebuild: x = (s << 15 | nibble << 7 | m) + (base << 7)   or   + ((e >> 4) << 11) when raw.
  * Spill slots: a row's raw blocks occupy consecutive slots in block order starting at
- * row_spill[row]; zf_encode_kv takes slots for rows in (sequence, token) order, zf_append_kv
- * in batch order, both starting at *spill_top, which they advance.  Slots are never freed.
+ * row_spill[row]; zf_encode_kv and zf_append_kv_n take slots for rows in (sequence, token)
+ * order, zf_append_kv in batch order, all starting at *spill_top, which they advance.  Only
+ * zf_compact_spill gives slots back: it rewrites the pool for the sequences still live.
  *
  * Arrays (device memory, 256-byte aligned, caller-owned; the library allocates nothing):
  *   sm        u8 [num_pages][H][2][page_size][D]

@@ -167,7 +167,7 @@ def test_attention_workspace_grows_with_the_query_group():
     B, H, L = 2, 8, 200000  # long enough to split
     w4 = zf.zf_attention_workspace_bytes(B, H, 4 * H, 128, L)
     w8 = zf.zf_attention_workspace_bytes(B, H, 8 * H, 128, L)
-    head = 256 + 256  # 256-byte header, B * H counters rounded to 256
+    head = 256  # 256-byte header
     assert w4 > head and w8 - head == 2 * (w4 - head)
     assert zf.zf_attention_workspace_bytes(B, H, 16 * H, 128, L) == 0
 
