@@ -45,8 +45,17 @@ SPLIT8 = synth.WORKLOADS[2].replace(name="long_b3_ctx24000_gqa8", batch=3, ctx_m
                                     ctx_max=24000, num_q_heads=64, seed=23)
 
 
+# 4 kv heads with 16 query heads, 2 kv heads with 16 query heads (8 per kv head), and a batch
+# of 300 short sequences (more workgroups than CUs, beyond the largest-first ordering's batch)
+SMALL_H4 = SMALL.replace(name="ragged_small_h4", num_kv_heads=4, num_q_heads=16, seed=25)
+SMALL_H2G8 = SMALL.replace(name="ragged_small_h2_gqa8", num_kv_heads=2, num_q_heads=16, seed=26)
+WIDE_B300 = SMALL.replace(name="ragged_b300_ctx1_120", batch=300, ctx_min=1, ctx_max=120, seed=27)
+
+
 def workload(key):
-    return {"small": SMALL, "small8": SMALL8, "split8": SPLIT8}.get(key) or synth.WORKLOADS[key]
+    named = {"small": SMALL, "small8": SMALL8, "split8": SPLIT8, "h4": SMALL_H4, "h2g8": SMALL_H2G8,
+             "b300": WIDE_B300}
+    return named.get(key) or synth.WORKLOADS[key]
 
 
 def put_tokens(inst, lens, k, v):
@@ -100,7 +109,7 @@ def sample_want(rng, B, Hq, n):
     return want
 
 
-@pytest.mark.parametrize("key", [0, "small", 1, 2, "small8", 5, "split8"])
+@pytest.mark.parametrize("key", [0, "small", 1, 2, "small8", 5, "split8", "h4", "h2g8", "b300"])
 def test_attention_full(key):
     w = workload(key)
     log(f"attention parity (all heads): workload {w.name}")

@@ -164,6 +164,30 @@ def test_append_n_spill_exhaustion_changes_no_defined_state():
         assert np.array_equal(a[m], b[m]), n
 
 
+# other geometries of the format: head_dim 64 (16 blocks per row), head_dim 256 with 4 kv heads
+# (32 blocks per row, every flag bit), 2 kv heads
+GEOMS = [SMALL.replace(name="small_d64", head_dim=64, seed=51),
+         SMALL.replace(name="small_d256_h4", head_dim=256, num_kv_heads=4, num_q_heads=16, seed=52),
+         SMALL.replace(name="small_h2", num_kv_heads=2, num_q_heads=16, seed=53)]
+
+
+@pytest.mark.parametrize("w", GEOMS, ids=lambda w: w.name)
+def test_other_geometries_encode_append_decode(w):
+    log(f"codec parity: workload {w.name} (H {w.num_kv_heads}, D {w.head_dim})")
+    s, inst, lens = _append_steps(w, 3)
+    out = torch.zeros_like(s.raw)
+    zf.zf_decode_kv(s.cache, s.seqs, out)
+    torch.cuda.synchronize()
+    assert s.status() == 0
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    st, want = orc.decode(inst.seq_lens, inst.page_table)
+    assert st == oracle.OK
+    rows = valid_rows(inst)
+    got = host(out, np.uint16)
+    m = np.broadcast_to(rows[:, None, None, :, None], got.shape)
+    assert np.array_equal(got[m], want[m])
+
+
 def test_encode_spill_exhaustion_keeps_pool():
     inst = synth.make(SMALL)
     orc = oracle_cache(inst, 1 << 20)
