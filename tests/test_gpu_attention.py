@@ -247,6 +247,19 @@ def test_bad_page_sets_status():
     assert s.status() & zf.ZF_DEV_EPAGE
 
 
+def test_bad_length_sets_status_and_stays_in_bounds():
+    """A length beyond the page-table row (or the host bound) is reported with ZF_DEV_ELEN; the
+    kernel clamps it and reads no page outside the row."""
+    inst = synth.make(SMALL)
+    s = Setup(inst)
+    lens = inst.seq_lens.copy()
+    lens[2] = s.seqs.max_seq_len + 7
+    s.seqs.seq_lens.copy_(dev(lens))
+    out = s.attention(synth.query(SMALL, 0))
+    assert s.status() & zf.ZF_DEV_ELEN
+    assert torch.isfinite(out).all()
+
+
 def test_host_argument_errors_raise():
     inst = synth.make(SMALL)
     s = Setup(inst)
