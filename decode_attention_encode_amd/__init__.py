@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import dataclasses
 import os
+from typing import Optional
 
 import torch  # loads the HIP runtime the library binds to
 
@@ -17,13 +18,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzf.so")
 
 ZF_OK, ZF_EINVAL, ZF_EUNSUPPORTED, ZF_EHIP, ZF_EWORKSPACE = 0, 1, 2, 3, 4
-ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN = 1, 2, 4
+ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN, ZF_DEV_ESYNC = 1, 2, 4, 8
+ZF_APPEND_SYNC_WORDS = 65  # hand-over words of the one-launch append (64) and its epoch
 
 EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_append_kv",
            "zf_append_kv_n", "zf_compact_spill", "zf_compact_workspace_bytes", "zf_max_sequences",
            "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_raw",
            "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
-           "zf_stream_read_probe", "zf_get_status", "zf_status_str")
+           "zf_stream_read_probe", "zf_set_append_wait_polls", "zf_get_status", "zf_status_str")
 ZF_PROBE_BLOCKS = 4096
 
 
@@ -37,7 +39,8 @@ class zf_cache(ctypes.Structure):
                 ("sm", ctypes.c_void_p), ("nib", ctypes.c_void_p), ("base", ctypes.c_void_p),
                 ("row_flags", ctypes.c_void_p), ("row_spill", ctypes.c_void_p),
                 ("spill", ctypes.c_void_p), ("spill_slots", ctypes.c_uint64),
-                ("spill_top", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("spill_top", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("append_sync", ctypes.c_void_p)]
 
 
 class zf_seqs(ctypes.Structure):
@@ -80,6 +83,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "zf_attention_workspace_init": (ctypes.c_int, [vp, sz, vp]),
         "zf_time_next_attention": (ctypes.c_int, [vp, vp]),
         "zf_stream_read_probe": (ctypes.c_int, [vp, sz, vp, vp]),
+        "zf_set_append_wait_polls": (None, [ctypes.c_uint32]),
         "zf_get_status": (ctypes.c_int, [vp, vp, vp]),
         "zf_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -125,9 +129,11 @@ class PackedCache:
     spill: torch.Tensor
     spill_top: torch.Tensor
     status: torch.Tensor
+    append_sync: Optional[torch.Tensor] = None  # int64 [65]; None: appends take two launches
 
     @classmethod
-    def empty(cls, num_pages, page_size, num_kv_heads, head_dim, spill_slots, device="cuda"):
+    def empty(cls, num_pages, page_size, num_kv_heads, head_dim, spill_slots, device="cuda",
+              one_launch_append=True):
         P, T, H, D = num_pages, page_size, num_kv_heads, head_dim
         u8 = dict(dtype=torch.uint8, device=device)
         i32 = dict(dtype=torch.int32, device=device)
@@ -139,13 +145,15 @@ class PackedCache:
                    row_spill=torch.zeros((P, T), **i32),
                    spill=torch.zeros((max(spill_slots, 1), 32), **u8),
                    spill_top=torch.zeros(1, dtype=torch.int64, device=device),
-                   status=torch.zeros(1, **i32))
+                   status=torch.zeros(1, **i32),
+                   append_sync=(torch.zeros(ZF_APPEND_SYNC_WORDS, dtype=torch.int64, device=device)
+                                if one_launch_append else None))
 
     def c(self) -> zf_cache:
         return zf_cache(self.num_pages, self.page_size, self.num_kv_heads, self.head_dim,
                         _ptr(self.sm), _ptr(self.nib), _ptr(self.base), _ptr(self.row_flags),
                         _ptr(self.row_spill), _ptr(self.spill), self.spill_slots,
-                        _ptr(self.spill_top), _ptr(self.status))
+                        _ptr(self.spill_top), _ptr(self.status), _ptr(self.append_sync))
 
 
 @dataclasses.dataclass
@@ -259,6 +267,10 @@ def zf_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> 
     ZF_PROBE_BLOCKS u32 checksums afterwards."""
     _check(load().zf_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                        _stream(stream)), "zf_stream_read_probe")
+
+
+def zf_set_append_wait_polls(polls: int) -> None:
+    load().zf_set_append_wait_polls(int(polls))
 
 
 def zf_get_status(status: torch.Tensor, stream=None) -> int:

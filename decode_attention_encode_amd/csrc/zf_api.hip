@@ -9,6 +9,7 @@ hipError_t launch_encode(const Geom&, const zf_cache*, const zf_seqs*, const uin
                          hipStream_t);
 size_t encode_workspace_bytes(const zf_seqs*);
 int append_max_rows();
+void set_append_wait_polls(uint32_t);
 hipError_t launch_append(const Geom&, const zf_cache*, const zf_seqs*, int32_t, const uint16_t*,
                          const uint16_t*, hipStream_t);
 hipError_t launch_decode(const Geom&, const zf_cache*, const zf_seqs*, uint16_t*, hipStream_t);
@@ -47,6 +48,7 @@ zf_status check_cache(const zf_cache* c) {
       !aligned(c->row_spill) || !c->spill_top || !c->status)
     return ZF_EINVAL;
   if (c->spill_slots > 0 && !aligned(c->spill)) return ZF_EINVAL;
+  if (reinterpret_cast<uintptr_t>(c->append_sync) & 7u) return ZF_EINVAL;
   if (c->spill_slots >= ((uint64_t)1 << 32)) return ZF_EUNSUPPORTED;  // row_spill is 32-bit
   return ZF_OK;
 }
@@ -125,6 +127,8 @@ zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_n
   return hip_status(zf::launch_append(geom_of(cache), cache, seqs, n_new, k_new, v_new,
                                       static_cast<hipStream_t>(stream)));
 }
+
+void zf_set_append_wait_polls(uint32_t polls) { zf::set_append_wait_polls(polls); }
 
 zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
                        const uint16_t* v_new, zf_stream_t stream) {

@@ -256,22 +256,35 @@ __global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint
 
 // ------------------------------------------------------------------------------ append
 
-// Append of n tokens per sequence runs as two kernels; new row r = b * n + j is token j of
-// sequence b, at position seq_lens[b] + j.  append_pack_k: one workgroup per new row
-// classifies its 32 blocks and writes their sm/nib/base bytes and the row's flag word into the
-// row's slot, which is not yet part of the sequence.  append_commit_k: one workgroup validates
-// every row, scans the rows' raw counts in row order ((sequence, token) order), and only if all
-// of them fit in the spill pool writes the spill slots and row_spill and advances seq_lens and
-// spill_top.  So a failed append changes no defined state: only slots at positions seq_lens[b]
-// and later may be touched.
+// Append of n tokens per sequence; new row r = b * n + j is token j of sequence b, at position
+// seq_lens[b] + j.  Packing: one workgroup per new row classifies its blocks and writes their
+// sm/nib/base bytes and the row's flag word into the row's slot, which is not yet part of the
+// sequence.  Commit: one workgroup validates every row, scans the rows' raw counts in row order
+// ((sequence, token) order), and only if all of them fit in the spill pool writes the spill
+// slots and row_spill and advances seq_lens and spill_top.  So a failed append changes no
+// defined state: only slots at positions seq_lens[b] and later may be touched.
+//
+// Two forms.  Two launches: append_pack_k, then append_commit_k, which reads the flag words
+// back from row_flags.  One launch (append_one_k, when the cache has sync words and there are
+// at most 64 new rows): R packing workgroups and one commit workgroup.  Each packing workgroup
+// publishes one 64-bit word, its row's flag word and error bits tagged with the call's epoch
+// (a counter in the sync area), stored only after its loads of the epoch, its length and
+// spill_top have returned.  Every workgroup then waits until all R words carry the tag and
+// takes the same all-or-nothing decision from them; a packing workgroup also gets its row's
+// first spill slot (spill_top plus the raw blocks of the rows before it) and writes its own
+// spill slots and row_spill, and the commit advances seq_lens and spill_top (every length was
+// read before its word was stored) and then the epoch.  Each word carries its data itself, so
+// no fence orders it after other stores.
 constexpr int kAppendThreads = 1024;
 constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS
+constexpr int kOneMaxRows = 64;       // new rows of a one-launch append (sync words 0 .. 63; 64: epoch)
+constexpr uint32_t kSyncPolls = 1u << 16;  // bound on each wait for the words (about 0.1 s)
+constexpr uint64_t kTagMod = (1u << 29) - 1u;
 
-// Row of new token j of sequence b (n per sequence), or -1 (with the error bit) when the
-// sequence cannot take them.
-__device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, int b, int j, int n,
-                                              uint32_t* err) {
-  const int32_t L = s.lens[b];
+// Row of new token j of sequence b (n per sequence) whose length was read as L, or -1 (with the
+// error bit) when the sequence cannot take them.
+__device__ __forceinline__ int64_t append_row_at(const Geom& g, const SeqView& s, int b, int j, int n,
+                                                 int32_t L, uint32_t* err) {
   if (L < 0 || (int64_t)L + n > (int64_t)s.maxp * g.T || (int64_t)L + n > s.max_seq_len) {
     *err = ZF_DEV_ELEN;
     return -1;
@@ -286,44 +299,76 @@ __device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, i
   return (int64_t)pid * g.T + t % g.T;
 }
 
+__device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, int b, int j, int n,
+                                              uint32_t* err) {
+  return append_row_at(g, s, b, j, n, s.lens[b], err);
+}
+
+// Block j of a new row, classified and packed in registers (8 lanes, 8 values each).
+struct NewBlock {
+  uint32_t sm0, sm1, nib, hi, bexp, raw;
+};
+
+// New row r is u16 [H][D] of K and of V; block j covers half j % nb of head j / nb / 2, K or V
+// by (j / nb) & 1, the order of the row's flag bits.
+__device__ __forceinline__ NewBlock classify_new(const Geom& g, int r, int j, int lane8,
+                                                 const uint16_t* __restrict__ k_new,
+                                                 const uint16_t* __restrict__ v_new) {
+  const int nb = g.nb(), half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
+  const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)r * g.H + h) * g.D +
+                                                   half * kBlock + lane8 * 8);
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+  Window win = window8(w);
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
+    win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
+    win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
+  }
+  NewBlock o;
+  o.raw = win.special | (uint32_t)(win.emax - win.emin > 15u);
+  o.bexp = o.raw ? 0u : win.emin;
+  uint32_t smw[2];
+  pack8(w, o.bexp, o.raw, smw, o.nib, o.hi);
+  o.sm0 = smw[0];
+  o.sm1 = smw[1];
+  return o;
+}
+
+__device__ __forceinline__ void store_new(const Geom& g, int64_t row, int j, int lane8, const NewBlock& o,
+                                          uint8_t* sm, uint8_t* nib, uint8_t* base) {
+  const int nb = g.nb(), half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
+  const int64_t pid = row / g.T, slot = row % g.T;
+  const int64_t v0 = ((pid * g.H + h) * 2 + kv) * g.T * g.D + slot * g.D + half * kBlock + lane8 * 8;
+  *reinterpret_cast<uint2*>(sm + v0) = make_uint2(o.sm0, o.sm1);
+  *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = o.nib;
+  if (lane8 == 0) base[v0 / kBlock] = (uint8_t)o.bexp;
+}
+
+// The row's flag word (bit j = block j raw) from the blocks the workgroup classified (block j on
+// threads 8j .. 8j + 7; the row has at most 32 blocks).  Every thread gets it.
+__device__ __forceinline__ uint32_t row_flag_word(bool has, int j, int lane8, uint32_t raw) {
+  __shared__ uint32_t s_f;
+  if (threadIdx.x == 0) s_f = 0u;
+  __syncthreads();
+  if (has && lane8 == 0 && raw) atomicOr(&s_f, 1u << j);
+  __syncthreads();
+  return s_f;
+}
+
 __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, uint8_t* sm,
                                                      uint8_t* nib, uint8_t* base, uint32_t* row_flags) {
-  const int r = blockIdx.x, b = r / n, tid = threadIdx.x, lane8 = tid & 7;
+  const int r = blockIdx.x, b = r / n, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
   uint32_t err;
   const int64_t row = append_row(g, s, b, r - b * n, n, &err);
   if (row < 0) return;  // reported by append_commit_k
-  const int64_t pid = row / g.T, slot = row % g.T;
-  __shared__ uint32_t s_f;
-  if (tid == 0) s_f = 0u;
-  __syncthreads();
-  const int nb = g.nb(), D = g.D, H = g.H, rb = 2 * H * nb;
-  for (int j = tid >> 3; j < rb; j += blockDim.x >> 3) {
-    const int half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
-    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)r * H + h) * D +
-                                                     half * kBlock + lane8 * 8);
-    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    Window win = window8(w);
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
-      win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
-      win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
-    }
-    const uint32_t raw_blk = win.special | (uint32_t)(win.emax - win.emin > 15u);
-    const uint32_t bexp = raw_blk ? 0u : win.emin;
-    uint32_t smw[2], nibw, hiw;
-    pack8(w, bexp, raw_blk, smw, nibw, hiw);
-    const int64_t v0 = ((pid * H + h) * 2 + kv) * g.T * D + slot * D + half * kBlock + lane8 * 8;
-    *reinterpret_cast<uint2*>(sm + v0) = make_uint2(smw[0], smw[1]);
-    *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = nibw;
-    if (lane8 == 0) {
-      base[v0 / kBlock] = (uint8_t)bexp;
-      if (raw_blk) atomicOr(&s_f, 1u << j);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) row_flags[row] = s_f;
+  const bool has = j < g.blocks_per_row();
+  NewBlock o{};
+  if (has) o = classify_new(g, r, j, lane8, k_new, v_new);
+  const uint32_t f = row_flag_word(has, j, lane8, o.raw);
+  if (has) store_new(g, row, j, lane8, o, sm, nib, base);
+  if (tid == 0) row_flags[row] = f;
 }
 
 __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqView s, int n,
@@ -401,6 +446,121 @@ __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqVie
   __syncthreads();  // every length has been read before any is advanced
   for (int b = tid; b < s.B; b += kAppendThreads) s.lens[b] += n;
   if (tid == 0) *spill_top = top + total;
+}
+
+// Tag of a hand-over word published under epoch E: never 0, and different for consecutive
+// epochs (a word left by the previous call never matches).
+__device__ __forceinline__ uint32_t sync_tag(uint64_t E) { return (uint32_t)(E % kTagMod) + 1u; }
+
+// Hand-over word of one new row: tag << 35 | error bits << 32 | flag word.
+__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 35); }
+
+// What every workgroup learns from the R hand-over words (wave 0 polls them, lane i word i).
+struct HandOver {
+  uint32_t seen, err, total, pref;  // pref: raw blocks of the rows before row `me`
+};
+
+__device__ __forceinline__ HandOver read_hand_over(const uint64_t* sync, int R, int me, uint32_t tag,
+                                                   uint32_t polls) {
+  __shared__ HandOver s_h;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    uint64_t w = 0u;
+    bool ok = tid >= R;
+    for (uint32_t p = 0; !ok && p < polls; ++p) {
+      w = __hip_atomic_load(&sync[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = word_tag(w) == tag;
+      if (!ok) __builtin_amdgcn_s_sleep(2);
+    }
+    const uint32_t cnt = tid < R ? __popc((uint32_t)w) : 0u;
+    uint32_t incl = cnt, err = tid < R ? (uint32_t)(w >> 32) & 7u : 0u, miss = ok ? 0u : 1u;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t up = __shfl_up((int)incl, o, 64);
+      if (tid >= o) incl += up;
+      err |= (uint32_t)__shfl_xor((int)err, o, 64);
+      miss |= (uint32_t)__shfl_xor((int)miss, o, 64);
+    }
+    if (tid == me) s_h.pref = incl - cnt;
+    if (tid == 63) {
+      s_h.total = incl;
+      s_h.err = err;
+      s_h.seen = miss == 0u;
+    }
+  }
+  __syncthreads();
+  return s_h;
+}
+
+// Commit workgroup of the one-launch append: once every row's word carries this call's tag, it
+// advances seq_lens and spill_top, clears the words of unused rows and moves to the next epoch.
+__device__ void commit_one(const SeqView& s, int n, uint64_t* spill_top, uint64_t spill_slots,
+                           uint32_t* status, uint64_t* sync, uint32_t polls) {
+  const int R = s.B * n, tid = threadIdx.x;
+  const uint64_t E = sync[kOneMaxRows];  // written only by an earlier launch: a plain load
+  const uint64_t top = *spill_top;
+  const int32_t L = tid < s.B ? s.lens[tid] : 0;
+  const HandOver h = read_hand_over(sync, R, -1, sync_tag(E), polls);
+  if (!h.seen) {  // some row's word never came: change nothing, keep the epoch
+    if (tid == 0) set_status(status, ZF_DEV_ESYNC);
+    return;
+  }
+  const bool fits = (uint64_t)h.total <= spill_slots - top;
+  if (tid == 0) set_status(status, h.err ? h.err : (fits ? 0u : ZF_DEV_ESPILL));
+  if (!h.err && fits) {
+    if (tid < s.B) s.lens[tid] = L + n;  // every packing workgroup read its length before its word
+    if (tid == 0) *spill_top = top + h.total;
+  }
+  if (tid >= R && tid < kOneMaxRows)
+    __hip_atomic_store(&sync[tid], (uint64_t)0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&sync[kOneMaxRows], E + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One-launch append: workgroups 0 .. R-1 pack new row blockIdx.x, workgroup R commits.
+__global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new,
+                                                    const uint16_t* __restrict__ v_new, uint8_t* sm,
+                                                    uint8_t* nib, uint8_t* base, uint32_t* row_flags,
+                                                    uint32_t* row_spill, uint8_t* spill, uint64_t* spill_top,
+                                                    uint64_t spill_slots, uint32_t* status, uint64_t* sync,
+                                                    uint32_t polls) {
+  const int R = s.B * n, r = blockIdx.x, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
+  if (r == R) {
+    commit_one(s, n, spill_top, spill_slots, status, sync, polls);
+    return;
+  }
+  const uint64_t E = sync[kOneMaxRows];
+  const uint64_t top = *spill_top;
+  const int b = r / n;
+  uint32_t err;
+  const int64_t row = append_row(g, s, b, r - b * n, n, &err);
+  const bool has = j < g.blocks_per_row();
+  NewBlock o{};
+  if (has) o = classify_new(g, r, j, lane8, k_new, v_new);
+  const uint32_t f = row_flag_word(has, j, lane8, o.raw);
+  if (tid == 0) {
+    // the word is built from the epoch, the length (through err and row) and spill_top as
+    // loaded, so it cannot be stored before those loads have returned
+    uint32_t hi = (sync_tag(E) << 3) | err;
+    asm volatile("" : "+v"(hi) : "v"((uint32_t)row), "v"((uint32_t)top));
+    __hip_atomic_store(&sync[r], ((uint64_t)hi << 32) | f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (row >= 0) {
+    if (has) store_new(g, row, j, lane8, o, sm, nib, base);
+    if (tid == 0) row_flags[row] = f;
+  }
+  const HandOver h = read_hand_over(sync, R, r, sync_tag(E), kSyncPolls);
+  if (!h.seen) {
+    if (tid == 0) set_status(status, ZF_DEV_ESYNC);
+    return;
+  }
+  // the commit takes the same decision from the same words
+  if (h.err || (uint64_t)h.total > spill_slots - top) return;
+  const uint64_t first = top + h.pref;
+  if (has && o.raw) {
+    const uint64_t slot = first + __popc(f & ((1u << j) - 1u));
+    *reinterpret_cast<uint32_t*>(spill + slot * 32u + lane8 * 4) = o.hi;
+  }
+  if (tid == 0) row_spill[row] = (uint32_t)first;
 }
 
 // ------------------------------------------------------------------------------ decode
@@ -598,10 +758,20 @@ size_t encode_lds_bytes(int32_t batch) {
 
 int append_max_rows() { return kAppendMaxRows; }
 
+static uint32_t g_append_wait_polls = kSyncPolls;
+
+void set_append_wait_polls(uint32_t polls) { g_append_wait_polls = polls; }
+
 hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int32_t n, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t st) {
   SeqView s = view(q);
   const int rows = q->batch * n;
+  if (c->append_sync && rows <= kOneMaxRows) {
+    hipLaunchKernelGGL(append_one_k, dim3(rows + 1), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
+                       c->base, c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status,
+                       c->append_sync, g_append_wait_polls);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(append_pack_k, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
                      c->base, c->row_flags);
   size_t lds = 2 * (size_t)rows * sizeof(uint32_t);

@@ -37,6 +37,7 @@
  *   row_spill u32[num_pages][page_size]              slot of the row's first raw block
  *   spill     u8 [spill_slots][32]
  *   spill_top u64 (one counter)   status u32 (sticky device error bits, ZF_DEV_*)
+ *   append_sync u64[65] (optional; the one-launch append's hand-over words and epoch)
  * Raw (uncompressed) pages use u16[num_pages][H][2][page_size][D], the same page ids.
  *
  * ---------------------------------------------------------------------------------- errors
@@ -71,6 +72,10 @@ typedef enum {
 #define ZF_DEV_ESPILL 1u  /* spill pool exhausted: the call wrote no spill, kept spill_top */
 #define ZF_DEV_EPAGE 2u   /* a page-table entry the call needed is out of range           */
 #define ZF_DEV_ELEN 4u    /* a length is negative or beyond the page table / host bound   */
+#define ZF_DEV_ESYNC 8u   /* one-launch append: a hand-over word did not arrive within the
+                             bounded wait (about 0.1 s; none is expected): zero the sync
+                             area before the next append.  Set by the commit, the call left
+                             seq_lens and spill_top as they were */
 
 typedef struct {
   int32_t num_pages, page_size, num_kv_heads, head_dim;
@@ -83,7 +88,11 @@ typedef struct {
   uint64_t spill_slots;
   uint64_t* spill_top;
   uint32_t* status;
+  uint64_t* append_sync; /* device u64[ZF_APPEND_SYNC_WORDS], zero when the cache is set
+                            up, or NULL: see zf_append_kv_n */
 } zf_cache;
+
+#define ZF_APPEND_SYNC_WORDS 65
 
 typedef struct {
   int32_t batch, max_pages_per_seq;
@@ -113,7 +122,7 @@ size_t zf_encode_workspace_bytes(const zf_seqs* seqs);
  * (ZF_DEV_*) seq_lens, spill_top, the spill pool and every row t < seq_lens[b] are left as
  * they were; only the slots at position seq_lens[b], which are not yet part of any sequence,
  * may have been overwritten.  seqs->max_seq_len bounds the lengths after the append.
- * Supports batch <= 4096.  Two kernel launches (those of zf_append_kv_n with n_new = 1). */
+ * Supports batch <= 4096.  Launches as zf_append_kv_n with n_new = 1. */
 zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
                        const uint16_t* v_new, zf_stream_t stream);
 
@@ -123,7 +132,13 @@ zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_
  * b.  All or nothing, as zf_append_kv (only slots at positions seq_lens[b] and later may have
  * been overwritten after a device error); seqs->max_seq_len bounds the grown lengths.
  * n_new == 0 does nothing; n_new < 0 is ZF_EINVAL.  Supports batch * n_new <= 4096 (callers
- * split longer chunks).  Two kernel launches.  zf_append_kv is the case n_new == 1. */
+ * split longer chunks).  zf_append_kv is the case n_new == 1.
+ * Launches: one when cache->append_sync is set and batch * n_new <= 64, else two.  In the
+ * one-launch form the new rows' workgroups hand their flag words to each other through
+ * append_sync, words tagged with an epoch that append_sync[64] counts; the area is zero when
+ * the cache is set up, holds the last call's words between calls (only these calls may write
+ * it), and appends sharing it must not overlap (appends to one cache are ordered anyway: they
+ * advance one spill_top).  Both forms write the same bytes. */
 zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_new,
                          const uint16_t* k_new, const uint16_t* v_new, zf_stream_t stream);
 
@@ -214,6 +229,11 @@ zf_status zf_time_next_attention(void* start_event, void* stop_event);
  * 16-byte aligned, else ZF_EINVAL.  One kernel launch. */
 #define ZF_PROBE_BLOCKS 4096
 zf_status zf_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, zf_stream_t stream);
+
+/* Bound on the one-launch append's wait for the new rows' flag words, in polls (default
+ * 65536, about 0.1 s), for appends enqueued after the call; process-wide.  0 makes every
+ * one-launch append end with ZF_DEV_ESYNC, which lets tests take that path. */
+void zf_set_append_wait_polls(uint32_t polls);
 
 /* Copies the sticky status word to *host_status (synchronizes `stream`). */
 zf_status zf_get_status(const uint32_t* status, uint32_t* host_status, zf_stream_t stream);

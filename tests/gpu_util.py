@@ -42,7 +42,7 @@ class Setup:
     """One workload resident on the GPU: raw pages, packed cache (GPU-encoded), seqs."""
 
     def __init__(self, inst: synth.Instance, spill_slots: int | None = None, max_seq_len=None,
-                 encode=True):
+                 encode=True, one_launch_append=True):
         self.inst = inst
         w = inst.w
         self.w = w
@@ -50,7 +50,8 @@ class Setup:
             spill_slots = spill_need(inst, w.batch * (w.extra_tokens + 1))
         self.raw = dev(inst.raw_pages)
         self.cache = zf.PackedCache.empty(inst.num_pages, w.page_size, w.num_kv_heads,
-                                          w.head_dim, spill_slots)
+                                          w.head_dim, spill_slots,
+                                          one_launch_append=one_launch_append)
         cap = inst.page_table.shape[1] * w.page_size
         self.seqs = zf.Seqs(dev(inst.page_table), dev(inst.seq_lens.copy()),
                             int(max_seq_len if max_seq_len is not None else cap))

@@ -70,6 +70,7 @@ def _cache(**kw):
     (dict(num_kv_heads=16), zf.ZF_EUNSUPPORTED),
     (dict(status=None), zf.ZF_EINVAL),
     (dict(spill_slots=1 << 32), zf.ZF_EUNSUPPORTED),
+    (dict(append_sync=2052), zf.ZF_EINVAL),   # sync words not 8-byte aligned
 ])
 def test_bad_cache_is_rejected_before_any_launch(kw, code):
     lib = zf.load()

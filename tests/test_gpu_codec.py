@@ -54,9 +54,9 @@ def test_decode_roundtrip(key):
     assert not got[untouched].any(), "decode wrote outside the defined rows"
 
 
-def _append_steps(w, steps, check_every=1):
+def _append_steps(w, steps, check_every=1, one_launch=True):
     inst = synth.make(w)
-    s = Setup(inst)
+    s = Setup(inst, one_launch_append=one_launch)
     orc = oracle_cache(inst, s.cache.spill_slots)
     lens = inst.seq_lens.copy()
     for step in range(steps):
@@ -71,13 +71,104 @@ def _append_steps(w, steps, check_every=1):
     return s, inst, lens
 
 
-@pytest.mark.parametrize("key,steps", [("small", 3), (1, 1), (3, 1), (4, 64)])
-def test_append_bitexact(key, steps):
+@pytest.mark.parametrize("key,steps,form", [("small", 3, "one"), (1, 1, "one"), (3, 1, "one"),
+                                            (4, 64, "one"), ("small", 3, "two"), (1, 2, "two")])
+def test_append_bitexact(key, steps, form):
+    """Single-token appends, in the one-launch form (batch <= 64 new rows, the cache's sync
+    words set; batch 64 is its limit) and in the two-launch form."""
     w = workload(key)
     if w.extra_tokens < steps:
         w = w.replace(extra_tokens=steps)
-    log(f"append parity: workload {w.name}, {steps} steps")
-    _append_steps(w, steps, check_every=16)
+    log(f"append parity: workload {w.name}, {steps} steps, {form}-launch form")
+    s, _, _ = _append_steps(w, steps, check_every=16, one_launch=form == "one")
+    if form == "one":
+        assert int(host(s.cache.append_sync)[64]) == steps, "one epoch per one-launch call"
+
+
+def test_append_forms_write_the_same_bytes():
+    """The same appends through both forms leave every array equal, spill pool included."""
+    w = SMALL.replace(extra_tokens=6, p_wide_block=0.2)
+    log(f"append forms: workload {w.name}")
+    inst = synth.make(w)
+    one, two = Setup(inst), Setup(inst, one_launch_append=False)
+    lens = inst.seq_lens.copy()
+    for step in range(6):
+        k, v = synth.tokens(w, lens)
+        if step == 2:
+            k[:, :, 0] = 0  # a raw block in every new row
+        zf.zf_append_kv(one.cache, one.seqs, dev(k), dev(v))
+        zf.zf_append_kv(two.cache, two.seqs, dev(k), dev(v))
+        lens += 1
+    torch.cuda.synchronize()
+    assert one.status() == 0 and two.status() == 0
+    for n in ("sm", "nib", "base", "row_flags", "row_spill", "spill", "spill_top"):
+        assert np.array_equal(host(getattr(one.cache, n)), host(getattr(two.cache, n))), n
+    assert np.array_equal(host(one.seqs.seq_lens), lens)
+    assert int(host(one.cache.append_sync)[64]) == 6
+
+
+def test_one_launch_append_wait_bound_reports_and_changes_nothing():
+    """A zero wait bound makes the commit give up at once: ZF_DEV_ESYNC, no defined state
+    changed; after the sync words are zeroed, the same append succeeds and matches the oracle."""
+    w = SMALL
+    inst = synth.make(w)
+    s = Setup(inst)
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    rows = valid_rows(inst)
+    names = ("sm", "nib", "base", "row_flags", "row_spill")
+    before = {n: host(getattr(s.cache, n)).copy() for n in names}
+    top = int(host(s.cache.spill_top)[0])
+    k, v = synth.tokens(w, inst.seq_lens)
+    zf.zf_set_append_wait_polls(0)
+    try:
+        zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
+        torch.cuda.synchronize()
+    finally:
+        zf.zf_set_append_wait_polls(1 << 16)
+    assert s.status() & zf.ZF_DEV_ESYNC
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == top
+    for n in names:
+        a, b = host(getattr(s.cache, n)), before[n]
+        m = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
+        assert np.array_equal(a[m], b[m]), n
+    s.cache.append_sync.zero_()
+    s.cache.status.zero_()
+    lens = inst.seq_lens.copy()
+    zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
+    assert orc.append(lens, inst.page_table, k, v) == oracle.OK
+    torch.cuda.synchronize()
+    assert s.status() == 0
+    compare_packed(s.cache, orc, valid_rows(inst, lens), "append after a timed-out one")
+
+
+def test_one_launch_append_bad_page_changes_nothing():
+    """A new row whose page-table entry is out of range: ZF_DEV_EPAGE, lengths and spill_top
+    kept, the epoch still advanced, and a later append on a good table matches the oracle."""
+    w = SMALL
+    inst = synth.make(w)
+    s = Setup(inst)
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    T = w.page_size
+    b = int(np.argmax(inst.seq_lens))
+    pt_bad = inst.page_table.copy()
+    pt_bad[b, int(inst.seq_lens[b]) // T] = inst.num_pages + 3
+    bad = zf.Seqs(dev(pt_bad), s.seqs.seq_lens, s.seqs.max_seq_len)
+    top = int(host(s.cache.spill_top)[0])
+    k, v = synth.tokens(w, inst.seq_lens)
+    zf.zf_append_kv(s.cache, bad, dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert s.status() & zf.ZF_DEV_EPAGE
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == top
+    assert int(host(s.cache.append_sync)[64]) == 1
+    s.cache.status.zero_()
+    lens = inst.seq_lens.copy()
+    zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
+    assert orc.append(lens, inst.page_table, k, v) == oracle.OK
+    torch.cuda.synchronize()
+    assert s.status() == 0
+    compare_packed(s.cache, orc, valid_rows(inst, lens), "append after a bad-page one")
 
 
 def test_append_spill_exhaustion_changes_no_defined_state():
