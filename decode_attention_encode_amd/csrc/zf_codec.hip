@@ -23,6 +23,12 @@ struct SeqView {
   int32_t* lens;
 };
 
+// Whether `need` more slots fit in a pool of `slots` whose first `top` are taken (a top beyond
+// the pool, which no call leaves behind, counts as full).
+__device__ __forceinline__ bool fits_in_pool(uint64_t need, uint64_t top, uint64_t slots) {
+  return top <= slots && need <= slots - top;
+}
+
 // Rows of logical page p of sequence b that hold tokens, or -1 when the length is invalid.
 __device__ __forceinline__ int rows_in_page(const SeqView& s, const Geom& g, int b, int p,
                                             int32_t* len_out) {
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan_k(Geom g, SeqView s,
       run += tot;
     }
     if (pass == 0) {
-      if (tid == 0) s_total = (run > spill_slots - top) ? 1u : 0u;
+      if (tid == 0) s_total = fits_in_pool(run, top, spill_slots) ? 0u : 1u;
       __syncthreads();
       if (s_total) {
         if (tid == 0) {
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqVie
   __syncthreads();
   const uint64_t top = *spill_top;
   const uint32_t total = s_total;
-  if ((uint64_t)total > spill_slots - top) {
+  if (!fits_in_pool(total, top, spill_slots)) {
     if (tid == 0) set_status(status, ZF_DEV_ESPILL);
     return;
   }
@@ -505,7 +511,7 @@ __device__ void commit_one(const SeqView& s, int n, uint64_t* spill_top, uint64_
     if (tid == 0) set_status(status, ZF_DEV_ESYNC);
     return;
   }
-  const bool fits = (uint64_t)h.total <= spill_slots - top;
+  const bool fits = fits_in_pool(h.total, top, spill_slots);
   if (tid == 0) set_status(status, h.err ? h.err : (fits ? 0u : ZF_DEV_ESPILL));
   if (!h.err && fits) {
     if (tid < s.B) s.lens[tid] = L + n;  // every packing workgroup read its length before its word
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
     return;
   }
   // the commit takes the same decision from the same words
-  if (h.err || (uint64_t)h.total > spill_slots - top) return;
+  if (h.err || !fits_in_pool(h.total, top, spill_slots)) return;
   const uint64_t first = top + h.pref;
   if (has && o.raw) {
     const uint64_t slot = first + __popc(f & ((1u << j) - 1u));

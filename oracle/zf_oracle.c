@@ -143,7 +143,8 @@ uint32_t orc_encode_kv(const orc_geom* g, orc_cache* c, int32_t batch, const int
       }
     if (pass == 0) {
       need = next - c->spill_top;
-      if (need > c->spill_slots - c->spill_top) { free(src); return ORC_ESPILL; }
+      /* a top beyond the pool leaves no free slot */
+      if (c->spill_top > c->spill_slots || need > c->spill_slots - c->spill_top) { free(src); return ORC_ESPILL; }
     } else {
       c->spill_top = next;
     }
@@ -175,7 +176,10 @@ uint32_t orc_append_kv_n(const orc_geom* g, orc_cache* c, int32_t batch, int32_t
         next += (uint64_t)encode_row(g, c, page, t % T, src, next, pass == 1);
       }
     if (pass == 0) {
-      if (next - c->spill_top > c->spill_slots - c->spill_top) { free(src); return ORC_ESPILL; }
+      if (c->spill_top > c->spill_slots || next - c->spill_top > c->spill_slots - c->spill_top) {
+        free(src);
+        return ORC_ESPILL;
+      }
     } else {
       c->spill_top = next;
     }

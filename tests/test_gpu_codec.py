@@ -205,6 +205,35 @@ def test_append_spill_exhaustion_changes_no_defined_state():
     compare_packed(s2.cache, orc2, valid_rows(inst, lens), "append after a failed one")
 
 
+@pytest.mark.parametrize("form", ["one", "two"])
+def test_top_beyond_the_pool_counts_as_full(form):
+    """spill_top past spill_slots (the buffers stay large, so nothing can land out of bounds):
+    an append reports ZF_DEV_ESPILL and changes nothing even with no raw block to spill, and so
+    does an encode; the oracle follows the same rule."""
+    w = SMALL
+    inst = synth.make(w)
+    s = Setup(inst, one_launch_append=form == "one")
+    top = int(host(s.cache.spill_top)[0])
+    s.cache.spill_slots = top - 1
+    k, v = synth.tokens(w, inst.seq_lens)
+    k[:] = 0x3F80  # 1.0: no raw block
+    v[:] = 0x3F80
+    spill_before = host(s.cache.spill).copy()
+    zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert s.status() & zf.ZF_DEV_ESPILL
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == top
+    assert np.array_equal(host(s.cache.spill), spill_before)
+    e = Setup(inst, encode=False)
+    e.cache.spill_slots = 8
+    e.cache.spill_top.fill_(9)
+    zf.zf_encode_kv(e.cache, e.seqs, e.raw, zf.encode_workspace(e.seqs))
+    torch.cuda.synchronize()
+    assert e.status() & zf.ZF_DEV_ESPILL
+    assert int(host(e.cache.spill_top)[0]) == 9 and not host(e.cache.spill).any()
+
+
 def _chunk_tokens(w, lens, n):
     """n new tokens per sequence at positions lens[b] .. lens[b] + n - 1: two u16[B][n][H][D]."""
     ks, vs = zip(*(synth.tokens(w, lens + j) for j in range(n)))

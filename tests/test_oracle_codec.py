@@ -387,6 +387,29 @@ def test_spill_exhaustion_is_all_or_nothing():
     assert np.array_equal(before, c.spill)
 
 
+def test_top_beyond_the_pool_counts_as_full():
+    """A spill_top past spill_slots (no call leaves one; a caller might) holds no free slot:
+    encode and append report exhaustion and write nothing, even when no new block is raw."""
+    inst = synth.make(_small(seed=15, extra_tokens=1))
+    w = inst.w
+    st, c = _encode(inst, slots=1 << 16)
+    assert st == oracle.OK
+    c.spill_slots = c.spill_top - 1
+    lens = inst.seq_lens.copy()
+    k, v = synth.tokens(w, lens)
+    k[:] = 0x3F80  # 1.0 everywhere: no raw block, nothing to spill
+    v[:] = 0x3F80
+    before = c.spill.copy()
+    top = c.spill_top
+    assert c.append(lens, inst.page_table, k, v) == oracle.ESPILL
+    assert np.array_equal(lens, inst.seq_lens) and c.spill_top == top
+    assert np.array_equal(before, c.spill)
+    c2 = oracle.Cache(inst.num_pages, w.page_size, w.num_kv_heads, w.head_dim, 8)
+    c2.spill_top = 9
+    assert c2.encode(inst.seq_lens, inst.page_table, inst.raw_pages) == oracle.ESPILL
+    assert c2.spill_top == 9 and not c2.spill.any()
+
+
 def test_bad_page_and_length_are_reported():
     inst = synth.make(_small(seed=16))
     pt = inst.page_table.copy()
