@@ -23,6 +23,7 @@ steps.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -269,8 +270,9 @@ def main():
 def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_bytes):
     """Twin (uncompressed) attention over the same rotation of layer caches, the unfused
     alternative (decode to bf16, then the twin), a plain streaming read over the same bytes,
-    the single-layer warm-cache loop, full-cache encode / decode rates, multi-token append,
-    spill compaction, and the capacity model at a fixed HBM budget."""
+    the single-layer warm-cache loop, full-cache encode / decode rates, the single-token append
+    in both forms, multi-token append, spill compaction, and the capacity model at a fixed HBM
+    budget."""
     res = {}
     stream = torch.cuda.current_stream()
     NL = len(layers)
@@ -352,6 +354,27 @@ def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_byte
     lens_at = torch.from_numpy(inst.seq_lens.copy()).to(raw.device)
     seqs_at = zf.Seqs(seqs.page_table, lens_at.clone(), seqs.max_seq_len)
     top_dev = cache.spill_top.clone()
+
+    # single-token append (the decode step's write) alone, in both forms: HIP events around
+    # each call only, lengths and spill_top restored between calls outside the timed interval
+    k1, v1 = k16[:, 0].contiguous(), v16[:, 0].contiguous()
+    for name, c in (("append_us", cache), ("append_two_launch_us", dataclasses.replace(cache, append_sync=None))):
+        if c.append_sync is None and name == "append_us":
+            continue
+        ts = []
+        for i in range(60):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            zf.zf_append_kv(c, seqs_at, k1, v1)
+            b.record(stream)
+            seqs_at.seq_lens.copy_(lens_at)
+            c.spill_top.copy_(top_dev)
+            if i >= 10:
+                ts.append((a, b))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in ts]
+        res[name] = round(float(np.mean(us)), 2)
+        res[name.replace("_us", "_us_min")] = round(float(np.min(us)), 2)
 
     def app(i):
         zf.zf_append_kv_n(cache, seqs_at, k16, v16)
