@@ -275,17 +275,19 @@ __global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint
 // at most 64 new rows): R packing workgroups and one commit workgroup.  Each packing workgroup
 // publishes one 64-bit word, its row's flag word and error bits tagged with the call's epoch
 // (a counter in the sync area), stored only after its loads of the epoch, its length and
-// spill_top have returned.  Every workgroup then waits until all R words carry the tag and
-// takes the same all-or-nothing decision from them; a packing workgroup also gets its row's
-// first spill slot (spill_top plus the raw blocks of the rows before it) and writes its own
-// spill slots and row_spill, and the commit advances seq_lens and spill_top (every length was
-// read before its word was stored) and then the epoch.  Each word carries its data itself, so
-// no fence orders it after other stores.
+// spill_top have returned.  Every packing workgroup then waits until all R words carry the tag,
+// takes the all-or-nothing decision from them, marks its own word decided, and writes its
+// row's spill slots (from spill_top plus the raw blocks of the rows before it) and row_spill.
+// The commit waits until all R words are marked decided, takes the same decision, and advances
+// seq_lens and spill_top (every length was read before its word was stored) and then the
+// epoch; a workgroup that gives up waiting never marks its word, so the commit then changes
+// nothing.  Each word carries its data itself, so no fence orders it after other stores.
 constexpr int kAppendThreads = 1024;
 constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS
 constexpr int kOneMaxRows = 64;       // new rows of a one-launch append (sync words 0 .. 63; 64: epoch)
-constexpr uint32_t kSyncPolls = 1u << 16;  // bound on each wait for the words (about 0.1 s)
-constexpr uint64_t kTagMod = (1u << 29) - 1u;
+constexpr uint32_t kSyncPolls = 1u << 16;  // bound on each wait for the words (about 0.1 s);
+                                           // the packing workgroups' bound can be lowered
+constexpr uint64_t kTagMod = (1u << 28) - 1u;
 
 // Row of new token j of sequence b (n per sequence) whose length was read as L, or -1 (with the
 // error bit) when the sequence cannot take them.
@@ -458,8 +460,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqVie
 // epochs (a word left by the previous call never matches).
 __device__ __forceinline__ uint32_t sync_tag(uint64_t E) { return (uint32_t)(E % kTagMod) + 1u; }
 
-// Hand-over word of one new row: tag << 35 | error bits << 32 | flag word.
-__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 35); }
+// Hand-over word of one new row: tag << 36 | decided << 35 | error bits << 32 | flag word.
+// `decided`: the row's workgroup has seen every word of the call (so it will write its spill
+// slots if the call succeeds).
+__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 36); }
+constexpr uint64_t kDecided = (uint64_t)1 << 35;
 
 // What every workgroup learns from the R hand-over words (wave 0 polls them, lane i word i).
 struct HandOver {
@@ -467,7 +472,7 @@ struct HandOver {
 };
 
 __device__ __forceinline__ HandOver read_hand_over(const uint64_t* sync, int R, int me, uint32_t tag,
-                                                   uint32_t polls) {
+                                                   bool need_decided, uint32_t polls) {
   __shared__ HandOver s_h;
   const int tid = threadIdx.x;
   if (tid < 64) {
@@ -475,7 +480,7 @@ __device__ __forceinline__ HandOver read_hand_over(const uint64_t* sync, int R, 
     bool ok = tid >= R;
     for (uint32_t p = 0; !ok && p < polls; ++p) {
       w = __hip_atomic_load(&sync[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = word_tag(w) == tag;
+      ok = word_tag(w) == tag && (!need_decided || (w & kDecided));
       if (!ok) __builtin_amdgcn_s_sleep(2);
     }
     const uint32_t cnt = tid < R ? __popc((uint32_t)w) : 0u;
@@ -498,16 +503,17 @@ __device__ __forceinline__ HandOver read_hand_over(const uint64_t* sync, int R, 
   return s_h;
 }
 
-// Commit workgroup of the one-launch append: once every row's word carries this call's tag, it
-// advances seq_lens and spill_top, clears the words of unused rows and moves to the next epoch.
+// Commit workgroup of the one-launch append: once every row's word carries this call's tag and
+// the decided mark, it advances seq_lens and spill_top, clears the words of unused rows and
+// moves to the next epoch.
 __device__ void commit_one(const SeqView& s, int n, uint64_t* spill_top, uint64_t spill_slots,
-                           uint32_t* status, uint64_t* sync, uint32_t polls) {
+                           uint32_t* status, uint64_t* sync) {
   const int R = s.B * n, tid = threadIdx.x;
   const uint64_t E = sync[kOneMaxRows];  // written only by an earlier launch: a plain load
   const uint64_t top = *spill_top;
   const int32_t L = tid < s.B ? s.lens[tid] : 0;
-  const HandOver h = read_hand_over(sync, R, -1, sync_tag(E), polls);
-  if (!h.seen) {  // some row's word never came: change nothing, keep the epoch
+  const HandOver h = read_hand_over(sync, R, -1, sync_tag(E), true, kSyncPolls);
+  if (!h.seen) {  // some row's word never came or never got decided: change nothing
     if (tid == 0) set_status(status, ZF_DEV_ESYNC);
     return;
   }
@@ -531,7 +537,7 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
                                                     uint32_t polls) {
   const int R = s.B * n, r = blockIdx.x, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
   if (r == R) {
-    commit_one(s, n, spill_top, spill_slots, status, sync, polls);
+    commit_one(s, n, spill_top, spill_slots, status, sync);
     return;
   }
   const uint64_t E = sync[kOneMaxRows];
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
   if (tid == 0) {
     // the word is built from the epoch, the length (through err and row) and spill_top as
     // loaded, so it cannot be stored before those loads have returned
-    uint32_t hi = (sync_tag(E) << 3) | err;
+    uint32_t hi = (sync_tag(E) << 4) | err;
     asm volatile("" : "+v"(hi) : "v"((uint32_t)row), "v"((uint32_t)top));
     __hip_atomic_store(&sync[r], ((uint64_t)hi << 32) | f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -554,11 +560,14 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
     if (has) store_new(g, row, j, lane8, o, sm, nib, base);
     if (tid == 0) row_flags[row] = f;
   }
-  const HandOver h = read_hand_over(sync, R, r, sync_tag(E), kSyncPolls);
-  if (!h.seen) {
+  const HandOver h = read_hand_over(sync, R, r, sync_tag(E), false, polls);
+  if (!h.seen) {  // the commit will not see this row decided, so the call changes nothing
     if (tid == 0) set_status(status, ZF_DEV_ESYNC);
     return;
   }
+  if (tid == 0)
+    __hip_atomic_store(&sync[r], ((uint64_t)((sync_tag(E) << 4) | err) << 32 | kDecided) | f,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // the commit takes the same decision from the same words
   if (h.err || !fits_in_pool(h.total, top, spill_slots)) return;
   const uint64_t first = top + h.pref;

@@ -108,8 +108,10 @@ def test_append_forms_write_the_same_bytes():
 
 
 def test_one_launch_append_wait_bound_reports_and_changes_nothing():
-    """A zero wait bound makes the commit give up at once: ZF_DEV_ESYNC, no defined state
-    changed; after the sync words are zeroed, the same append succeeds and matches the oracle."""
+    """A zero wait bound makes the packing workgroups give up before they mark their words
+    decided; the commit, which saw every word's tag but no decided mark, waits out its bound:
+    ZF_DEV_ESYNC and no defined state changed.  After the sync words are zeroed, the same
+    append succeeds and matches the oracle."""
     w = SMALL
     inst = synth.make(w)
     s = Setup(inst)
