@@ -118,9 +118,9 @@ size_t zf_encode_workspace_bytes(const zf_seqs* seqs);
 /* Decode-step append: encodes one new token per sequence (k_new, v_new u16[batch][H][D])
  * into row seq_lens[b] of its page, spill slots from *spill_top in batch order, then
  * seq_lens[b] += 1 for every b.  All or nothing for defined state: on a device error
- * (ZF_DEV_*) seq_lens, spill_top, the spill pool and every row t < seq_lens[b] are left as
- * they were; only the slots at position seq_lens[b], which are not yet part of any sequence,
- * may have been overwritten.  seqs->max_seq_len bounds the lengths after the append.
+ * (ZF_DEV_*) seq_lens, spill_top, the spill slots below spill_top and every row
+ * t < seq_lens[b] are left as they were; only the rows at position seq_lens[b] and the spill
+ * slots from spill_top on, which hold nothing yet, may have been overwritten.  seqs->max_seq_len bounds the lengths after the append.
  * Supports batch <= 4096.  Launches as zf_append_kv_n with n_new = 1. */
 zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
                        const uint16_t* v_new, zf_stream_t stream);
