@@ -207,3 +207,12 @@ def test_attention_rejects_spill_pool_beyond_32bit_offsets():
                                    4096, 4096, 1 << 20, None) == zf.ZF_EUNSUPPORTED
     assert lib.zf_decode_attention(ctypes.byref(ok), ctypes.byref(s), 4096, 32, ctypes.c_float(0.1),
                                    4096, 4096, 0, None) == zf.ZF_EWORKSPACE
+
+
+def test_header_constants_match_the_binding():
+    """The device status bits and the size of the append sync area are the header's."""
+    text = open(HEADER).read()
+    defs = {k: int(v.rstrip("u")) for k, v in re.findall(r"#define\s+(ZF_\w+)\s+(\d+u?)", text)}
+    for name in ("ZF_DEV_ESPILL", "ZF_DEV_EPAGE", "ZF_DEV_ELEN", "ZF_DEV_ESYNC", "ZF_APPEND_SYNC_WORDS"):
+        assert defs[name] == getattr(zf, name), name
+
