@@ -107,6 +107,41 @@ def test_append_forms_write_the_same_bytes():
     assert int(host(one.cache.append_sync)[64]) == 6
 
 
+def test_one_launch_append_with_changing_batch():
+    """One cache appended 24 times while the number of new rows changes between calls (a prefix
+    of the batch, 1 or 2 tokens per sequence: 1 to 64 rows in one launch, more in two), so the
+    hand-over words of rows a call does not use, and words left by earlier calls, are exercised;
+    bit-exact against the oracle after every call, one epoch per one-launch call."""
+    w = SMALL.replace(name="ragged_b64_short", batch=64, ctx_min=1, ctx_max=40, extra_tokens=48,
+                      seed=61)
+    log(f"one-launch append, changing batch: workload {w.name}")
+    inst = synth.make(w)
+    s = Setup(inst)
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    lens = inst.seq_lens.copy()
+    rng = np.random.default_rng(7)
+    ones = 0
+    for call in range(24):
+        k_seq = int(rng.choice([1, 2, 17, 33, 63, 64]))
+        n = int(rng.choice([1, 1, 2]))
+        kk, vv = _chunk_tokens(w, lens, n)
+        kk, vv = np.ascontiguousarray(kk[:k_seq]), np.ascontiguousarray(vv[:k_seq])
+        sub = zf.Seqs(dev(np.ascontiguousarray(inst.page_table[:k_seq])), s.seqs.seq_lens[:k_seq],
+                      s.seqs.max_seq_len)
+        if n == 1:
+            zf.zf_append_kv(s.cache, sub, dev(kk[:, 0].copy()), dev(vv[:, 0].copy()))
+            assert orc.append(lens[:k_seq], inst.page_table[:k_seq], kk[:, 0].copy(), vv[:, 0].copy()) == oracle.OK
+        else:
+            zf.zf_append_kv_n(s.cache, sub, dev(kk), dev(vv))
+            assert orc.append_n(lens[:k_seq], inst.page_table[:k_seq], kk, vv) == oracle.OK
+        ones += k_seq * n <= 64
+        torch.cuda.synchronize()
+        assert s.status() == 0, f"call {call}"
+        assert np.array_equal(host(s.seqs.seq_lens), lens), f"call {call}"
+        compare_packed(s.cache, orc, valid_rows(inst, lens), f"call {call} ({k_seq} x {n})")
+    assert int(host(s.cache.append_sync)[64]) == ones
+
+
 def test_one_launch_append_wait_bound_reports_and_changes_nothing():
     """A zero wait bound makes the packing workgroups give up before they mark their words
     decided; the commit, which saw every word's tag but no decided mark, waits out its bound:
