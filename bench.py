@@ -15,7 +15,7 @@ layer.  `roofline` prices the attention kernel (the dominant one) against HBM: a
 bytes per launch (packed planes of the attended rows, spill slots of their raw blocks, q, out,
 page table and lengths) / its mean duration from HIP events on the launch stream, stamped at
 the kernel's own start and end (zf_time_next_attention: the interval a kernel trace reports) on
-every 4th timed step (a stamped launch pays ~8 us more dispatch, so `value` would be understated
+every 8th timed step (a stamped launch pays ~8 us more dispatch, so `value` would be understated
 if every step carried the stamps); the call time with dispatch overhead is reported beside it.
 `cpu_baseline` times the CPU oracle (plain C, one thread) on a bounded sample of the same
 steps.
@@ -51,7 +51,7 @@ def attn_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-STAMP_EVERY = 4  # timed steps per kernel-stamped step
+STAMP_EVERY = 8  # timed steps per kernel-stamped step
 
 
 def parse():
