@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint
 constexpr int kAppendThreads = 1024;
 constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS
 constexpr int kOneMaxRows = 64;       // new rows of a one-launch append (sync words 0 .. 63; 64: epoch)
-constexpr uint32_t kSyncPolls = 1u << 16;  // bound on each wait for the words (about 0.1 s);
+constexpr uint32_t kSyncPolls = 1u << 20;  // bound on each wait for the words (about 1 s);
                                            // the packing workgroups' bound can be lowered
 constexpr uint64_t kTagMod = (1u << 28) - 1u;
 

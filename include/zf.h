@@ -73,7 +73,7 @@ typedef enum {
 #define ZF_DEV_EPAGE 2u   /* a page-table entry the call needed is out of range           */
 #define ZF_DEV_ELEN 4u    /* a length is negative or beyond the page table / host bound   */
 #define ZF_DEV_ESYNC 8u   /* one-launch append: a hand-over word did not arrive within the
-                             bounded wait (about 0.1 s; none is expected): the call changed
+                             bounded wait (about 1 s; none is expected): the call changed
                              no defined state; zero the sync area before the next append */
 
 typedef struct {
@@ -230,9 +230,9 @@ zf_status zf_time_next_attention(void* start_event, void* stop_event);
 zf_status zf_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, zf_stream_t stream);
 
 /* Bound on the one-launch append's packing workgroups' wait for each other's hand-over words,
- * in polls (default 65536, about 0.1 s), for appends enqueued after the call; process-wide.
+ * in polls (default 1048576, about 1 s), for appends enqueued after the call; process-wide.
  * 0 makes them give up at once, so every one-launch append then ends with ZF_DEV_ESYNC after
- * the commit has waited out its own bound (about 0.1 s): it lets tests take that path. */
+ * the commit has waited out its own bound (about 1 s): it lets tests take that path. */
 void zf_set_append_wait_polls(uint32_t polls);
 
 /* Copies the sticky status word to *host_status (synchronizes `stream`). */

@@ -161,7 +161,7 @@ def test_one_launch_append_wait_bound_reports_and_changes_nothing():
         zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
         torch.cuda.synchronize()
     finally:
-        zf.zf_set_append_wait_polls(1 << 16)
+        zf.zf_set_append_wait_polls(1 << 20)  # the default
     assert s.status() & zf.ZF_DEV_ESYNC
     assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
     assert int(host(s.cache.spill_top)[0]) == top
