@@ -23,9 +23,15 @@
 //   bf16 parts by truncation, hi + mid + lo = p exactly; row 4i + 3 zero), B is V with
 //   k = token: lane (t, qd) rebuilds V rows qd + 4j at head_dim 8t..8t+7 straight into token
 //   pairs.  The hi row goes to fp64 every page, mid and lo stay in the MFMA accumulators.
-//   Softmax: running max in fp64, raised (with a rescale) only when a page exceeds it.  Pages
-//   holding a score with |q.k| > kBigScore that can still matter get exact fp64 scores: at that
-//   size one fp32 ulp of a score is already a visible change of its weight.
+//   Softmax: running max in fp64, raised (with an fp64 rescale) only when a page exceeds it.
+//   Precise path: every score whose weight may reach 2^-40 of the final maximum is recomputed
+//   in fp64 from the exact bf16 products and weighted with an fp64 exp; the weight sums carry
+//   those fp64 weights.  An output that one large value dominates must be right to ~1e-9
+//   before its one rounding (the 1e-3 bar is an fp32 ulp at 2^14), and the matrix cores' fp32
+//   scores are only good to ~1e-6 of a weight.
+//   Large values: a lane's 8 values of a V row holding a magnitude >= 2^4 leave the p.V MFMA
+//   and are added in fp64 instead, with the fp64 weight, so the MFMA only ever sums products
+//   below 2^4 (where the fp32 rounding of its weights stays below 1e-6 of the output).
 //   Splits of the token axis write (acc, l, m) partials; a second small kernel merges them
 //   in split order, so results do not depend on timing.
 // One kernel body serves the packed cache and raw bf16 pages (the uncompressed twin): both
@@ -47,8 +53,30 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // older one is issued first and the younger one then finishes alone at half occupancy.
 constexpr int kD = 128, kT = 16, kWaves = 8, kThreads = 64 * kWaves;
 constexpr double kLog2e = 1.4426950408889634;
-constexpr float kBigScore = 64.f;  // |q.k| above which a score may need the fp64 path
-constexpr double kNegligible = 16.0;  // weights below 2^-16 of the largest never need it
+// Exact-value path: V values whose product with their weight may reach 2^4 leave the p.V MFMA,
+// which then only ever sums products below 2^4.  With the page's largest weight w in
+// [2^e, 2^(e+1)), e <= 0, that is every value with a biased exponent >= max(131, 130 - e)
+// (magnitude >= 2^4 while w can be 1).
+constexpr uint32_t kLargeExp = 131;
+// Which of the lane's four V rows (token qd + 4j) hold a value with biased exponent >= T among
+// their 8 values (bit j), from the rebuilt pairs: vt[2n] holds rows 0 and 1 in its two halves,
+// vt[2n + 1] rows 2 and 3.  Per half the largest magnitude (bf16 bits less the sign: exponent
+// at bits 7..14); adding 0x8000 - (T << 7) sets bit 15 exactly when that exponent is >= T.
+__device__ __forceinline__ uint32_t large_rows(const uint32_t (&vt)[16], uint32_t T) {
+  uint32_t m01 = 0u, m23 = 0u;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    m01 = pk_max_u16(m01, vt[2 * n] & 0x7FFF7FFFu);
+    m23 = pk_max_u16(m23, vt[2 * n + 1] & 0x7FFF7FFFu);
+  }
+  const uint32_t bias = (0x8000u - (T << 7)) * 0x00010001u;  // T <= 255: lanes stay below 0xBE80
+  const uint32_t r01 = m01 + bias, r23 = m23 + bias;
+  return ((r01 >> 15) & 1u) | ((r01 >> 30) & 2u) | ((r23 >> 13) & 4u) | ((r23 >> 28) & 8u);
+}
+// Precise path: tokens whose weight may reach 2^-kSigBits of the final maximum get fp64 scores
+// and fp64 weights.  Below that, a weight's fp32 error cannot show: even 2^20 tokens with
+// values of 2^17 move the output by less than 2^-40 * 2^20 * 2^17 * 2^-20 < 1e-7.
+constexpr double kSigBits = 40.0;
 // The hi row of p.V (below) sums this many pages in the MFMA's fp32 accumulator before it is
 // added in fp64: each MFMA rounds to a few fp32 ulps of its largest term, so a few pages of
 // weights <= 1 keep the row within ~2^-19 of its value.
@@ -74,6 +102,9 @@ struct AttnArgs {
   const int32_t* lens;
   const uint16_t* q;
   double scale_log2e;
+  float scale_log2e_f32;  // the same in fp32
+  float negl_f32;         // kSigBits / scale_log2e in fp32: scores further below the maximum
+                          // than this weigh less than 2^-kSigBits of it
   float* out;
   double* part;  // [B][H][nsplit_max][part_doubles(G)]
   uint32_t* status;
@@ -140,7 +171,8 @@ __device__ __forceinline__ void wait_vm() {
 // A loader moves one page (16 tokens of kv head h) into an LDS slot and rebuilds it as bf16 pairs:
 //   kp[4c + r]   K (head_dim 32*qd + 8c + r, same + 4) of token krow(t)
 //   vt[2n], vt[2n + 1]   V (tokens qd, qd + 4) and (qd + 8, qd + 12) at head_dim vdim(n, t)
-// with t = lane & 15, qd = lane >> 4.  kMetaLoads / kPageLoads: direct loads per meta / page.
+// with t = lane & 15, qd = lane >> 4.
+// kMetaLoads / kPageLoads: direct loads per meta / page.
 //
 // Token order: row i of the score MFMA's A operand holds token krow(i), so its output row
 // 4qd + r -- the r-th score of lane (t, qd) -- is token qd + 4r.  The p.V operands use the same
@@ -299,15 +331,13 @@ struct PackedLoader {
   }
 
   __device__ __forceinline__ void rebuild_k(const Page& p, int, int, uint32_t (&kp)[16]) const {
-    {
-      // a raw block has base 0 and its spill piece, a compressed one its base and zeros
-      const uint32_t bp = p.kb * 0x00010001u;
-      const uint32_t smw[8] = {p.ks0.x, p.ks0.y, p.ks0.z, p.ks0.w, p.ks1.x, p.ks1.y, p.ks1.z, p.ks1.w};
-      const uint32_t nw[4] = {p.kn.x, p.kn.y, p.kn.z, p.kn.w};
-      const uint32_t hw[4] = {p.kh.x, p.kh.y, p.kh.z, p.kh.w};
+    // a raw block has base 0 and its spill piece, a compressed one its base and zeros
+    const uint32_t bp = p.kb * 0x00010001u;
+    const uint32_t smw[8] = {p.ks0.x, p.ks0.y, p.ks0.z, p.ks0.w, p.ks1.x, p.ks1.y, p.ks1.z, p.ks1.w};
+    const uint32_t nw[4] = {p.kn.x, p.kn.y, p.kn.z, p.kn.w};
+    const uint32_t hw[4] = {p.kh.x, p.kh.y, p.kh.z, p.kh.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) rebuild8(smw[2 * c], smw[2 * c + 1], nw[c], hw[c], bp, kp + 4 * c);
-    }
+    for (int c = 0; c < 4; ++c) rebuild8(smw[2 * c], smw[2 * c + 1], nw[c], hw[c], bp, kp + 4 * c);
   }
 
   // V is rebuilt in groups of two rows: group (q, hh) takes dims 4hh..4hh+3 of rows j = 2q and
@@ -444,6 +474,34 @@ __device__ __forceinline__ double rows_sum_d(double v) {
   pair_d<true>(a + b, a, b);
   return a + b;
 }
+// 2^x in fp64 for x <= 0 (weights and rescale factors).  x = n + f with n = rint(x) and
+// |f| <= 1/2; 2^f = e^y, y = f ln 2, |y| < 0.35, from the Taylor series of e^y to degree 9
+// (truncation below 0.35^10 / 10! < 8e-12 of the result); then 2^n by the exponent.  Written
+// here rather than taken from the math library so that its coefficients come from the constant
+// table below (scalar registers): as VGPRs they pushed the 8-head kernel past its register
+// budget.  Exponents below -1075 give 0 (x = -inf included).
+__constant__ double kExpTaylor[10] = {
+    1.0, 1.0, 1.0 / 2, 1.0 / 6, 1.0 / 24, 1.0 / 120, 1.0 / 720, 1.0 / 5040, 1.0 / 40320,
+    1.0 / 362880};
+__device__ __forceinline__ double exp2_neg(double x) {
+  const double n = rint(x);
+  const double y = (x - n) * 0.69314718055994530942;
+  double r = kExpTaylor[9];
+#pragma unroll
+  for (int k = 8; k >= 0; --k) r = fma(r, y, kExpTaylor[k]);
+  return x < -1075.0 ? 0.0 : ldexp(r, (int)fmax(n, -1100.0));
+}
+
+// A double from lane I of the lane's quad (DPP quad_perm, both halves the same way).
+template <int I0, int I1, int I2, int I3>
+__device__ __forceinline__ double quad_pick(double v) {
+  constexpr int ctrl = I0 | (I1 << 2) | (I2 << 4) | (I3 << 6);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, ctrl, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, false);
+  return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+
 // max over the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48) of a float
 __device__ __forceinline__ float rows_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -641,10 +699,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     cacc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const double c2 = a.scale_log2e;
-  const float c2f = (float)c2;
+  const float c2f = a.scale_log2e_f32;
   double mc2 = 0.0;        // m * c2 once m is finite
   float m32 = -INFINITY;   // m in fp32, for the exact-path test
-  const float negl32 = (float)(kNegligible / c2);
+  // from the kernel arguments, so it stays in a scalar register (computed here it sat in a VGPR
+  // that was spilled and reloaded inside the page loop, behind a wait for every load in flight)
+  const float negl32 = a.negl_f32;
   float shared32 = -INFINITY;  // the workgroup's maximum kShareLag steps ago (fp32)
 
   // page n of this wave; indices past the end repeat the last page (their metadata loads keep
@@ -676,48 +736,73 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       for (int i = 0; i < 4; ++i) sc[i] = qd + 4 * i < ntok ? sc[i] : -INFINITY;
     }
     const float pm32 = rows_max(max_f32(max3_f32(sc[0], sc[1], sc[2]), sc[3]));
-    // A score needs the exact path when it is large (one fp32 ulp of it is then a visible
-    // change of its weight) and its weight can matter: scores more than kNegligible / c2
-    // below the running maximum get a weight under 2^-kNegligible of the largest one.
+    // A score is significant unless it lies more than kSigBits / c2 below a lower bound of the
+    // final maximum (the wave's running maximum, this page's, and the workgroup's of a few steps
+    // ago): only then is its weight sure to stay under 2^-kSigBits of the largest one.  The
+    // fp32 score of the matrix cores is off by up to ~1e-6 of its weight, and an output that a
+    // large value dominates needs its weights to ~1e-9, so significant scores are recomputed in
+    // fp64 from the exact bf16 products (the margin covers the fp32 error of this test).
     const float floor32 = max_f32(max_f32(m32, pm32), shared32) - negl32;
     bool big = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) big |= fabsf(sc[i]) > kBigScore && sc[i] > floor32;
+    for (int i = 0; i < 4; ++i) big |= sc[i] > floor32;
     double sd[4], pm;
     const bool exact = __any(big);
     if (exact) {
-      // exact fp64 scores for the heads that hold such a score (a page usually has one or two):
-      // lane (t, qd) sums its 32 dims of token krow(t) for each of them, the four quarters are
-      // added, and each lane then fetches its own (token, head) entries.  Heads without one keep
-      // their fp32 scores.
+      // exact fp64 scores for the heads that hold a significant score: lane (t, qd) sums its 32
+      // dims of token krow(t) for each of them, the four quarters are added, and each lane then
+      // fetches its own (token, head) entries.  Heads without one keep their fp32 scores.
       const uint64_t bm = __ballot(big);  // bit 16 qd + t: head t / kParts
       const uint32_t cols = (uint32_t)(bm | (bm >> 16) | (bm >> 32) | (bm >> 48)) & 0xFFFFu;
-      float klo[16], khi[16];  // this lane's K values, exact in fp32
+      // K in fp64 four dims at a time, shared by every head that needs it; per head and group
+      // of four dims the four q reads go out together; two FMA chains per head (G = 4)
+      constexpr int kChains = G == 4 ? 2 : 1;
+      uint32_t hm = 0;  // heads with a significant score (wave-uniform)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        klo[k] = __uint_as_float(kp[k] << 16);
-        khi[k] = __uint_as_float(kp[k] & 0xFFFF0000u);
+      for (int i = 0; i < G; ++i) hm |= ((cols >> (kParts * i)) & kColMask) ? 1u << i : 0u;
+      double acc2[G][kChains];
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc2[i][c] = 0.0;
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        double kl[4], kh[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kl[u] = (double)__uint_as_float(kp[k0 + u] << 16);
+          kh[u] = (double)__uint_as_float(kp[k0 + u] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          if ((hm >> i) & 1u) {  // wave-uniform
+            double2 qq[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) qq[u] = s_q64[i][qd][k0 + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              acc2[i][0] = fma(qq[u].x, kl[u], acc2[i][0]);
+              acc2[i][kChains - 1] = fma(qq[u].y, kh[u], acc2[i][kChains - 1]);
+            }
+          }
+        }
       }
       double pd[G];
 #pragma unroll
       for (int i = 0; i < G; ++i) {
         pd[i] = 0.0;
-        if ((cols >> (kParts * i)) & kColMask) {  // wave-uniform
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const double2 qq = s_q64[i][qd][k];
-            pd[i] = fma(qq.x, (double)klo[k], pd[i]);
-            pd[i] = fma(qq.y, (double)khi[k], pd[i]);
-          }
-          pd[i] = rows_sum_d(pd[i]);
-        }
+        if ((hm >> i) & 1u) pd[i] = rows_sum_d(kChains == 2 ? acc2[i][0] + acc2[i][kChains - 1] : acc2[i][0]);
       }
       // lane (t', qd') offers heads qd' (and qd' + 4) of token krow(t'); lane (t, qd) reads
       // token qd + 4i = krow(4qd + i), head t / kParts
       const double offer = qd == 0 ? pd[0] : qd == 1 ? pd[1] : qd == 2 ? pd[2] : pd[3];
       double offer2 = 0.0;
       if constexpr (G == 8) offer2 = qd == 0 ? pd[4] : qd == 1 ? pd[5] : qd == 2 ? pd[6] : pd[7];
-      const bool mine = (cols >> (kParts * head)) & kColMask;
+      // (the shift is rebuilt from an opaque copy of t on every page: hoisted out of the loop,
+      // it would hold a register for the whole kernel)
+      int tq = t;
+      asm volatile("" : "+v"(tq));
+      const bool mine = (cols >> (tq & ~(kParts - 1))) & kColMask;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         double x = __shfl(offer, (head & 3) * 16 + 4 * qd + i, 64);
@@ -725,7 +810,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
           const double x2 = __shfl(offer2, (head & 3) * 16 + 4 * qd + i, 64);
           x = head >= 4 ? x2 : x;
         }
-        // tokens past the end stay out; heads without a big score keep the fp32 one
+        // tokens past the end stay out; heads without a significant score keep the fp32 one
         sd[i] = sc[i] == -INFINITY ? -INFINITY : mine ? x : (double)sc[i];
       }
       pm = rows_max_d(max_f64(max_f64(sd[0], sd[1]), max_f64(sd[2], sd[3])));
@@ -747,20 +832,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       }
     }
     if (__any(pm > m)) {
-      // rescale by alpha = 2^((m - mn) c2), one fp32 factor for all of this head's sums (fp64
-      // and MFMA ones alike): where alpha is not negligible its exponent is small, so fp32 is
-      // accurate to ~1e-6 there, and a common factor cancels in acc / l anyway
+      // rescale by alpha = 2^((m - mn) c2) in fp64: the factor applies to every earlier token,
+      // so its error would act as a weight error of all of them
       const double mn = fmax(m, pm);
-      const float alpha = __builtin_amdgcn_exp2f((float)((m - mn) * c2));
+      const double alpha = exp2_neg((m - mn) * c2);  // m = -inf (no finite score yet): 0
       m = mn;
       m32 = (float)m;
       mc2 = m * c2;
-      l *= (double)alpha;
+      l *= alpha;
 #pragma unroll
       for (int j = 0; j < kHeadsPerLane; ++j) {
         // acc slot j holds head kHeadsPerLane qd + j; lane head * kParts has that head's alpha
-        const float alf = __shfl(alpha, (kHeadsPerLane * qd + j) * kParts, 64);
-        const double al = (double)alf;
+        const double al = __shfl(alpha, (kHeadsPerLane * qd + j) * kParts, 64);
+        const float alf = (float)al;  // the MFMA sums only hold products below 2^4
 #pragma unroll
         for (int nn = 0; nn < 8; ++nn) {
           acc[j][nn] *= al;
@@ -771,19 +855,100 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       }
     }
     // weights 2^((s - m) c2); a page seen before any finite score leaves m = -inf and mc2 = 0.
-    // Off the exact path every score that can matter has |s| <= kBigScore, so the running
-    // maximum is below kBigScore + kNegligible / c2 and the exponent, formed in fp32, is off by
-    // a few 1e-7 at most (an fp64 exponent is rounded to fp32 for the exp anyway).
+    // On the precise path in fp64 (w64, which the weight sum and the exact-value path take);
+    // p, their fp32 rounding, feeds the p.V MFMA, whose values all stay below 2^4.  Off it every
+    // score is insignificant and fp32 is plenty.
     float p[4];
+    double w64[4];
     if (exact) {
+      // the kParts lanes of a quad that share a head hold the same four scores: each takes the
+      // exp of 4 / kParts of them and the quad swaps the results
+      if constexpr (G == 4) {
+        const int x = t & 3;
+        const double e = exp2_neg(fma(x == 0 ? sd[0] : x == 1 ? sd[1] : x == 2 ? sd[2] : sd[3], c2, -mc2));
+        w64[0] = quad_pick<0, 0, 0, 0>(e);
+        w64[1] = quad_pick<1, 1, 1, 1>(e);
+        w64[2] = quad_pick<2, 2, 2, 2>(e);
+        w64[3] = quad_pick<3, 3, 3, 3>(e);
+      } else {
+        const bool x = t & 1;
+        const double e0 = exp2_neg(fma(x ? sd[1] : sd[0], c2, -mc2));
+        const double e1 = exp2_neg(fma(x ? sd[3] : sd[2], c2, -mc2));
+        w64[0] = quad_pick<0, 0, 2, 2>(e0);
+        w64[1] = quad_pick<1, 1, 3, 3>(e0);
+        w64[2] = quad_pick<0, 0, 2, 2>(e1);
+        w64[3] = quad_pick<1, 1, 3, 3>(e1);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f((float)fma(sd[i], c2, -mc2));
+      for (int i = 0; i < 4; ++i) p[i] = (float)w64[i];
+      l += (w64[0] + w64[1]) + (w64[2] + w64[3]);
     } else {
       const float mc2f = (float)mc2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2f, -mc2f));
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2f, -mc2f));
+        w64[i] = (double)p[i];
+      }
+      l += (double)((p[0] + p[1]) + (p[2] + p[3]));
     }
-    l += (double)((p[0] + p[1]) + (p[2] + p[3]));  // 4 values <= 1: fp32 to a few 1e-7
+    // Exact-value path: a lane's 8 values of row j holding a large value are added here, in
+    // fp64, by the lanes that own those output columns, and leave the MFMA operand.  Lane
+    // (t, qd) owns heads kHeadsPerLane qd + hh at head_dim vdim(n, t); the values of token
+    // qs + 4j at those dims sit in lane (t, qs), its weight for head i in lane (i kParts, qs).
+    // "Large" depends on the page's largest weight in the units of the final result: its heads'
+    // page maxima against a lower bound of their final maxima (the running maximum and the
+    // workgroup's of a few steps ago).  Once a far larger score has been seen, even outliers
+    // stay in the MFMA: the sums they enter are scaled down by at least that much later.
+    float wpage = 0.f;
+    {
+      const double mlb = fmax(m, (double)shared32);
+      const float pw = __builtin_amdgcn_exp2f((float)((pm - mlb) * c2));  // this lane's head, <= 1
+#pragma unroll
+      for (int i = 0; i < G; ++i)  // lane i kParts holds head i (a NaN from an empty page drops out)
+        wpage = fmaxf(wpage, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), i * kParts)));
+    }
+    const int we = (int)((__float_as_uint(wpage) >> 23) & 0xFFu) - 127;  // floor(log2), -127 for 0
+    const uint32_t vthr = (uint32_t)max((int)kLargeExp, 130 - we);  // wave-uniform
+    // (rows past the end of the page are zero by now)
+    const uint32_t vlarge = vthr <= 255u ? large_rows(vt, vthr) : 0u;
+    if (__any(vlarge != 0u)) {
+      uint64_t bw[4];     // bw[j]: lanes whose row j is large
+      uint32_t toks = 0;  // bit qs + 4j: token qs + 4j has a large chunk in some lane
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bw[j] = __ballot((vlarge >> j) & 1u);
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) toks |= ((bw[j] >> (16 * qs)) & 0xFFFFull) ? 1u << (qs + 4 * j) : 0u;
+      }
+      while (toks) {  // wave-uniform: one large token per iteration
+        const int tok = __builtin_ctz(toks);
+        toks &= toks - 1u;
+        const int j = tok >> 2, qs = tok & 3, src = t + 16 * qs;
+        const uint64_t bj = j == 0 ? bw[0] : j == 1 ? bw[1] : j == 2 ? bw[2] : bw[3];
+        const bool take = ((uint32_t)(bj >> (16 * qs)) >> t) & 1u;
+        const double wj = j == 0 ? w64[0] : j == 1 ? w64[1] : j == 2 ? w64[2] : w64[3];
+        double wgt[kHeadsPerLane];
+#pragma unroll
+        for (int hh = 0; hh < kHeadsPerLane; ++hh)
+          wgt[hh] = __shfl(wj, (kHeadsPerLane * qd + hh) * kParts + 16 * qs, 64);
+        const uint32_t sh = (j & 1) ? 0u : 16u;  // row 2q in the low halves, 2q + 1 in the high
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const uint32_t x = __shfl((j >> 1) ? vt[2 * n + 1] : vt[2 * n], src, 64);
+          if (take) acc[0][n] = fma(wgt[0], (double)__uint_as_float((x << sh) & 0xFFFF0000u), acc[0][n]);
+          if constexpr (kHeadsPerLane == 2)
+            if (take) acc[1][n] = fma(wgt[1], (double)__uint_as_float((x << sh) & 0xFFFF0000u), acc[1][n]);
+        }
+      }
+      // this lane's large chunks leave the MFMA operand
+      const uint32_t keep0 = ((vlarge & 1u) ? 0u : 0x0000FFFFu) | ((vlarge & 2u) ? 0u : 0xFFFF0000u);
+      const uint32_t keep1 = ((vlarge & 4u) ? 0u : 0x0000FFFFu) | ((vlarge & 8u) ? 0u : 0xFFFF0000u);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) {
+        vt[2 * nn] &= keep0;
+        vt[2 * nn + 1] &= keep1;
+      }
+    }
     // A operand: this lane's row carries one bf16 part of the weights, p = hi + mid + lo, all
     // three by truncation: hi = the top 8 significant bits of p, mid those of x1 = p - hi,
     // lo = x1 - mid (at most 8 bits left).  The differences are exact, so the three parts
@@ -851,13 +1016,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       if (lane < 16 && part == 0) lds_max_f64(gmax_at(n), m);
       lds_store_u32(prog_base + 4 * wave, (uint32_t)n + 1);
       uint32_t prog = lds_load_u32(prog_base + 4 * (lane & (kWaves - 1)));
-      if (n >= kShareLag) {
-        const uint32_t need = (uint32_t)(n - kShareLag) + 1;  // every wave past step n - lag
+      if (n > 0) {
+        // the workgroup's maximum over the pages before step n - lag; on the first steps lag 0
+        // (every wave has just published its first pages' maximum, and without it each wave
+        // would take its first pages on the precise path), then kShareLag
+        const int lag = n >= kShareLag ? kShareLag : 0;
+        const uint32_t need = (uint32_t)(n - lag) + 1;  // every wave past step n - lag
         while (!__all(prog >= need)) {
           __builtin_amdgcn_s_sleep(1);
           prog = lds_load_u32(prog_base + 4 * (lane & (kWaves - 1)));
         }
-        shared32 = (float)lds_load_f64(gmax_at(n - kShareLag));
+        shared32 = (float)lds_load_f64(gmax_at(n - lag));
       }
       if ((uint32_t)n + 1 > __builtin_amdgcn_readlane(prog, wave ^ 4)) __builtin_amdgcn_s_setprio(0);
       else __builtin_amdgcn_s_setprio(2);
@@ -1049,6 +1218,8 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   a.lens = q->seq_lens;
   a.q = qv;
   a.scale_log2e = (double)scale * kLog2e;
+  a.scale_log2e_f32 = (float)a.scale_log2e;
+  a.negl_f32 = (float)(kSigBits / a.scale_log2e);
   a.out = out;
   a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + 256);
   a.status = status;

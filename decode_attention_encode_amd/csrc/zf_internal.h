@@ -88,6 +88,13 @@ __device__ __forceinline__ uint32_t bitselect(uint32_t mask, uint32_t a, uint32_
   return r;
 }
 
+// Two 16-bit lanes at once (v_pk_max_u16).
+typedef unsigned short zf_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(zf_u16x2, a),
+                                                                __builtin_bit_cast(zf_u16x2, b)));
+}
+
 __device__ __forceinline__ void rebuild8(uint32_t s0, uint32_t s1, uint32_t nib, uint32_t hi,
                                          uint32_t base16, uint32_t out[4]) {
   const uint32_t xe = bitselect(0x0F0F0F0Fu, nib, hi << 4);  // e of values 0, 2, 4, 6

@@ -197,21 +197,48 @@ def max_sequences(kv_budget: int, layers: int, context: int, page_size: int, num
 
 
 def attention(raw_pages: np.ndarray, seq_lens, page_table, q: np.ndarray,
-              scale: float | None = None, want: np.ndarray | None = None):
-    """fp64 decode attention; returns (status, out f64[B][Hq][D])."""
+              scale: float | None = None, want: np.ndarray | None = None,
+              threads: int = 1, with_neff: bool = False):
+    """fp64 decode attention; returns (status, out f64[B][Hq][D]) or, with ``with_neff``,
+    (status, out, neff f64[B][Hq]) where neff is each row's effective number of tokens.
+
+    ``threads`` > 1 runs the unchanged C routine on disjoint slices of the wanted rows at once
+    (each call computes only its slice, selected through ``want``; ctypes releases the GIL), so
+    every row is computed exactly as a single call computes it."""
     P, H, two, T, D = raw_pages.shape
     B, Hq, Dq = q.shape
     assert two == 2 and Dq == D and Hq % H == 0
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = np.zeros((B, Hq, D), np.float64)
+    neff = np.zeros((B, Hq), np.float64)
     lens = np.ascontiguousarray(seq_lens, np.int32)
     pt = np.ascontiguousarray(page_table, np.int32)
-    wnt = None if want is None else np.ascontiguousarray(want, np.uint8)
+    pages = np.ascontiguousarray(raw_pages, np.uint16)
+    qq = np.ascontiguousarray(q, np.uint16)
+    wnt = np.ones((B, Hq), np.uint8) if want is None else np.ascontiguousarray(want, np.uint8)
     g = _Geom(P, T, H, D)
-    st = _load().orc_attention(ctypes.byref(g), ctypes.c_int32(B), ctypes.c_int32(Hq),
-                               _p(lens), _p(pt), ctypes.c_int32(pt.shape[1]),
-                               _p(np.ascontiguousarray(raw_pages, np.uint16)),
-                               _p(np.ascontiguousarray(q, np.uint16)), ctypes.c_double(scale),
-                               _p(wnt), _p(out))
-    return int(st), out
+    lib = _load()
+
+    def run(mask):
+        return int(lib.orc_attention(ctypes.byref(g), ctypes.c_int32(B), ctypes.c_int32(Hq),
+                                     _p(lens), _p(pt), ctypes.c_int32(pt.shape[1]), _p(pages),
+                                     _p(qq), ctypes.c_double(scale), _p(mask), _p(out),
+                                     _p(neff)))
+
+    rows = np.flatnonzero(wnt.reshape(-1))
+    if threads <= 1 or len(rows) < 2:
+        st = run(wnt)
+    else:
+        import concurrent.futures
+        masks = []
+        for part in np.array_split(rows, min(threads, len(rows))):
+            m = np.zeros(B * Hq, np.uint8)
+            m[part] = 1
+            masks.append(m.reshape(B, Hq))
+        with concurrent.futures.ThreadPoolExecutor(len(masks)) as ex:
+            sts = list(ex.map(run, masks))
+        st = 0
+        for x in sts:
+            st |= x
+    return (int(st), out, neff) if with_neff else (int(st), out)

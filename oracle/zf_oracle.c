@@ -282,7 +282,7 @@ static double bf16_value(uint16_t x) {
 uint32_t orc_attention(const orc_geom* g, int32_t batch, int32_t num_q_heads,
                        const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
                        const uint16_t* raw_pages, const uint16_t* q, double scale,
-                       const uint8_t* want, double* out) {
+                       const uint8_t* want, double* out, double* neff) {
   uint32_t st = check_rows(g, batch, seq_lens, page_table, max_pages, 0);
   if (st) return st;
   const int H = g->num_kv_heads, D = g->head_dim, T = g->page_size;
@@ -297,6 +297,7 @@ uint32_t orc_attention(const orc_geom* g, int32_t batch, int32_t num_q_heads,
       const uint16_t* qv = q + ((int64_t)b * num_q_heads + hq) * D;
       double* o = out + ((int64_t)b * num_q_heads + hq) * D;
       for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (neff) neff[(int64_t)b * num_q_heads + hq] = 0.0;
       const int L = seq_lens[b];
       if (L == 0) continue;
       /* scores s_t = scale * <q, k_t> */
@@ -310,15 +311,17 @@ uint32_t orc_attention(const orc_geom* g, int32_t batch, int32_t num_q_heads,
         if (s[t] > mx) mx = s[t];
       }
       /* softmax weights and the weighted sum of V */
-      double denom = 0.0;
+      double denom = 0.0, sq = 0.0;
       for (int t = 0; t < L; ++t) {
         double w = exp(s[t] - mx);
         denom += w;
+        sq += w * w;
         int64_t page = page_table[(int64_t)b * max_pages + t / T];
         const uint16_t* v = raw_pages + raw_index(g, page, hk, 1, t % T);
         for (int d = 0; d < D; ++d) o[d] += w * bf16_value(v[d]);
       }
       for (int d = 0; d < D; ++d) o[d] /= denom;
+      if (neff) neff[(int64_t)b * num_q_heads + hq] = denom * denom / sq;
     }
   free(s);
   return ORC_OK;

@@ -107,10 +107,13 @@ uint32_t orc_compact_spill(const orc_geom* g, orc_cache* c, int32_t batch,
 int64_t orc_max_sequences(int64_t kv_budget, int32_t layers, int32_t context, int32_t page_size,
                           int32_t num_kv_heads, int32_t head_dim, double raw_blocks_per_row);
 /* fp64 decode attention over raw bf16 pages; q u16[B][Hq][D]; out f64[B][Hq][D].
- * `want` (u8[B][Hq], may be NULL = all) selects which (sequence, q head) rows to compute. */
+ * `want` (u8[B][Hq], may be NULL = all) selects which (sequence, q head) rows to compute;
+ * rows not wanted are not written.  `neff` (f64[B][Hq], may be NULL) receives each computed
+ * row's effective number of tokens, (sum of weights)^2 / (sum of squared weights): 1 when one
+ * token takes all the weight, L when all L tokens weigh the same (0 for L = 0). */
 uint32_t orc_attention(const orc_geom* g, int32_t batch, int32_t num_q_heads,
                        const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
                        const uint16_t* raw_pages, const uint16_t* q, double scale,
-                       const uint8_t* want, double* out);
+                       const uint8_t* want, double* out, double* neff);
 
 #endif

@@ -41,7 +41,7 @@ class _Cfg(ctypes.Structure):
                 ("v_scale_lo", ctypes.c_double), ("v_scale_hi", ctypes.c_double),
                 ("p_outlier_block", ctypes.c_double), ("p_zero_value", ctypes.c_double),
                 ("p_wide_block", ctypes.c_double), ("pool_factor", ctypes.c_double),
-                ("seed", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("outlier_kinds", ctypes.c_int32)]
 
 
 _lib = None
@@ -78,6 +78,7 @@ class Workload:
     p_wide_block: float = 0.0
     pool_factor: float = 1.0
     seed: int = 0
+    outlier_kinds: int = 3  # outlier blocks in K (bit 0) and/or V (bit 1)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -87,7 +88,7 @@ class Workload:
                     self.page_size, self.ctx_min, self.ctx_max, self.extra_tokens,
                     self.k_scale[0], self.k_scale[1], self.v_scale[0], self.v_scale[1],
                     self.p_outlier_block, self.p_zero_value, self.p_wide_block,
-                    self.pool_factor, self.seed)
+                    self.pool_factor, self.seed, self.outlier_kinds)
 
 
 # The workloads (sizes, value distributions and page-table structure).

@@ -14,14 +14,12 @@
  * Value recipe for one element (K or V, sequence b, token t, kv head h, dim d):
  *   x  = N(0,1) * s[kv][h][d], rounded fp64 -> fp32 -> bf16 (round to nearest even),
  *        N(0,1) by the cosine branch of Box-Muller, s = exp(U(ln lo, ln hi)) per channel;
- *   wide blocks     (probability p_wide per 64-value block): x *= 2^k per value, k uniform in
- *                   [-12, 12] for K and in [-24, 0] for V;
- *   outlier blocks  (probability p_outlier per block): the value at one uniform position *= 2^10
- *                   for K (massive key activations) and *= 2^-10 for V;
+ *   wide blocks     (probability p_wide per 64-value block): x *= 2^k per value, k uniform
+ *                   integer in [-12, 12];
+ *   outlier blocks  (probability p_outlier per block, in K and/or V as outlier_kinds says): the
+ *                   value at one uniform position *= 2^10;
  *   zero values     (probability p_zero per value): x = +0.0.
- * V's perturbations scale values down: they widen a block's exponent spread exactly as far as
- * K's do (so the codec sees the same raw/compressed mix), while value magnitudes stay within
- * their channel scale.
+ * K and V are perturbed alike.
  * A 64-value block is 64 consecutive head_dim values of one (token, head, K-or-V).
  */
 #include <math.h>
@@ -45,6 +43,7 @@ typedef struct {
   double p_outlier_block, p_zero_value, p_wide_block;
   double pool_factor;            /* page pool size / pages needed (>= 1) */
   uint64_t seed;
+  int32_t outlier_kinds;         /* which tensors get outlier blocks: bit 0 K, bit 1 V */
 } synth_cfg;
 
 static inline uint64_t mix64(uint64_t z) {
@@ -104,12 +103,13 @@ static uint16_t element(const synth_cfg* c, int kv, int b, int t, int h, int d, 
   uint64_t s = c->seed;
   uint16_t x = f32_to_bf16_rne((float)(normal01(stream_key(s, ST_VALUE), eid) * scale));
   if (c->p_wide_block > 0 && uniform01(stream_key(s, ST_WIDE), bid) < c->p_wide_block) {
-    int k = (int)floor(uniform01(stream_key(s, ST_WIDE_K), eid) * 25.0) - (kv ? 24 : 12);
+    int k = (int)floor(uniform01(stream_key(s, ST_WIDE_K), eid) * 25.0) - 12;
     x = f32_to_bf16_rne(ldexpf(bf16_to_f32(x), k));
   }
-  if (c->p_outlier_block > 0 && uniform01(stream_key(s, ST_OUT), bid) < c->p_outlier_block) {
+  if (c->p_outlier_block > 0 && ((c->outlier_kinds >> kv) & 1) &&
+      uniform01(stream_key(s, ST_OUT), bid) < c->p_outlier_block) {
     int pos = (int)floor(uniform01(stream_key(s, ST_OUT_POS), bid) * 64.0);
-    if ((d & 63) == pos) x = f32_to_bf16_rne(bf16_to_f32(x) * (kv ? 0x1.0p-10f : 1024.0f));
+    if ((d & 63) == pos) x = f32_to_bf16_rne(bf16_to_f32(x) * 1024.0f);
   }
   if (c->p_zero_value > 0 && uniform01(stream_key(s, ST_ZERO), eid) < c->p_zero_value) x = 0;
   return x;

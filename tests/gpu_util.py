@@ -11,6 +11,12 @@ import oracle
 import synth
 
 
+def attention_scale(head_dim: int) -> float:
+    """1/sqrt(head_dim) as the C ABI carries it (an fp32 argument): the oracle is handed the
+    same value, so both sides compute the definition with the same scale."""
+    return float(np.float32(1.0 / np.sqrt(head_dim)))
+
+
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
@@ -71,7 +77,7 @@ class Setup:
         if ws is None:
             ws = zf.attention_workspace(w.batch, w.num_kv_heads, q.shape[1], w.head_dim,
                                         self.seqs.max_seq_len)
-        scale = 1.0 / float(np.sqrt(w.head_dim))
+        scale = attention_scale(w.head_dim)
         if packed:
             zf.zf_decode_attention(self.cache, self.seqs, qd, scale, out, ws)
         else:

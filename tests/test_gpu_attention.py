@@ -1,10 +1,17 @@
 """GPU parity for the fused compressed decode attention (zf_decode_attention) and its
 uncompressed twin (zf_decode_attention_raw), through the C ABI.
 
-Tolerance: fp32 output within max |err| <= 1e-3 of the fp64 oracle (the bound set for this
-path).  The compressed path must equal the twin bit for bit (same kernel, same split plan;
-the compressed loader rebuilds exactly the bf16 bits the twin reads), must not depend on
-where pages sit physically, and must repeat bitwise.
+Tolerance: the fp32 output within max(1e-3, half an fp32 ulp of |ref|) of the fp64 oracle,
+plus 2^-30 |ref| for the fp64 rounding of the oracle itself.  A correctly rounded fp32 result
+is within half an ulp, and that is below 1e-3 for every |ref| < 2^15, so there the plain 1e-3
+is asserted on its own as well (no element over 1e-3 below 32768).  The compressed path must
+equal the twin bit for bit (same kernel, same split plan; the compressed loader rebuilds
+exactly the bf16 bits the twin reads), must not depend on where pages sit physically, and must
+repeat bitwise.
+
+Inputs: the workloads' stated value distributions (K and V outliers x2^10, wide blocks
+x2^U[-12,12]), which make most rows one-hot, plus full-size diffuse-softmax cases (K outliers
+removed) whose median effective token count, computed by the oracle, is asserted >= 100.
 
 Attention: page "Open Weights: from files to tokens / second", section "03 / The inference
 loop" (decode step over the KV cache);
@@ -20,19 +27,21 @@ import torch
 import decode_attention_encode_amd as zf
 import oracle
 import synth
-from gpu_util import Setup, dev, host, log
+from gpu_util import Setup, attention_scale, dev, host, log
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
-# Beyond |out| = 2^12 the fp32 spacing alone approaches the absolute bound (half an ulp is
-# 9.8e-4 at 2^14 and 2e-3 at 2^15), so there the bound becomes two fp32 ulps of the exact
-# value; below 4194 it is the plain 1e-3.  The strict 1e-3 count is logged either way.
-ULP2 = 2.0 ** -22
+STRICT_BELOW = 2.0 ** 15  # half an fp32 ulp stays below 1e-3 up to here
+ORACLE_REL = 2.0 ** -30   # fp64 rounding of the oracle's own sums, relative (generous)
+ORACLE_THREADS = 16
 
 
 def tolerance(ref):
-    return np.maximum(TOL, ULP2 * np.abs(ref))
+    """max(1e-3, half an fp32 ulp of |ref|) + 2^-30 |ref|."""
+    a = np.abs(ref)
+    _, e = np.frexp(a)  # a = m 2^e, m in [0.5, 1): fp32 spacing there is 2^(e - 24)
+    return np.maximum(TOL, np.ldexp(1.0, e - 25) + ORACLE_REL * a)
 
 
 SMALL = synth.WORKLOADS[0].replace(name="ragged_small", batch=5, ctx_min=1, ctx_max=300,
@@ -52,9 +61,22 @@ SMALL_H2G8 = SMALL.replace(name="ragged_small_h2_gqa8", num_kv_heads=2, num_q_he
 WIDE_B300 = SMALL.replace(name="ragged_b300_ctx1_120", batch=300, ctx_min=1, ctx_max=120, seed=27)
 
 
+# Diffuse softmax at full size: the batch-32 decode step without outlier keys (V outliers kept,
+# or no outliers at all), and the long-context split case without outlier keys (K scale as the
+# batch-32 workload's, [0.25, 4]: with [0.25, 8] the median effective token count is ~73).
+DIFFUSE1 = synth.WORKLOADS[1].replace(name="diffuse_b32_ctx4096_v_outliers", outlier_kinds=2, seed=41)
+DIFFUSE1_PLAIN = synth.WORKLOADS[1].replace(name="diffuse_b32_ctx4096_no_outliers",
+                                            p_outlier_block=0.0, seed=42)
+DIFFUSE2 = synth.WORKLOADS[2].replace(name="diffuse_b16_ctx32768_v_outliers", k_scale=(0.25, 4.0),
+                                      outlier_kinds=2, seed=43)
+DIFFUSE8 = synth.WORKLOADS[5].replace(name="diffuse_gqa8_b32_ctx4096_v_outliers", outlier_kinds=2,
+                                      seed=44)
+
+
 def workload(key):
     named = {"small": SMALL, "small8": SMALL8, "split8": SPLIT8, "h4": SMALL_H4, "h2g8": SMALL_H2G8,
-             "b300": WIDE_B300}
+             "b300": WIDE_B300, "diffuse1": DIFFUSE1, "diffuse1_plain": DIFFUSE1_PLAIN,
+             "diffuse2": DIFFUSE2, "diffuse8": DIFFUSE8}
     return named.get(key) or synth.WORKLOADS[key]
 
 
@@ -83,30 +105,38 @@ def decode_step(s, inst, lens, step):
     return synth.query(inst.w, step)
 
 
-def check(got, inst, lens, q, want=None, what=""):
-    st, ref = oracle.attention(inst.raw_pages, lens, inst.page_table, q, want=want)
+def check(got, inst, lens, q, want=None, what="", min_median_neff=None):
+    st, ref, neff = oracle.attention(inst.raw_pages, lens, inst.page_table, q,
+                                     scale=attention_scale(inst.w.head_dim), want=want,
+                                     threads=ORACLE_THREADS, with_neff=True)
     assert st == 0
     g = host(got)
     if want is not None:
         sel = want.astype(bool)
-        g, ref = g[sel], ref[sel]
+        g, ref, neff = g[sel], ref[sel], neff[sel]
     err = np.abs(g.astype(np.float64) - ref)
     big = np.abs(ref) > 1e-3
     rel = err[big] / np.abs(ref[big]) if big.any() else np.zeros(1)
-    strict = int(np.count_nonzero(err > TOL))
+    over = err > TOL
+    strict = int(np.count_nonzero(over & (np.abs(ref) < STRICT_BELOW)))
+    # error in fp32 ulps of the exact value where the bar is a few ulps (|ref| >= 1024); a
+    # correctly rounded result is within 0.5
+    large = np.abs(ref) >= 1024.0
+    _, e = np.frexp(np.abs(ref[large]))
+    ulps = float((err[large] / np.ldexp(1.0, e - 24)).max()) if large.any() else 0.0
+    live = neff[neff > 0]
+    med = float(np.median(live)) if live.size else 0.0
     log(f"  {what}: max|err| {err.max():.3e}  max|ref| {np.abs(ref).max():.3e}  "
-        f"max rel {rel.max():.3e}  elements over 1e-3: {strict}"
-        + (f" (smallest |ref| among them {np.abs(ref[err > TOL]).min():.3e})" if strict else ""))
+        f"max rel {rel.max():.3e}  max {ulps:.2f} fp32 ulps at |ref| >= 1024  elements over 1e-3: {int(over.sum())} "
+        f"(below 32768: {strict})  median effective tokens {med:.1f}"
+        + (f" (smallest |ref| over 1e-3 {np.abs(ref[over]).min():.3e})" if over.any() else ""))
     assert np.isfinite(g).all()
+    assert strict == 0, f"{what}: {strict} outputs below 32768 off by more than 1e-3"
     bad = err > tolerance(ref)
     assert not bad.any(), f"{what}: {bad.sum()} outputs beyond tolerance, max abs error {err.max()}"
-
-
-def sample_want(rng, B, Hq, n):
-    want = np.zeros((B, Hq), np.uint8)
-    idx = rng.choice(B * Hq, size=min(n, B * Hq), replace=False)
-    want.reshape(-1)[idx] = 1
-    return want
+    if min_median_neff is not None:
+        assert med >= min_median_neff, f"{what}: median effective token count {med:.1f}"
+    return err
 
 
 @pytest.mark.parametrize("key", [0, "small", 1, 2, "small8", 5, "split8", "h4", "h2g8", "b300"])
@@ -127,36 +157,56 @@ def test_attention_full(key):
     assert torch.equal(out, twin), "compressed and raw twin differ"
 
 
-def test_attention_ragged_sampled():
+@pytest.mark.parametrize("key", ["diffuse1", "diffuse1_plain", "diffuse2", "diffuse8"])
+@pytest.mark.timeout(600)
+def test_attention_diffuse_full(key):
+    """Every head at full size with a diffuse softmax (hundreds of tokens sharing the weight):
+    the long p.V sums, the rescales across pages and, for the 32k case, the merge of splits
+    with comparable partials all carry the result."""
+    w = workload(key)
+    log(f"attention parity, diffuse softmax (all heads): workload {w.name}")
+    inst = synth.make(w)
+    s = Setup(inst)
+    lens = inst.seq_lens.copy()
+    q = decode_step(s, inst, lens, 0) if w.extra_tokens else synth.query(w, 0)
+    out = s.attention(q)
+    assert s.status() == 0
+    check(out, inst, lens, q, what=w.name, min_median_neff=100.0)
+    assert torch.equal(out, s.attention(q, packed=False)), "compressed and raw twin differ"
+
+
+@pytest.mark.timeout(600)
+def test_attention_ragged_full():
     w = synth.WORKLOADS[3]
-    log(f"attention parity (sampled heads): workload {w.name}")
+    log(f"attention parity (all heads): workload {w.name}")
     inst = synth.make(w)
     s = Setup(inst)
     lens = inst.seq_lens.copy()
     q = synth.query(w, 0)
     out = s.attention(q)
     assert s.status() == 0
-    want = sample_want(np.random.default_rng(3), w.batch, w.num_q_heads, 96)
-    check(out, inst, lens, q, want=want, what=w.name)
+    check(out, inst, lens, q, what=w.name)
     assert torch.equal(out, s.attention(q, packed=False))
 
 
-def test_attention_maxcap_64_steps_sampled():
+@pytest.mark.timeout(1200)
+def test_attention_maxcap_64_steps_full():
+    """The 128k workload: 64 decode steps, each appending one token per sequence and attending
+    over the grown cache; every output of every step against the oracle."""
     w = synth.WORKLOADS[4]
-    log(f"attention parity over 64 decode steps (sampled): workload {w.name}")
+    log(f"attention parity over 64 decode steps (all heads, every step): workload {w.name}")
     inst = synth.make(w)
     s = Setup(inst)
     lens = inst.seq_lens.copy()
-    rng = np.random.default_rng(4)
     ws = zf.attention_workspace(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim,
                                 s.seqs.max_seq_len)
+    worst = 0.0
     for step in range(64):
         q = decode_step(s, inst, lens, step)
         out = s.attention(q, ws=ws)
-        if step in (0, 31, 63):
-            assert s.status() == 0
-            check(out, inst, lens, q, want=sample_want(rng, w.batch, w.num_q_heads, 6),
-                  what=f"{w.name} step {step}")
+        assert s.status() == 0
+        worst = max(worst, float(check(out, inst, lens, q, what=f"{w.name} step {step}").max()))
+    log(f"  {w.name}: largest error over the 64 steps {worst:.3e}")
     assert np.array_equal(host(s.seqs.seq_lens), lens)
 
 

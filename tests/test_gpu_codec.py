@@ -36,7 +36,7 @@ def test_encode_bitexact(key):
     log(f"  raw blocks {orc.spill_top} of {int(inst.seq_lens.sum()) * 32}")
 
 
-@pytest.mark.parametrize("key", [0, "small", 1, 4])
+@pytest.mark.parametrize("key", [0, "small", 1, 2, 3, 4])
 def test_decode_roundtrip(key):
     w = workload(key)
     log(f"decode round trip: workload {w.name}")

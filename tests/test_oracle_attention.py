@@ -170,3 +170,51 @@ def test_want_mask_computes_only_selected_rows():
     _, part = oracle.attention(raw, lens, pt, q, want=want)
     assert np.array_equal(part[0, 1], full[0, 1]) and np.array_equal(part[0, 3], full[0, 3])
     assert not part[0, 0].any() and not part[0, 2].any()
+
+
+def test_effective_token_count_closed_forms():
+    """neff = (sum w)^2 / sum w^2: 1 for a dominating logit, L for equal keys, and for two
+    tokens with logit gap d, (1 + e^d)^2 / (1 + e^(2d))."""
+    rng = np.random.default_rng(10)
+    D, T = 64, 16
+    lens = np.array([37, 40], np.int32)
+    pt, raw, _ = make_cache(rng, 2, 1, D, T, lens)
+    for t in range(37):  # sequence 0: every key equal
+        raw[pt[0, t // T], 0, 0, t % T] = raw[pt[0, 0], 0, 0, 0]
+    hot = 23             # sequence 1: one key 2048 logits above the rest on dim 5
+    raw[pt[1, hot // T], 0, 0, hot % T, :] = 0
+    raw[pt[1, hot // T], 0, 0, hot % T, 5] = bits(2.0 ** 14)
+    q = bits(rng.standard_normal((2, 1, D)))
+    q[1, 0, :] = 0
+    q[1, 0, 5] = bits(1.0)
+    st, _, neff = oracle.attention(raw, lens, pt, q, with_neff=True)
+    assert st == 0
+    np.testing.assert_allclose(neff[0, 0], 37.0, rtol=1e-13)
+    assert neff[1, 0] == 1.0
+    # two tokens: the scale-pinning case above
+    pt2 = np.array([[0]], np.int32)
+    raw2 = np.zeros((1, 1, 2, T, 128), np.uint16)
+    q2 = np.zeros((1, 1, 128), np.float32)
+    q2[0, 0, :4] = [1.0, 2.0, -1.0, 0.5]
+    raw2[0, 0, 0, 0, :4] = bits([0.5, 0.25, 0.0, 1.0])
+    raw2[0, 0, 0, 1, :4] = bits([2.0, 1.0, -1.0, 2.0])
+    _, _, n2 = oracle.attention(raw2, np.array([2], np.int32), pt2, bits(q2), with_neff=True)
+    d = (6.0 - 1.5) / math.sqrt(128.0)
+    np.testing.assert_allclose(n2[0, 0], (1 + math.exp(d)) ** 2 / (1 + math.exp(2 * d)), rtol=1e-14)
+    _, _, n0 = oracle.attention(raw, np.array([0, 40], np.int32), pt, q, with_neff=True)
+    assert n0[0, 0] == 0.0
+
+
+def test_threaded_slices_equal_one_call_bit_for_bit():
+    rng = np.random.default_rng(11)
+    B, H, G, D, T = 5, 2, 4, 64, 16
+    lens = rng.integers(0, 90, B).astype(np.int32)
+    pt, raw, _ = make_cache(rng, B, H, D, T, np.maximum(lens, 1))
+    q = bits(rng.standard_normal((B, H * G, D)))
+    _, one, n1 = oracle.attention(raw, lens, pt, q, with_neff=True)
+    _, many, n2 = oracle.attention(raw, lens, pt, q, threads=7, with_neff=True)
+    assert np.array_equal(one, many) and np.array_equal(n1, n2)
+    want = (rng.random((B, H * G)) < 0.5).astype(np.uint8)
+    _, part = oracle.attention(raw, lens, pt, q, want=want, threads=3)
+    sel = want.astype(bool)
+    assert np.array_equal(part[sel], one[sel]) and not part[~sel].any()
