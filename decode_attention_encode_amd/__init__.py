@@ -17,13 +17,15 @@ import torch  # loads the HIP runtime the library binds to
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzf.so")
 
-ZF_OK, ZF_EINVAL, ZF_EUNSUPPORTED, ZF_EHIP, ZF_EWORKSPACE = 0, 1, 2, 3, 4
+ZF_OK, ZF_EINVAL, ZF_EUNSUPPORTED, ZF_EHIP, ZF_EWORKSPACE, ZF_ESCRATCH = 0, 1, 2, 3, 4, 5
+ZF_NOALLOC_SCRATCH_BYTES = 16 << 20
 ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN, ZF_DEV_ESYNC = 1, 2, 4, 8
 ZF_APPEND_SYNC_WORDS = 65  # hand-over words of the one-launch append (64) and its epoch
 
 EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_append_kv",
            "zf_append_kv_n", "zf_compact_spill", "zf_compact_workspace_bytes", "zf_max_sequences",
-           "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_raw",
+           "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_noalloc",
+           "zf_decode_attention_raw",
            "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
            "zf_stream_read_probe", "zf_set_append_wait_polls", "zf_get_status", "zf_status_str")
 ZF_PROBE_BLOCKS = 4096
@@ -77,6 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                               ctypes.c_double]),
         "zf_decode_kv": (ctypes.c_int, [pc, ps, vp, vp]),
         "zf_decode_attention": (ctypes.c_int, [pc, ps, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
+        "zf_decode_attention_noalloc": (ctypes.c_int, [pc, ps, vp, i32, ctypes.c_float, vp, vp]),
         "zf_decode_attention_raw": (ctypes.c_int, [vp, i32, i32, i32, i32, ps, vp, i32,
                                                    ctypes.c_float, vp, vp, sz, vp, vp]),
         "zf_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -240,6 +243,14 @@ def zf_decode_attention(cache: PackedCache, seqs: Seqs, q: torch.Tensor, scale: 
                                       q.shape[1], scale, _ptr(out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "zf_decode_attention")
+
+
+def zf_decode_attention_noalloc(cache: PackedCache, seqs: Seqs, q: torch.Tensor, scale: float,
+                                out: torch.Tensor, stream=None) -> None:
+    """zf_decode_attention with the library's fixed scratch instead of a workspace."""
+    _check(load().zf_decode_attention_noalloc(ctypes.byref(cache.c()), ctypes.byref(seqs.c()),
+                                              _ptr(q), q.shape[1], scale, _ptr(out),
+                                              _stream(stream)), "zf_decode_attention_noalloc")
 
 
 def zf_decode_attention_raw(raw_pages: torch.Tensor, seqs: Seqs, q: torch.Tensor, scale: float,

@@ -21,6 +21,7 @@ hipError_t launch_attention_raw(const uint16_t*, int32_t, int32_t, const zf_seqs
                                 const uint16_t*, int32_t, float, float*, void*, uint32_t*,
                                 hipStream_t);
 size_t attention_workspace_bytes(int32_t, int32_t, int32_t, int32_t);
+hipError_t scratch_address(void**);
 hipError_t launch_fill_zero(void*, size_t, hipStream_t);
 void set_attention_timing(hipEvent_t, hipEvent_t);
 }  // namespace zf
@@ -232,6 +233,29 @@ zf_status zf_decode_attention(const zf_cache* cache, const zf_seqs* seqs, const 
                                                 static_cast<hipStream_t>(stream)));
 }
 
+zf_status zf_decode_attention_noalloc(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* q,
+                                      int32_t num_q_heads, float scale, float* out,
+                                      zf_stream_t stream) {
+  zf_status s = check_cache(cache);
+  if (s != ZF_OK) return s;
+  if ((s = check_seqs(seqs, cache->page_size)) != ZF_OK) return s;
+  if ((s = check_attention_shape(cache->page_size, cache->num_kv_heads, cache->head_dim,
+                                 num_q_heads)) != ZF_OK)
+    return s;
+  if (cache->spill_slots > kMaxAttentionSpillSlots) return ZF_EUNSUPPORTED;
+  if (seqs->batch == 0) return ZF_OK;
+  if (!aligned(q) || !aligned(out)) return ZF_EINVAL;
+  if (seqs->max_seq_len > kMaxAttentionLen) return ZF_EUNSUPPORTED;
+  const size_t need = zf::attention_workspace_bytes(seqs->batch, cache->num_kv_heads,
+                                                    num_q_heads / cache->num_kv_heads,
+                                                    seqs->max_seq_len);
+  if (need > ZF_NOALLOC_SCRATCH_BYTES) return ZF_ESCRATCH;
+  void* ws = nullptr;
+  if (zf::scratch_address(&ws) != hipSuccess) return ZF_EHIP;
+  return hip_status(zf::launch_attention_packed(cache, seqs, q, num_q_heads, scale, out, ws,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 zf_status zf_decode_attention_raw(const uint16_t* raw_pages, int32_t num_pages,
                                   int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
                                   const zf_seqs* seqs, const uint16_t* q, int32_t num_q_heads,
@@ -272,6 +296,7 @@ const char* zf_status_str(zf_status s) {
     case ZF_EUNSUPPORTED: return "unsupported shape";
     case ZF_EHIP: return "HIP runtime error";
     case ZF_EWORKSPACE: return "workspace missing or too small";
+    case ZF_ESCRATCH: return "the call needs more than the fixed scratch area (ZF_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

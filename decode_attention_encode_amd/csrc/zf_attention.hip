@@ -37,6 +37,7 @@
 // One kernel body serves the packed cache and raw bf16 pages (the uncompressed twin): both
 // loaders hand the same bf16 pairs to the same arithmetic, so the outputs match bit for bit.
 #include <algorithm>
+#include <mutex>
 #include <hip/hip_ext.h>
 
 #include "zf_internal.h"
@@ -1254,6 +1255,35 @@ hipError_t launch_attention_packed(const zf_cache* c, const zf_seqs* q, const ui
   const uint32_t spill_bytes = (uint32_t)(c->spill_slots * 32);  // validated below 2^32
   PackedLoader ld{c->sm, c->nib, c->base, c->row_flags, c->row_spill, spill, spill_bytes};
   return launch_g(ld, c->num_pages, c->num_kv_heads, Hq, q, qv, scale, out, ws, c->status, st);
+}
+
+// ---------------------------------------------------------------- allocation-free scratch
+
+// The split partials of zf_decode_attention_noalloc live here instead of in a caller's
+// workspace: one array per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, so its device address is looked up once per device
+// and only that address is handed to kernels.  Calls on one device share the array.
+static __device__ __align__(256) unsigned char scratch[ZF_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attention_raw(const uint16_t* pages, int32_t num_pages, int32_t H,

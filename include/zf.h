@@ -66,7 +66,9 @@ typedef enum {
   ZF_EINVAL = 1,        /* bad argument (null or misaligned pointer, bad sizes)        */
   ZF_EUNSUPPORTED = 2,  /* valid but outside what the kernels implement                */
   ZF_EHIP = 3,          /* a HIP runtime call failed                                   */
-  ZF_EWORKSPACE = 4     /* workspace missing or smaller than the matching _bytes query */
+  ZF_EWORKSPACE = 4,    /* workspace missing or smaller than the matching _bytes query */
+  ZF_ESCRATCH = 5       /* zf_decode_attention_noalloc: the call's split partials need more
+                           than ZF_NOALLOC_SCRATCH_BYTES                                   */
 } zf_status;
 
 #define ZF_DEV_ESPILL 1u  /* spill pool exhausted: the call wrote no spill, kept spill_top */
@@ -197,6 +199,21 @@ zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw
 zf_status zf_decode_attention(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* q,
                               int32_t num_q_heads, float scale, float* out, void* workspace,
                               size_t workspace_bytes, zf_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): zf_decode_attention without a workspace argument.
+ * The split partials live in a fixed device array inside the library, ZF_NOALLOC_SCRATCH_BYTES
+ * per GPU (set up when the library's code is loaded on that GPU, held until the process ends);
+ * the call itself allocates nothing.  Every call on one GPU uses that GPU's array, so calls that
+ * overlap on one GPU (other streams, other threads) race: order them, as appends to one cache
+ * are ordered anyway.  The partials are written before they are read, so the array's contents
+ * from an earlier call never matter.  A shape whose partials need more than the array
+ * (zf_attention_workspace_bytes(...) > ZF_NOALLOC_SCRATCH_BYTES) returns ZF_ESCRATCH and
+ * enqueues nothing; other errors and the result are those of zf_decode_attention. */
+#define ZF_NOALLOC_SCRATCH_BYTES (16u << 20)
+zf_status zf_decode_attention_noalloc(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* q,
+                                      int32_t num_q_heads, float scale, float* out,
+                                      zf_stream_t stream);
 
 /* The same attention kernel reading an uncompressed bf16 cache; same split plan and
  * arithmetic, so its output is bitwise identical to zf_decode_attention on the encoded copy
