@@ -11,14 +11,15 @@ sequence, 16-token pages in random order, synthetic bf16 K/V (seeded generator; 
 weights exist here).  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  `value` = tokens/s of the whole job (sequences x steps / time), one
-layer.  `roofline` prices the attention kernel (the dominant one) against HBM: algorithmic
-bytes per launch (packed planes of the attended rows, spill slots of their raw blocks, q, out,
-page table and lengths) / its mean duration from HIP events on the launch stream, stamped at
-the kernel's own start and end (zf_time_next_attention: the interval a kernel trace reports) on
-every 8th timed step (a stamped launch pays ~8 us more dispatch, so `value` would be understated
-if every step carried the stamps); the call time with dispatch overhead is reported beside it.
-`cpu_baseline` times the CPU oracle (plain C, one thread) on a bounded sample of the same
-steps.
+layer, from the K timed steps, none of which carries a timing stamp.  `roofline` prices the
+attention kernel (the dominant one) against HBM: algorithmic bytes per launch (packed planes of
+the attended rows, spill slots of their raw blocks, q, out, page table and lengths) / its mean
+duration from HIP events on the launch stream, stamped at the kernel's own start and end
+(zf_time_next_attention: the interval a kernel trace reports) in a separate pass of at least 60
+further decode steps after the timed ones (a stamped launch pays ~8 us more dispatch, so the
+timed steps carry no stamps).  Before the warm-up steps, attention calls alone (which change no
+state) bring the GPU to its working clock.  `cpu_baseline` times the CPU oracle (plain C) on all
+host cores on a bounded sample of the same steps; the one-core rate is in `extra`.
 """
 from __future__ import annotations
 
@@ -51,16 +52,16 @@ def attn_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-STAMP_EVERY = 8  # timed steps per kernel-stamped step
+STAMPED_STEPS = 60    # decode steps of the stamped pass (kernel start / end) after the timed ones
+CLOCK_WARMUP_MS = 30  # attention calls alone before the warm-up steps: an idle MI355X needs
+                      # ~10 ms of load to reach its working clock
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=150)
-    ap.add_argument("--warmup", type=int, default=150,
-                    help="untimed steps first: an idle MI355X needs ~10 ms of load to reach "
-                         "its working clock (the first ms run ~15 %% slower)")
+    ap.add_argument("--warmup", type=int, default=150, help="untimed decode steps first")
     ap.add_argument("--layers", type=int, default=3,
                     help="layer caches the steps rotate over (1.35 GB at 3, beyond the 256 MB "
                          "last-level cache, as in a multi-layer model)")
@@ -70,14 +71,22 @@ def parse():
                     help="also time the raw twin, a cache-flushed attention, encode and decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("OUT", "FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
+                                                       "CAL_WRITE_DIR"),
+                    help="only summarize rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (of this "
+                         "bench and of --calibrate-copy) into OUT (JSON) and exit")
     ap.add_argument("--per-config", default="",
                     help="only time the attention call on these workloads (e.g. 1,2,3,4: the "
-                         "parity configurations), one JSON line each, and exit")
+                         "parity configurations; d1, d2, d8: their diffuse-softmax forms), one "
+                         "JSON line each, and exit")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X and is not "
               "sharded across GPUs (run with --gpus 1)", file=sys.stderr)
@@ -104,22 +113,23 @@ def main():
                           "launches": 3}))
         return
     if args.per_config:
-        for wi in [int(x) for x in args.per_config.split(",")]:
-            print(json.dumps(per_config(torch, zf, synth, wi, dev)), flush=True)
+        for key in args.per_config.split(","):
+            print(json.dumps(per_config(torch, zf, synth, key, dev)), flush=True)
         return
 
-    W, K = args.warmup, args.steps
+    W, K, KS = args.warmup, args.steps, STAMPED_STEPS
     NL = max(1, args.layers)
-    w = synth.WORKLOADS[WORKLOAD].replace(extra_tokens=(W + K + NL - 1) // NL + 1)
+    NS = W + K + KS  # decode steps in all
+    w = synth.WORKLOADS[WORKLOAD].replace(extra_tokens=(NS + NL - 1) // NL + 1)
     t0 = time.time()
     inst = synth.make(w)
     B, H, Hq, D, T = w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.page_size
     lens0 = inst.seq_lens.copy()
     to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
     # step s works on layer s % NL; per layer the sequences grow by one token per visit
-    visits = [(s // NL) for s in range(W + K)]  # appends this layer has seen before step s
+    visits = [(s // NL) for s in range(NS)]  # appends this layer has seen before step s
     ks, vs, qs = [], [], []
-    for s in range(W + K):
+    for s in range(NS):
         k, v = synth.tokens(w, lens0 + visits[s])
         ks.append(k)
         vs.append(v)
@@ -147,7 +157,7 @@ def main():
     rows0 = int(lens0.sum())
     ws = zf.attention_workspace(B, H, Hq, D, max_len, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    scale = 1.0 / math.sqrt(D)
+    scale = fp32_scale(D)
     stream = torch.cuda.current_stream()
 
     def step(s, ev=None):
@@ -160,28 +170,39 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    # clock warm-up: attention calls alone (no state changes) for CLOCK_WARMUP_MS
+    t0 = time.perf_counter()
+    warm_calls = 0
+    while time.perf_counter() - t0 < CLOCK_WARMUP_MS / 1e3 or warm_calls < 50:
+        for _ in range(10):
+            cache, seqs = layers[warm_calls % NL]
+            zf.zf_decode_attention(cache, seqs, q_dev[0], scale, out, ws)
+            warm_calls += 1
+        torch.cuda.synchronize()
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
-    # every STAMP_EVERY-th timed step: kernel start / end (device timestamps of the dispatch)
-    # and call start / end.  A stamped launch costs ~8 us of dispatch, so only a sample of the
-    # timed steps carries the stamps.
-    sampled = [i for i in range(K) if i % STAMP_EVERY == 0]
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in sampled]
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(W + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    # the stamped pass: KS more decode steps, each with kernel start / end (device timestamps
+    # of the dispatch) and call start / end
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(KS)]
     for ev in evs:
         for e in ev:
             e.record(stream)  # creates the events on the device
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(K):
-        step(W + i, evs[i // STAMP_EVERY] if i % STAMP_EVERY == 0 else None)
+    for i in range(KS):
+        step(W + K + i, evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
     for cache, _ in layers:
         status = zf.zf_get_status(cache.status)
         assert status == 0, f"device status {status}"
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])   # kernel execution
     call_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])   # call, dispatch included
+    stamped = [W + K + i for i in range(KS)]
 
     # ---- algorithmic bytes of each timed attention launch
     pt = inst.page_table
@@ -189,7 +210,7 @@ def main():
     flags = [c.row_flags.cpu().numpy().view(np.uint32) for c, _ in layers]
     raw_after = []  # raw blocks in the attended layer right after step s's append
     seen = [top0] * NL
-    for s in range(W + K):
+    for s in range(NS):
         lay = s % NL
         pos = lens0 + visits[s]
         pages = pt[np.arange(B), pos // T]
@@ -197,18 +218,17 @@ def main():
         seen[lay] += sum(bin(int(x)).count("1") for x in f)
         raw_after.append(seen[lay])
     attn_bytes = []
-    tokens_attended = 0
-    for i in range(K):
-        s = W + i
+    tokens_attended = []
+    for s in stamped:
         L = lens0 + visits[s] + 1
-        tokens_attended += int(L.sum())
+        tokens_attended.append(int(L.sum()))
         nbytes = int(L.sum()) * row_bytes + 32 * int(raw_after[s])
         nbytes += B * Hq * D * (2 + 4) + int(np.ceil(L / T).sum()) * 4 + B * 4
         attn_bytes.append(nbytes)
     attn_bytes = np.array(attn_bytes, np.float64)
     mean_attn_s = attn_ms.mean() / 1e3
-    achieved = attn_bytes[sampled].mean() / mean_attn_s / 1e9  # bytes of the stamped launches
-    uncompressed_eq = tokens_attended / K * H * 2 * D * 2 / mean_attn_s / 1e9
+    achieved = attn_bytes.mean() / mean_attn_s / 1e9  # bytes of the stamped launches
+    uncompressed_eq = np.mean(tokens_attended) * H * 2 * D * 2 / mean_attn_s / 1e9
     packed_valid = rows0 * row_bytes + 32 * top0
     ratio = packed_valid / (rows0 * H * 2 * D * 2)
 
@@ -220,8 +240,10 @@ def main():
 
     extra = {
         "layers_rotated": NL,
+        "clock_warmup_attention_calls": warm_calls,
         "attention_kernel_us_mean": round(attn_ms.mean() * 1e3, 2),
-        "attention_launches_stamped": len(sampled),
+        "attention_kernel_us_median": round(float(np.median(attn_ms)) * 1e3, 2),
+        "attention_launches_stamped": KS,
         "attention_kernel_us_min": round(attn_ms.min() * 1e3, 2),
         "attention_call_us_mean": round(call_ms.mean() * 1e3, 2),
         "attention_bytes_per_launch": int(attn_bytes.mean()),
@@ -232,14 +254,18 @@ def main():
     }
 
     if args.extras:
-        extra.update(extras(torch, zf, inst, layers, raw, q_dev[W + K - 1], ws, out, scale,
+        extra.update(extras(torch, zf, inst, layers, raw, q_dev[NS - 1], ws, out, scale,
                             attn_bytes.mean(), row_bytes))
+        extra.update(full_cache_codec(torch, zf, synth, 4, dev))
         if not args.no_cpu_baseline:
             extra["oracle_single_thread"] = oracle_ops(w, inst, lens0, ks, vs, qs)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inst, lens0, ks, vs, qs, args.cpu_seconds, row_bytes)
+        cpu = cpu_baseline(w, inst, lens0, ks, vs, qs, args.cpu_seconds, host_cores())
+        one = cpu_baseline(w, inst, lens0, ks, vs, qs, args.cpu_seconds / 2, 1)
+        extra["cpu_baseline_one_core"] = {"value": one["value"], "unit": one["unit"],
+                                          "cores": 1, "sample": one["sample"]}
 
     result = {
         "metric": METRIC,
@@ -415,10 +441,25 @@ def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_byte
     return res
 
 
-def per_config(torch, zf, synth, wi, dev):
+def diffuse_workloads(synth):
+    """Diffuse-softmax forms of the batch-32 decode step, the 32k-token split case and the
+    8-head groups: the stated value distributions without outlier keys (outlier values kept),
+    so that a row's weight spreads over hundreds of tokens instead of one."""
+    W = synth.WORKLOADS
+    return {"d1": W[1].replace(name="diffuse_b32_ctx4096_v_outliers", outlier_kinds=2, seed=41),
+            "d2": W[2].replace(name="diffuse_b16_ctx32768_v_outliers", k_scale=(0.25, 4.0),
+                               outlier_kinds=2, seed=43),
+            "d8": W[5].replace(name="diffuse_gqa8_b32_ctx4096_v_outliers", outlier_kinds=2, seed=44)}
+
+
+def per_config(torch, zf, synth, key, dev):
     """Attention alone on one workload (no append): the packed call and its split kernel, and
-    the twin, rotating over layer caches well beyond the last-level cache."""
-    w = synth.WORKLOADS[wi].replace(extra_tokens=0)
+    the twin, rotating over layer caches well beyond the last-level cache.  `key`: a workload
+    index, or d1 / d2 / d8 for a diffuse-softmax form."""
+    key = str(key)
+    diffuse = diffuse_workloads(synth)
+    w = (diffuse[key] if key in diffuse else synth.WORKLOADS[int(key)]).replace(extra_tokens=0)
+    wi = int(key) if key.isdigit() else 100 + list(diffuse).index(key)
     inst = synth.make(w)
     to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
     T, H, D, Hq = w.page_size, w.num_kv_heads, w.head_dim, w.num_q_heads
@@ -440,7 +481,7 @@ def per_config(torch, zf, synth, wi, dev):
     out = torch.empty((w.batch, Hq, D), dtype=torch.float32, device=dev)
     ws = zf.attention_workspace(w.batch, H, Hq, D, layers[0][1].max_seq_len, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    scale = 1.0 / math.sqrt(D)
+    scale = fp32_scale(D)
     stream = torch.cuda.current_stream()
     N = 55  # 50 timed calls after the first 5
 
@@ -475,14 +516,16 @@ def per_config(torch, zf, synth, wi, dev):
                                                         status), False)
     for cache, _ in layers:
         assert zf.zf_get_status(cache.status) == 0
-    # sampled parity against the oracle: 8 (sequence, q head) rows
+    # sampled parity against the oracle: 16 (sequence, q head) rows, with their effective token
+    # counts (sum w)^2 / sum w^2, so that a row one token dominates is told from a diffuse one
     import oracle
     rng = np.random.default_rng(wi)
     want = np.zeros((w.batch, Hq), np.uint8)
-    want.reshape(-1)[rng.choice(w.batch * Hq, size=min(8, w.batch * Hq), replace=False)] = 1
+    want.reshape(-1)[rng.choice(w.batch * Hq, size=min(16, w.batch * Hq), replace=False)] = 1
     zf.zf_decode_attention(layers[0][0], layers[0][1], q, scale, out, ws)
     got = out.cpu().numpy().astype(np.float64)
-    st, ref = oracle.attention(inst.raw_pages, inst.seq_lens, inst.page_table, synth.query(w, 0), want=want)
+    st, ref, neff = oracle.attention(inst.raw_pages, inst.seq_lens, inst.page_table, synth.query(w, 0),
+                                     scale=scale, want=want, threads=host_cores(), with_neff=True)
     assert st == 0
     sel = want.astype(bool)
     err = np.abs(got[sel] - ref[sel])
@@ -504,8 +547,10 @@ def per_config(torch, zf, synth, wi, dev):
             "raw_blocks_by_cause": raw_causes(inst, rng),
             "sampled_max_abs_err": float(err.max()),
             "sampled_max_rel_err": float((err[big] / np.abs(ref[sel][big])).max()) if big.any() else 0.0,
+            "sampled_max_abs_ref": float(np.abs(ref[sel]).max()),
+            "sampled_effective_tokens_median": round(float(np.median(neff[sel])), 1),
             "note": "call = split kernel + merge when the plan splits sequences; back to back; "
-                    "50 timed calls; errors over 8 sampled (sequence, q head) rows against the oracle"}
+                    "50 timed calls; errors over 16 sampled (sequence, q head) rows against the oracle"}
 
 
 def raw_causes(inst, rng, sample_rows=20000):
@@ -551,7 +596,7 @@ def oracle_ops(w, inst, lens0, ks, vs, qs):
     assert c.append(lens, inst.page_table, ks[0], vs[0]) == 0
     t_app = time.perf_counter() - t0
     t0 = time.perf_counter()
-    st, _ = oracle.attention(inst.raw_pages, lens0, inst.page_table, qs[0])
+    st, _ = oracle.attention(inst.raw_pages, lens0, inst.page_table, qs[0], scale=fp32_scale(w.head_dim))
     t_att = time.perf_counter() - t0
     assert st == 0
     return {"cores": 1, "encode_rows_per_s": round(rows / t_enc, 1), "decode_rows_per_s": round(rows / t_dec, 1),
@@ -559,10 +604,83 @@ def oracle_ops(w, inst, lens0, ks, vs, qs):
             "rows": rows}
 
 
-def cpu_baseline(w, inst, lens0, ks, vs, qs, budget_s, row_bytes):
-    """The oracle as it stands (plain C, one thread): whole decode steps of the same workload
-    (append one token per sequence + fp64 attention for every head), repeated until the
-    budget is spent; steps/s -> tokens/s."""
+def _pmc_rows(d: str):
+    """(kernel name, counter, value) of every dispatch in the rocprofv3 counter CSVs under d."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _per_dispatch(rows, counter, match):
+    vals = [v for k, c, v in rows if c == counter and match(k)]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def pmc_summary(out, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """HBM bytes per dispatch of the path's kernels from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, summed over the chip's channels), each scaled by what the same counter reads for
+    a plain device copy of 1 GiB (the --calibrate-copy run)."""
+    fetch, write = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    cal_f, _ = _per_dispatch(_pmc_rows(cal_fetch_dir), "FETCH_SIZE", lambda k: "copyBuffer" in k)
+    cal_w, _ = _per_dispatch(_pmc_rows(cal_write_dir), "WRITE_SIZE", lambda k: "copyBuffer" in k)
+    n = 1 << 30
+    ff, wf = n / (cal_f * 1024), n / (cal_w * 1024)
+    kernels = {}
+    for name in sorted({k for k, _, _ in fetch} | {k for k, _, _ in write}):
+        short = name.split("(")[0]
+        if not short.startswith("zf::"):
+            continue
+        f, nf = _per_dispatch(fetch, "FETCH_SIZE", lambda k: k == name)
+        w_, nw = _per_dispatch(write, "WRITE_SIZE", lambda k: k == name)
+        kernels[short] = {"dispatches": max(nf, nw),
+                          "FETCH_SIZE_KiB_per_dispatch": f, "WRITE_SIZE_KiB_per_dispatch": w_,
+                          "hbm_read_bytes_per_dispatch": None if f is None else round(f * 1024 * ff),
+                          "hbm_write_bytes_per_dispatch": None if w_ is None else round(w_ * 1024 * wf)}
+    res = {"attn_source_hash": attn_source_hash(),
+           "calibration": {"copy_bytes_read": n, "copy_bytes_written": n, "FETCH_SIZE_KiB": cal_f,
+                           "WRITE_SIZE_KiB": cal_w, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "kernels": kernels}
+    attn = next((v for k, v in kernels.items() if k.startswith("zf::attn_k<zf::PackedLoader")), None)
+    if attn and attn["hbm_read_bytes_per_dispatch"] is not None and attn["hbm_write_bytes_per_dispatch"] is not None:
+        res["hbm_bytes_per_launch"] = attn["hbm_read_bytes_per_dispatch"] + attn["hbm_write_bytes_per_dispatch"]
+    json.dump(res, open(out, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def fp32_scale(head_dim: int) -> float:
+    """1/sqrt(head_dim) as the C ABI carries it (an fp32 argument); the oracle gets the same."""
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+def host_cores() -> int:
+    """Host cores this process may use (its affinity mask, capped at 16: the host share of one
+    GPU on the boxes this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, inst, lens0, ks, vs, qs, budget_s, cores):
+    """The oracle as it stands (plain C): whole decode steps of the same workload (append one
+    token per sequence + fp64 attention for every head, the heads split over `cores` threads
+    running the unchanged C routine on disjoint rows), repeated until the budget is spent;
+    steps/s -> tokens/s."""
     import oracle
 
     T = w.page_size
@@ -571,6 +689,7 @@ def cpu_baseline(w, inst, lens0, ks, vs, qs, budget_s, row_bytes):
     assert c.encode(lens0, inst.page_table, inst.raw_pages) == 0
     raw = inst.raw_pages.copy()
     lens = lens0.copy()
+    scale = fp32_scale(w.head_dim)
     done = 0
     t0 = time.perf_counter()
     cap = inst.page_table.shape[1] * T
@@ -582,16 +701,63 @@ def cpu_baseline(w, inst, lens0, ks, vs, qs, budget_s, row_bytes):
             page = inst.page_table[b, pos[b] // T]
             raw[page, :, 0, pos[b] % T] = k[b]
             raw[page, :, 1, pos[b] % T] = v[b]
-        st, _ = oracle.attention(raw, lens, inst.page_table, qs[done])
+        st, _ = oracle.attention(raw, lens, inst.page_table, qs[done], scale=scale, threads=cores)
         assert st == 0
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": round(w.batch * done / el, 3), "unit": "tokens/s", "cores": 1,
+    return {"value": round(w.batch * done / el, 3), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{done} full decode steps (batch {w.batch}, append + fp64 attention over "
-                      f"{int(lens0[0]) + 1}+ tokens, all 32 heads), {el:.1f} s on one core"}
+                      f"{int(lens0[0]) + 1}+ tokens, all {w.num_q_heads} heads), {el:.1f} s on "
+                      f"{cores} thread(s) of {cpu_model()}"}
+
+
+def full_cache_codec(torch, zf, synth, wi, dev):
+    """Full-cache encode and decode of one workload (the 4 x 131072-token cache by default),
+    each timed alone with HIP events over 10 calls after one untimed call: read + written
+    bytes per second (raw bf16 rows read and packed bytes written for encode, the reverse for
+    decode)."""
+    w = synth.WORKLOADS[wi].replace(extra_tokens=0)
+    inst = synth.make(w)
+    H, D, T = w.num_kv_heads, w.head_dim, w.page_size
+    to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    raw = to(inst.raw_pages)
+    rows = int(inst.seq_lens.sum())
+    cache = zf.PackedCache.empty(inst.num_pages, T, H, D, rows * 2 * H * (D // 64), device=dev)
+    seqs = zf.Seqs(to(inst.page_table), to(inst.seq_lens.copy()), int(inst.seq_lens.max()))
+    ws = zf.encode_workspace(seqs)
+    stream = torch.cuda.current_stream()
+
+    def timeit(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+    def enc():
+        cache.spill_top.zero_()
+        zf.zf_encode_kv(cache, seqs, raw, ws)
+    t_enc = timeit(enc)
+    assert zf.zf_get_status(cache.status) == 0
+    top = int(cache.spill_top.item())
+    out = torch.empty_like(raw)
+    t_dec = timeit(lambda: zf.zf_decode_kv(cache, seqs, out))
+    assert zf.zf_get_status(cache.status) == 0
+    raw_bytes = rows * 2 * H * D * 2
+    packed_bytes = rows * (2 * H * (D + D // 2 + D // 64) + 8) + 32 * top
+    pref = f"codec_{w.name}"
+    return {f"{pref}_encode_us": round(t_enc * 1e6, 1),
+            f"{pref}_encode_GBps_read_plus_written": round((raw_bytes + packed_bytes) / t_enc / 1e9, 1),
+            f"{pref}_decode_us": round(t_dec * 1e6, 1),
+            f"{pref}_decode_GBps_read_plus_written": round((raw_bytes + packed_bytes) / t_dec / 1e9, 1),
+            f"{pref}_rows": rows, f"{pref}_raw_blocks": top}
 
 
 if __name__ == "__main__":

@@ -15,19 +15,21 @@ from typing import Optional
 import torch  # loads the HIP runtime the library binds to
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzf.so")
+# ZF_LIB names another build of the same sources (the sanitized host build); default in-tree
+LIB_PATH = os.environ.get("ZF_LIB") or os.path.join(_HERE, "libzf.so")
 
 ZF_OK, ZF_EINVAL, ZF_EUNSUPPORTED, ZF_EHIP, ZF_EWORKSPACE, ZF_ESCRATCH = 0, 1, 2, 3, 4, 5
 ZF_NOALLOC_SCRATCH_BYTES = 16 << 20
 ZF_DEV_ESPILL, ZF_DEV_EPAGE, ZF_DEV_ELEN, ZF_DEV_ESYNC = 1, 2, 4, 8
-ZF_APPEND_SYNC_WORDS = 65  # hand-over words of the one-launch append (64) and its epoch
+ZF_APPEND_SYNC_WORDS = 66  # one-launch append: hand-over words (64), epoch, give-up test hook
+ZF_SYNC_EPOCH, ZF_SYNC_GIVE_UP = 64, 65
 
 EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_append_kv",
            "zf_append_kv_n", "zf_compact_spill", "zf_compact_workspace_bytes", "zf_max_sequences",
            "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_noalloc",
            "zf_decode_attention_raw",
            "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
-           "zf_stream_read_probe", "zf_set_append_wait_polls", "zf_get_status", "zf_status_str")
+           "zf_stream_read_probe", "zf_get_status", "zf_status_str")
 ZF_PROBE_BLOCKS = 4096
 
 
@@ -86,7 +88,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "zf_attention_workspace_init": (ctypes.c_int, [vp, sz, vp]),
         "zf_time_next_attention": (ctypes.c_int, [vp, vp]),
         "zf_stream_read_probe": (ctypes.c_int, [vp, sz, vp, vp]),
-        "zf_set_append_wait_polls": (None, [ctypes.c_uint32]),
         "zf_get_status": (ctypes.c_int, [vp, vp, vp]),
         "zf_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -132,7 +133,7 @@ class PackedCache:
     spill: torch.Tensor
     spill_top: torch.Tensor
     status: torch.Tensor
-    append_sync: Optional[torch.Tensor] = None  # int64 [65]; None: appends take two launches
+    append_sync: Optional[torch.Tensor] = None  # int64 [66]; None: appends take two launches
 
     @classmethod
     def empty(cls, num_pages, page_size, num_kv_heads, head_dim, spill_slots, device="cuda",
@@ -278,10 +279,6 @@ def zf_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> 
     ZF_PROBE_BLOCKS u32 checksums afterwards."""
     _check(load().zf_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                        _stream(stream)), "zf_stream_read_probe")
-
-
-def zf_set_append_wait_polls(polls: int) -> None:
-    load().zf_set_append_wait_polls(int(polls))
 
 
 def zf_get_status(status: torch.Tensor, stream=None) -> int:

@@ -9,7 +9,6 @@ hipError_t launch_encode(const Geom&, const zf_cache*, const zf_seqs*, const uin
                          hipStream_t);
 size_t encode_workspace_bytes(const zf_seqs*);
 int append_max_rows();
-void set_append_wait_polls(uint32_t);
 hipError_t launch_append(const Geom&, const zf_cache*, const zf_seqs*, int32_t, const uint16_t*,
                          const uint16_t*, hipStream_t);
 hipError_t launch_decode(const Geom&, const zf_cache*, const zf_seqs*, uint16_t*, hipStream_t);
@@ -129,7 +128,6 @@ zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_n
                                       static_cast<hipStream_t>(stream)));
 }
 
-void zf_set_append_wait_polls(uint32_t polls) { zf::set_append_wait_polls(polls); }
 
 zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
                        const uint16_t* v_new, zf_stream_t stream) {

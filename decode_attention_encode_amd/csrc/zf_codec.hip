@@ -6,16 +6,19 @@
 //
 // Work split.  A raw page u16[H][2][T][D] is one contiguous 64 KB run (H = 8, T = 16,
 // D = 128), so one workgroup owns one (sequence, logical page) and streams it with 16-byte
-// loads: 8 lanes cover one 64-value block, a 256-thread group covers 32 blocks per sweep.
-// Spill slots follow an exclusive scan of raw-block counts in (sequence, token) order, so
-// encode runs as pack -> scan -> spill: the pack pass writes sm/nib/base/row_flags and a
-// per-page raw count; one workgroup scans the page counts; the spill pass turns them into
-// row_spill and writes the 32-byte spill slots of the raw blocks.
+// loads: 8 lanes cover one 64-value block, a 256-thread group covers 32 blocks per sweep, and
+// a thread issues the loads of 16 sweeps before it uses the first.  Spill slots follow an
+// exclusive scan of raw-block counts in (sequence, token) order, which encode computes in the
+// same pass by decoupled look-back (Merrill and Garland, "Single-pass Parallel Prefix Scan
+// with Decoupled Look-back", NVIDIA technical report NVR-2016-002): each page publishes its
+// raw count, then takes its prefix from the pages before it, so a raw block's spill nibbles
+// are written from the registers that classified it and the raw input is read once.
 #include "zf_internal.h"
 
 namespace zf {
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+size_t encode_workspace_bytes(const zf_seqs* q);
 
 struct SeqView {
   int32_t B, maxp, max_seq_len;
@@ -39,69 +42,231 @@ __device__ __forceinline__ int rows_in_page(const SeqView& s, const Geom& g, int
   return r <= 0 ? 0 : (r > g.T ? g.T : (int)r);
 }
 
-// ------------------------------------------------------------------------------ encode: pack
+// ------------------------------------------------------------------------------ encode
 
-__global__ __launch_bounds__(256) void enc_pack_k(Geom g, SeqView s, const uint16_t* __restrict__ raw,
-                                                  uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
-                                                  uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags,
-                                                  uint32_t* __restrict__ page_count, uint32_t* status) {
+// Look-back words, one per (sequence, logical page) in the workspace (zeroed before the pass):
+// flag in bits 62..63 (0 nothing yet, 1 the page's own raw count, 2 the count of every page up
+// to and including it), the count below.
+constexpr uint64_t kLbAggregate = (uint64_t)1 << 62;
+constexpr uint64_t kLbInclusive = (uint64_t)2 << 62;
+constexpr uint64_t kLbValue = ((uint64_t)1 << 62) - 1u;
+constexpr uint32_t kLbPolls = 1u << 22;  // bound on one look-back wait (~ seconds; none is expected)
+constexpr int kEncChunks = 16;           // 16-byte loads in flight per thread
+
+// Pages of sequence b that hold tokens (0 for an invalid length).
+__device__ __forceinline__ int pages_of(const SeqView& s, const Geom& g, int b) {
+  const int32_t L = s.lens[b];
+  if (L <= 0 || (int64_t)L > (int64_t)s.maxp * g.T) return 0;
+  return (L + g.T - 1) / g.T;
+}
+
+// Raw blocks of every page before (b, p) in (sequence, page) order, from the look-back words
+// (called by wave 0 of the workgroup; the result in every lane).  Lane l looks at the l-th page
+// back within one sequence; the walk stops at the nearest page that has published an inclusive
+// count and otherwise adds the pages' own counts, moving on to the previous sequence's last
+// page when it has passed a sequence's first.  Every page waited for comes earlier in the grid,
+// so it has been dispatched and publishes without waiting for this one.  *failed is set if a
+// wait ran out (the sum is then incomplete).
+__device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* look, int b, int p,
+                              uint32_t* failed) {
+  const int lane = threadIdx.x & 63;
+  uint64_t sum = 0;
+  int pb = b, hi = p - 1;  // next page to look at: (pb, hi)
+  while (true) {
+    while (hi < 0) {  // on to the previous sequence's last page
+      if (--pb < 0) return sum;
+      hi = pages_of(s, g, pb) - 1;
+    }
+    const int q = hi - lane;
+    uint64_t w = kLbInclusive;  // before the sequence's first page: a stop with nothing in it
+    if (q >= 0) {
+      const uint64_t* a = look + (int64_t)pb * s.maxp + q;
+      uint32_t n = 0;
+      while (true) {
+        w = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((w >> 62) != 0u) break;
+        if (++n == kLbPolls) {
+          *failed = 1u;
+          w = kLbAggregate;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    const uint64_t stop = __ballot((w >> 62) == 2u);
+    const int k = stop ? __builtin_ctzll(stop) : 63;  // nearest stop, or the whole window
+    uint64_t v = lane <= k ? (w & kLbValue) : 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    sum += v;
+    if (!stop) {
+      hi -= 64;
+      continue;
+    }
+    if (hi - k >= 0) return sum;  // lane k holds an inclusive count: everything before is in it
+    hi = -1;                      // the window passed the sequence's first page
+  }
+}
+
+__global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* __restrict__ raw,
+                                             uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
+                                             uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags,
+                                             uint32_t* __restrict__ row_spill, uint8_t* __restrict__ spill,
+                                             const uint64_t* spill_top, uint64_t spill_slots,
+                                             uint64_t* look, uint32_t* failed, uint32_t* status) {
   const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int32_t L;
-  const int rows = rows_in_page(s, g, b, p, &L);
+  int rows = rows_in_page(s, g, b, p, &L);
   if (rows < 0) {
     if (p == 0 && tid == 0) set_status(status, ZF_DEV_ELEN);
-    return;
+    return;  // the sequence counts as empty
   }
-  if (rows == 0) return;
+  if (rows == 0) return;  // past the sequence's end: no page, no word
   const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
   if (pid < 0 || pid >= g.P) {
-    if (tid == 0) {
-      set_status(status, ZF_DEV_EPAGE);
-      page_count[(int64_t)b * s.maxp + p] = 0u;
-    }
-    return;
+    if (tid == 0) set_status(status, ZF_DEV_EPAGE);
+    rows = 0;  // the page counts no raw block and writes nothing, but still takes part
   }
-  __shared__ uint32_t s_flags[64];
-  if (tid < g.T) s_flags[tid] = 0u;
+
+  __shared__ uint32_t s_flags[64], s_first[64];
+  if (tid < 64) s_flags[tid] = 0u;
   __syncthreads();
 
   const int nb = g.nb();
   const int blocks = 2 * g.H * g.T * nb;
   const int64_t page_vals = g.vals_per_page();
   const int lane8 = tid & 7;
-  for (int m = tid >> 3; m < blocks; m += blockDim.x >> 3) {
-    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
-    if (slot >= rows) continue;  // uniform over the 8 lanes of the block
-    const int64_t v0 = (int64_t)pid * page_vals + (int64_t)m * kBlock + lane8 * 8;
-    uint4 in = *reinterpret_cast<const uint4*>(raw + v0);
-    uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    Window win = window8(w);
+  const int64_t page0 = (int64_t)(rows > 0 ? pid : 0) * page_vals;
+  // Classify blocks m0 + 32 i + tid / 8 (i < kEncChunks): all loads first, then per block the
+  // exponent window over its 8 lanes, the planes and the row flag bits.  Returns the raw
+  // blocks' spill nibbles (hiw[i]) and which chunks are raw (the mask).
+  auto classify = [&](int m0, uint32_t (&hiw)[kEncChunks]) -> uint32_t {
+    uint32_t w[kEncChunks][4];
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
-      win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
-      win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
+    for (int i = 0; i < kEncChunks; ++i) {
+      const int m = m0 + 32 * i + (tid >> 3);
+      if (m < blocks && (m / nb) % g.T < rows) {
+        const uint4 in = *reinterpret_cast<const uint4*>(raw + page0 + (int64_t)m * kBlock + lane8 * 8);
+        w[i][0] = in.x;
+        w[i][1] = in.y;
+        w[i][2] = in.z;
+        w[i][3] = in.w;
+      }
     }
-    const uint32_t raw_blk = win.special | (uint32_t)(win.emax - win.emin > 15u);
-    const uint32_t bexp = raw_blk ? 0u : win.emin;
-    uint32_t smw[2], nibw, hiw;
-    pack8(w, bexp, raw_blk, smw, nibw, hiw);
-    *reinterpret_cast<uint2*>(sm + v0) = make_uint2(smw[0], smw[1]);
-    *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = nibw;
-    if (lane8 == 0) {
-      base[v0 / kBlock] = (uint8_t)bexp;
-      if (raw_blk) atomicOr(&s_flags[slot], 1u << (hk * nb + half));
+    uint32_t raw_mask = 0u;
+#pragma unroll
+    for (int i = 0; i < kEncChunks; ++i) {
+      const int m = m0 + 32 * i + (tid >> 3);
+      const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+      hiw[i] = 0u;
+      if (m < blocks && slot < rows) {  // uniform over the 8 lanes of the block
+        Window win = window8(w[i]);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
+          win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
+          win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
+        }
+        const uint32_t raw_blk = win.special | (uint32_t)(win.emax - win.emin > 15u);
+        const uint32_t bexp = raw_blk ? 0u : win.emin;
+        uint32_t smw[2], nibw;
+        pack8(w[i], bexp, raw_blk, smw, nibw, hiw[i]);
+        const int64_t v0 = page0 + (int64_t)m * kBlock + lane8 * 8;
+        *reinterpret_cast<uint2*>(sm + v0) = make_uint2(smw[0], smw[1]);
+        *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = nibw;
+        raw_mask |= raw_blk << i;
+        if (lane8 == 0) {
+          base[v0 / kBlock] = (uint8_t)bexp;
+          if (raw_blk) atomicOr(&s_flags[slot], 1u << (hk * nb + half));
+        }
+      }
     }
+    return raw_mask;
+  };
+  constexpr int kGroup = kEncChunks * 32;  // blocks per group of sweeps
+  uint32_t hiw0[kEncChunks];
+  const uint32_t mask0 = classify(0, hiw0);  // the first group's spill nibbles stay in registers
+  for (int m0 = kGroup; m0 < blocks; m0 += kGroup) {  // pages of more than 512 blocks
+    uint32_t hiw[kEncChunks];
+    classify(m0, hiw);
   }
   __syncthreads();
+
+  // wave 0: row flags, the page's raw count, its prefix by look-back, row_spill
   if (tid < 64) {
-    uint32_t f = tid < rows ? s_flags[tid] : 0u;
+    const uint32_t f = tid < rows ? s_flags[tid] : 0u;
     if (tid < rows) row_flags[(int64_t)pid * g.T + tid] = f;
-    uint32_t c = __popc(f);
+    const uint32_t c = __popc(f);
+    uint32_t incl = c;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) c += __shfl_xor((int)c, o, 64);
-    if (tid == 0) page_count[(int64_t)b * s.maxp + p] = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t up = __shfl_up((int)incl, o, 64);
+      if (tid >= o) incl += up;
+    }
+    const uint32_t total = __shfl((int)incl, 63, 64);
+    uint64_t* my_word = look + (int64_t)b * s.maxp + p;
+    if (tid == 0) __hip_atomic_store(my_word, kLbAggregate | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t fail = 0u;
+    const uint64_t before = look_back(s, g, look, b, p, &fail);
+    if (tid == 0) {
+      __hip_atomic_store(my_word, kLbInclusive | (before + total), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (fail) atomicOr(failed, 1u);
+    }
+    const uint64_t first = before + (incl - c);  // offset from spill_top
+    if (tid < rows) row_spill[(int64_t)pid * g.T + tid] = (uint32_t)(*spill_top + first);
+    s_first[tid] = (uint32_t)first;
   }
+  __syncthreads();
+
+  // spill slots: the first group's from registers, any later group's from the raw input again
+  const uint64_t top = *spill_top;
+  auto slot_of = [&](int m) -> uint64_t {
+    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+    const int j = hk * nb + half;
+    return top + s_first[slot] + __popc(s_flags[slot] & ((1u << j) - 1u));
+  };
+#pragma unroll
+  for (int i = 0; i < kEncChunks; ++i) {
+    if (!((mask0 >> i) & 1u)) continue;
+    const uint64_t idx = slot_of(32 * i + (tid >> 3));
+    if (idx < spill_slots)  // a pool too small for the call: slots past its end are skipped
+      *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hiw0[i];
+  }
+  for (int m = kGroup + (tid >> 3); m < blocks; m += 32) {
+    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+    if (slot >= rows || !((s_flags[slot] >> (hk * nb + half)) & 1u)) continue;
+    const uint64_t idx = slot_of(m);
+    if (idx >= spill_slots) continue;
+    const uint4 in = *reinterpret_cast<const uint4*>(raw + page0 + (int64_t)m * kBlock + lane8 * 8);
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t hi = 0u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
+    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
+  }
+}
+
+// Ends an encode: spill_top += the raw blocks of all pages (the inclusive count of the last
+// page that holds tokens) if the pool holds them, else ZF_DEV_ESPILL and spill_top kept;
+// ZF_DEV_ESYNC instead if a look-back wait ran out.
+__global__ void enc_finish_k(Geom g, SeqView s, const uint64_t* look, const uint32_t* failed,
+                             uint64_t* spill_top, uint64_t spill_slots, uint32_t* status) {
+  if (threadIdx.x != 0) return;
+  if (*failed) {
+    set_status(status, ZF_DEV_ESYNC);
+    return;
+  }
+  uint64_t total = 0;
+  for (int b = s.B - 1; b >= 0; --b) {
+    const int np = pages_of(s, g, b);
+    if (np > 0) {
+      total = look[(int64_t)b * s.maxp + np - 1] & kLbValue;
+      break;
+    }
+  }
+  const uint64_t top = *spill_top;
+  if (fits_in_pool(total, top, spill_slots)) *spill_top = top + total;
+  else set_status(status, ZF_DEV_ESPILL);
 }
 
 // ------------------------------------------------------------------------------ encode: scan
@@ -210,56 +375,6 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan_k(Geom g, SeqView s,
   }
 }
 
-// ------------------------------------------------------------------------------ encode: spill
-
-__global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint16_t* __restrict__ raw,
-                                                   const uint32_t* __restrict__ row_flags,
-                                                   uint32_t* __restrict__ row_spill, uint8_t* __restrict__ spill,
-                                                   const uint32_t* __restrict__ page_prefix,
-                                                   const uint32_t* ws_flag, uint64_t spill_slots) {
-  if (*ws_flag != 0u) return;
-  const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  int32_t L;
-  const int rows = rows_in_page(s, g, b, p, &L);
-  if (rows <= 0) return;
-  const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
-  if (pid < 0 || pid >= g.P) return;
-  __shared__ uint32_t s_flags[64], s_first[64];
-  if (tid < 64) {
-    uint32_t f = tid < rows ? row_flags[(int64_t)pid * g.T + tid] : 0u;
-    uint32_t c = __popc(f), incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t up = __shfl_up((int)incl, o, 64);
-      if (tid >= o) incl += up;
-    }
-    uint32_t first = page_prefix[(int64_t)b * s.maxp + p] + (incl - c);
-    s_flags[tid] = f;
-    s_first[tid] = first;
-    if (tid < rows) row_spill[(int64_t)pid * g.T + tid] = first;
-  }
-  __syncthreads();
-  const int nb = g.nb();
-  const int blocks = 2 * g.H * g.T * nb;
-  const int lane8 = tid & 7;
-  for (int m = tid >> 3; m < blocks; m += blockDim.x >> 3) {
-    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
-    if (slot >= rows) continue;
-    const int j = hk * nb + half;
-    const uint32_t f = s_flags[slot];
-    if (!((f >> j) & 1u)) continue;
-    const uint64_t idx = (uint64_t)s_first[slot] + __popc(f & ((1u << j) - 1u));
-    if (idx >= spill_slots) continue;  // only reachable when two sequences share a page
-    const int64_t v0 = (int64_t)pid * g.vals_per_page() + (int64_t)m * kBlock + lane8 * 8;
-    uint4 in = *reinterpret_cast<const uint4*>(raw + v0);
-    uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    uint32_t hi = 0u;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
-    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
-  }
-}
-
 // ------------------------------------------------------------------------------ append
 
 // Append of n tokens per sequence; new row r = b * n + j is token j of sequence b, at position
@@ -272,22 +387,30 @@ __global__ __launch_bounds__(256) void enc_spill_k(Geom g, SeqView s, const uint
 //
 // Two forms.  Two launches: append_pack_k, then append_commit_k, which reads the flag words
 // back from row_flags.  One launch (append_one_k, when the cache has sync words and there are
-// at most 64 new rows): R packing workgroups and one commit workgroup.  Each packing workgroup
-// publishes one 64-bit word, its row's flag word and error bits tagged with the call's epoch
-// (a counter in the sync area), stored only after its loads of the epoch, its length and
-// spill_top have returned.  Every packing workgroup then waits until all R words carry the tag,
-// takes the all-or-nothing decision from them, marks its own word decided, and writes its
-// row's spill slots (from spill_top plus the raw blocks of the rows before it) and row_spill.
-// The commit waits until all R words are marked decided, takes the same decision, and advances
-// seq_lens and spill_top (every length was read before its word was stored) and then the
-// epoch; a workgroup that gives up waiting never marks its word, so the commit then changes
-// nothing.  Each word carries its data itself, so no fence orders it after other stores.
+// at most 64 new rows): R packing workgroups and one commit workgroup (the last), handing
+// their flag words to each other by decoupled look-back.  Packing workgroup r publishes one
+// 64-bit word, its row's flag word and error bits tagged with the call's epoch (a counter in
+// the sync area), stored only after its loads of the epoch, its length and spill_top have
+// returned.  It then waits only for the words of rows 0 .. r-1, which take its prefix (their
+// raw blocks) and their error bits, writes its spill slots and row_spill from spill_top plus
+// that prefix, and marks its word done.  These writes land in slots that hold nothing yet
+// (positions seq_lens[b] and later, spill slots from spill_top on, below spill_slots), so they
+// are harmless if the call fails.  The commit waits until all R words are marked done, takes
+// the all-or-nothing decision, and advances seq_lens and spill_top (every length was read
+// before its word was stored); it always advances the epoch, so no word of this call can match
+// the next one.  Every wait is for lower-numbered workgroups, which are dispatched first, so
+// every wait ends without any assumption of co-residency.  A packing workgroup that still gives
+// up waiting marks its word abandoned instead, and the commit then changes nothing
+// (ZF_DEV_ESYNC).  Each word carries its data itself, so no fence orders it after other stores.
 constexpr int kAppendThreads = 1024;
-constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS
+constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS (beyond: the chunked form)
+constexpr int kAppendChunkedMaxRows = 1 << 24;  // new rows of one call
 constexpr int kOneMaxRows = 64;       // new rows of a one-launch append (sync words 0 .. 63; 64: epoch)
-constexpr uint32_t kSyncPolls = 1u << 20;  // bound on each wait for the words (about 1 s);
-                                           // the packing workgroups' bound can be lowered
-constexpr uint64_t kTagMod = (1u << 28) - 1u;
+constexpr uint32_t kSyncPolls = 1u << 20;  // bound on each wait for the words (about 1 s)
+constexpr int kSyncEpoch = kOneMaxRows;      // sync word holding the epoch
+constexpr int kSyncGiveUp = kOneMaxRows + 1; // sync word: nonzero makes waiting packing
+                                             // workgroups give up at once (forces ZF_DEV_ESYNC)
+constexpr uint64_t kTagMod = (1u << 27) - 1u;
 
 // Row of new token j of sequence b (n per sequence) whose length was read as L, or -1 (with the
 // error bit) when the sequence cannot take them.
@@ -364,9 +487,12 @@ __device__ __forceinline__ uint32_t row_flag_word(bool has, int j, int lane8, ui
   return s_f;
 }
 
+// count_out: the chunked form also leaves the row's raw count in its row_spill entry (the new
+// row's, which holds nothing yet) for the chunk scan.
 __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, uint8_t* sm,
-                                                     uint8_t* nib, uint8_t* base, uint32_t* row_flags) {
+                                                     uint8_t* nib, uint8_t* base, uint32_t* row_flags,
+                                                     uint32_t* count_out) {
   const int r = blockIdx.x, b = r / n, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
   uint32_t err;
   const int64_t row = append_row(g, s, b, r - b * n, n, &err);
@@ -376,7 +502,10 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, c
   if (has) o = classify_new(g, r, j, lane8, k_new, v_new);
   const uint32_t f = row_flag_word(has, j, lane8, o.raw);
   if (has) store_new(g, row, j, lane8, o, sm, nib, base);
-  if (tid == 0) row_flags[row] = f;
+  if (tid == 0) {
+    row_flags[row] = f;
+    if (count_out) count_out[row] = __popc(f);
+  }
 }
 
 __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqView s, int n,
@@ -456,47 +585,225 @@ __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqVie
   if (tid == 0) *spill_top = top + total;
 }
 
+// ------------------------------------------------------------------ append: chunked form
+// For more new rows than one commit workgroup holds (prefill written in chunks, long
+// speculative runs), four launches and no workspace: the pack kernel above leaves each row's raw
+// count in its (not yet defined) row_spill entry; append_chunk_scan_k turns the counts of each
+// chunk of kChunkRows rows into row-local exclusive prefixes there, the chunk's total in its
+// first row's entry; append_chunk_commit_k adds the totals of the chunks before its own and
+// writes the chunk's final row_spill entries (all but the first row's, which the other chunks
+// still read) and spill slots; append_chunk_finish_k checks the whole call (lengths, page ids,
+// room in the pool) and only then writes the first rows' entries and advances seq_lens and
+// spill_top.  Until that last step only slots that hold nothing yet are written (rows at
+// positions seq_lens[b] and later, spill slots from spill_top on within the pool), so a failed
+// call changes no defined state.  Rows with an invalid position are skipped by every step (the
+// call then fails in the last).
+constexpr int kChunkItems = 4;
+constexpr int kChunkRows = kScanThreads * kChunkItems;
+
+__global__ __launch_bounds__(kScanThreads) void append_chunk_scan_k(Geom g, SeqView s, int n,
+                                                                    uint32_t* row_spill) {
+  __shared__ uint32_t s_tmp[kScanThreads];
+  const int R = s.B * n, r0 = blockIdx.x * kChunkRows, tid = threadIdx.x;
+  int64_t row[kChunkItems];
+  uint32_t cnt[kChunkItems], mine = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkItems; ++i) {
+    const int r = r0 + tid * kChunkItems + i;
+    uint32_t e;
+    row[i] = r < R ? append_row(g, s, r / n, r % n, n, &e) : -1;
+    cnt[i] = row[i] >= 0 ? row_spill[row[i]] : 0u;
+    mine += cnt[i];
+  }
+  uint32_t total;
+  uint32_t ex = block_exclusive_scan(mine, s_tmp, &total);
+#pragma unroll
+  for (int i = 0; i < kChunkItems; ++i) {
+    if (row[i] >= 0) row_spill[row[i]] = (tid == 0 && i == 0) ? total : ex;
+    ex += cnt[i];
+  }
+}
+
+// Raw blocks of the chunks before chunk c (every thread gets the sum).
+__device__ uint64_t chunks_before(const Geom& g, const SeqView& s, int n, int c,
+                                  const uint32_t* row_spill) {
+  uint64_t part = 0;
+  for (int k = threadIdx.x; k < c; k += kScanThreads) {
+    uint32_t e;
+    const int r = k * kChunkRows;
+    const int64_t row = append_row(g, s, r / n, r % n, n, &e);
+    if (row >= 0) part += row_spill[row];
+  }
+  __shared__ unsigned long long s_sum;
+  if (threadIdx.x == 0) s_sum = 0ull;
+  __syncthreads();
+  atomicAdd(&s_sum, (unsigned long long)part);
+  __syncthreads();
+  const uint64_t r = s_sum;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kScanThreads) void append_chunk_commit_k(
+    Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint32_t* __restrict__ row_flags, uint32_t* row_spill, uint8_t* spill,
+    const uint64_t* spill_top, uint64_t spill_slots) {
+  __shared__ uint32_t s_flags[kChunkRows], s_first[kChunkRows];
+  const int R = s.B * n, c = blockIdx.x, r0 = c * kChunkRows, tid = threadIdx.x;
+  const int rows = min(kChunkRows, R - r0);
+  const uint64_t before = *spill_top + chunks_before(g, s, n, c, row_spill);
+  for (int i = tid; i < rows; i += kScanThreads) {
+    const int r = r0 + i;
+    uint32_t e;
+    const int64_t row = append_row(g, s, r / n, r % n, n, &e);
+    uint32_t f = 0u, local = 0u;
+    if (row >= 0) {
+      f = row_flags[row];
+      local = i == 0 ? 0u : row_spill[row];
+    }
+    s_flags[i] = f;
+    s_first[i] = local;
+    if (row >= 0 && i > 0) row_spill[row] = (uint32_t)(before + local);
+  }
+  __syncthreads();
+  // spill slots of the raw blocks: 8 lanes per block, blocks walked in (row, block) order
+  const int nb = g.nb(), D = g.D, H = g.H;
+  const uint32_t rb = 2u * H * nb, nblk = (uint32_t)rows * rb;
+  const int lane8 = tid & 7;
+  for (uint32_t m = tid >> 3; m < nblk; m += kScanThreads >> 3) {
+    const uint32_t i = m / rb, j = m - i * rb;
+    const uint32_t f = s_flags[i];
+    if (!((f >> j) & 1u)) continue;
+    const uint64_t idx = before + s_first[i] + __popc(f & ((1u << j) - 1u));
+    if (idx >= spill_slots) continue;  // the call fails in the last step
+    const uint32_t hk = j / nb, half = j - hk * nb, h = hk >> 1, kv = hk & 1;
+    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)(r0 + i) * H + h) * D +
+                                                     half * kBlock + lane8 * 8);
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t hi = 0u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
+    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
+  }
+}
+
+// The last step of the chunked form (one workgroup): every sequence's length and the page ids
+// of its new rows, then room in the pool; on success the first rows' row_spill entries,
+// seq_lens and spill_top.
+__global__ __launch_bounds__(kScanThreads) void append_chunk_finish_k(Geom g, SeqView s, int n,
+                                                                      uint32_t* row_spill, uint64_t* spill_top,
+                                                                      uint64_t spill_slots, uint32_t* status) {
+  __shared__ uint32_t s_err;
+  __shared__ unsigned long long s_total;
+  const int tid = threadIdx.x, R = s.B * n, nchunks = (R + kChunkRows - 1) / kChunkRows;
+  if (tid == 0) {
+    s_err = 0u;
+    s_total = 0ull;
+  }
+  __syncthreads();
+  // 32 threads per sequence check the page ids of its new rows
+  uint32_t err = 0u;
+  for (int b = tid >> 5; b < s.B; b += kScanThreads >> 5) {
+    const int32_t L = s.lens[b];
+    if (L < 0 || (int64_t)L + n > (int64_t)s.maxp * g.T || (int64_t)L + n > s.max_seq_len) {
+      err |= ZF_DEV_ELEN;
+      continue;
+    }
+    const int p_lo = L / g.T, p_hi = (L + n - 1) / g.T;
+    for (int p = p_lo + (tid & 31); p <= p_hi; p += 32) {
+      const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
+      if (pid < 0 || pid >= g.P) err |= ZF_DEV_EPAGE;
+    }
+  }
+  if (err) atomicOr(&s_err, err);
+  uint64_t part = 0;
+  for (int k = tid; k < nchunks; k += kScanThreads) {
+    uint32_t e;
+    const int r = k * kChunkRows;
+    const int64_t row = append_row(g, s, r / n, r % n, n, &e);
+    if (row >= 0) part += row_spill[row];
+  }
+  atomicAdd(&s_total, (unsigned long long)part);
+  __syncthreads();
+  const uint64_t top = *spill_top, total = s_total;
+  if (s_err) {
+    if (tid == 0) set_status(status, s_err);
+    return;
+  }
+  if (!fits_in_pool(total, top, spill_slots)) {
+    if (tid == 0) set_status(status, ZF_DEV_ESPILL);
+    return;
+  }
+  // first rows: the exclusive prefixes of the chunk totals, kScanThreads chunks at a time
+  __shared__ uint32_t s_scan[kScanThreads];
+  uint64_t carry = 0;  // the same in every thread
+  for (int c0 = 0; c0 < nchunks; c0 += kScanThreads) {
+    const int c = c0 + tid;
+    int64_t row = -1;
+    uint32_t tot = 0u;
+    if (c < nchunks) {
+      uint32_t e;
+      const int r = c * kChunkRows;
+      row = append_row(g, s, r / n, r % n, n, &e);
+      tot = row_spill[row];
+    }
+    uint32_t sum;
+    const uint32_t ex = block_exclusive_scan(tot, s_scan, &sum);
+    if (row >= 0) row_spill[row] = (uint32_t)(top + carry + ex);
+    carry += sum;
+  }
+  __syncthreads();  // every length was read above
+  for (int b = tid; b < s.B; b += kScanThreads) s.lens[b] += n;
+  if (tid == 0) *spill_top = top + total;
+}
+
 // Tag of a hand-over word published under epoch E: never 0, and different for consecutive
-// epochs (a word left by the previous call never matches).
+// epochs (a word left by an earlier call never matches).
 __device__ __forceinline__ uint32_t sync_tag(uint64_t E) { return (uint32_t)(E % kTagMod) + 1u; }
 
-// Hand-over word of one new row: tag << 36 | decided << 35 | error bits << 32 | flag word.
-// `decided`: the row's workgroup has seen every word of the call (so it will write its spill
-// slots if the call succeeds).
-__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 36); }
-constexpr uint64_t kDecided = (uint64_t)1 << 35;
+// Hand-over word of one new row: tag << 37 | abandoned << 36 | done << 35 | error bits << 32 |
+// flag word.  done: the row's workgroup has its prefix and has written its spill slots;
+// abandoned: it gave up waiting for the rows before it.
+__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> 37); }
+constexpr uint64_t kDone = (uint64_t)1 << 35;
+constexpr uint64_t kAbandoned = (uint64_t)1 << 36;
+__device__ __forceinline__ uint64_t hand_over_word(uint32_t tag, uint32_t err, uint32_t flags) {
+  return ((uint64_t)tag << 37) | ((uint64_t)err << 32) | flags;
+}
 
-// What every workgroup learns from the R hand-over words (wave 0 polls them, lane i word i).
+// What a workgroup learns from the hand-over words of rows 0 .. n-1 (wave 0 polls them, lane
+// i word i): whether all arrived (with the done or abandoned mark when `final`), their raw
+// blocks, their error bits, and whether one was abandoned.
 struct HandOver {
-  uint32_t seen, err, total, pref;  // pref: raw blocks of the rows before row `me`
+  uint32_t seen, err, total, abandoned;
 };
 
-__device__ __forceinline__ HandOver read_hand_over(const uint64_t* sync, int R, int me, uint32_t tag,
-                                                   bool need_decided, uint32_t polls) {
+__device__ __forceinline__ HandOver read_hand_over(const uint64_t* sync, int n, uint32_t tag, bool final,
+                                                   uint32_t polls) {
   __shared__ HandOver s_h;
   const int tid = threadIdx.x;
   if (tid < 64) {
     uint64_t w = 0u;
-    bool ok = tid >= R;
+    bool ok = tid >= n;
     for (uint32_t p = 0; !ok && p < polls; ++p) {
       w = __hip_atomic_load(&sync[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = word_tag(w) == tag && (!need_decided || (w & kDecided));
+      ok = word_tag(w) == tag && (!final || (w & (kDone | kAbandoned)));
       if (!ok) __builtin_amdgcn_s_sleep(2);
     }
-    const uint32_t cnt = tid < R ? __popc((uint32_t)w) : 0u;
-    uint32_t incl = cnt, err = tid < R ? (uint32_t)(w >> 32) & 7u : 0u, miss = ok ? 0u : 1u;
+    uint32_t cnt = tid < n ? __popc((uint32_t)w) : 0u, err = tid < n ? (uint32_t)(w >> 32) & 7u : 0u;
+    uint32_t miss = ok ? 0u : 1u, ab = tid < n && (w & kAbandoned) ? 1u : 0u;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t up = __shfl_up((int)incl, o, 64);
-      if (tid >= o) incl += up;
+      cnt += (uint32_t)__shfl_xor((int)cnt, o, 64);
       err |= (uint32_t)__shfl_xor((int)err, o, 64);
       miss |= (uint32_t)__shfl_xor((int)miss, o, 64);
+      ab |= (uint32_t)__shfl_xor((int)ab, o, 64);
     }
-    if (tid == me) s_h.pref = incl - cnt;
-    if (tid == 63) {
-      s_h.total = incl;
+    if (tid == 0) {
+      s_h.total = cnt;
       s_h.err = err;
       s_h.seen = miss == 0u;
+      s_h.abandoned = ab;
     }
   }
   __syncthreads();
@@ -504,28 +811,25 @@ __device__ __forceinline__ HandOver read_hand_over(const uint64_t* sync, int R, 
 }
 
 // Commit workgroup of the one-launch append: once every row's word carries this call's tag and
-// the decided mark, it advances seq_lens and spill_top, clears the words of unused rows and
-// moves to the next epoch.
+// its done (or abandoned) mark, it advances seq_lens and spill_top if the call succeeded, and
+// moves to the next epoch in every case.
 __device__ void commit_one(const SeqView& s, int n, uint64_t* spill_top, uint64_t spill_slots,
                            uint32_t* status, uint64_t* sync) {
   const int R = s.B * n, tid = threadIdx.x;
-  const uint64_t E = sync[kOneMaxRows];  // written only by an earlier launch: a plain load
+  const uint64_t E = sync[kSyncEpoch];  // written only by an earlier launch: a plain load
   const uint64_t top = *spill_top;
   const int32_t L = tid < s.B ? s.lens[tid] : 0;
-  const HandOver h = read_hand_over(sync, R, -1, sync_tag(E), true, kSyncPolls);
-  if (!h.seen) {  // some row's word never came or never got decided: change nothing
-    if (tid == 0) set_status(status, ZF_DEV_ESYNC);
-    return;
-  }
+  const HandOver h = read_hand_over(sync, R, sync_tag(E), true, kSyncPolls);
   const bool fits = fits_in_pool(h.total, top, spill_slots);
-  if (tid == 0) set_status(status, h.err ? h.err : (fits ? 0u : ZF_DEV_ESPILL));
-  if (!h.err && fits) {
+  if (tid == 0) {
+    const uint32_t e = !h.seen || h.abandoned ? ZF_DEV_ESYNC : h.err ? h.err : fits ? 0u : ZF_DEV_ESPILL;
+    set_status(status, e);
+  }
+  if (h.seen && !h.abandoned && !h.err && fits) {
     if (tid < s.B) s.lens[tid] = L + n;  // every packing workgroup read its length before its word
     if (tid == 0) *spill_top = top + h.total;
   }
-  if (tid >= R && tid < kOneMaxRows)
-    __hip_atomic_store(&sync[tid], (uint64_t)0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (tid == 0) __hip_atomic_store(&sync[kOneMaxRows], E + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&sync[kSyncEpoch], E + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One-launch append: workgroups 0 .. R-1 pack new row blockIdx.x, workgroup R commits.
@@ -533,14 +837,14 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
                                                     const uint16_t* __restrict__ v_new, uint8_t* sm,
                                                     uint8_t* nib, uint8_t* base, uint32_t* row_flags,
                                                     uint32_t* row_spill, uint8_t* spill, uint64_t* spill_top,
-                                                    uint64_t spill_slots, uint32_t* status, uint64_t* sync,
-                                                    uint32_t polls) {
+                                                    uint64_t spill_slots, uint32_t* status, uint64_t* sync) {
   const int R = s.B * n, r = blockIdx.x, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
   if (r == R) {
     commit_one(s, n, spill_top, spill_slots, status, sync);
     return;
   }
-  const uint64_t E = sync[kOneMaxRows];
+  const uint64_t E = sync[kSyncEpoch];
+  const uint32_t tag = sync_tag(E);
   const uint64_t top = *spill_top;
   const int b = r / n;
   uint32_t err;
@@ -552,30 +856,35 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
   if (tid == 0) {
     // the word is built from the epoch, the length (through err and row) and spill_top as
     // loaded, so it cannot be stored before those loads have returned
-    uint32_t hi = (sync_tag(E) << 4) | err;
-    asm volatile("" : "+v"(hi) : "v"((uint32_t)row), "v"((uint32_t)top));
-    __hip_atomic_store(&sync[r], ((uint64_t)hi << 32) | f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t t = tag;
+    asm volatile("" : "+v"(t) : "v"((uint32_t)row), "v"((uint32_t)top));
+    __hip_atomic_store(&sync[r], hand_over_word(t, err, f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (row >= 0) {
     if (has) store_new(g, row, j, lane8, o, sm, nib, base);
     if (tid == 0) row_flags[row] = f;
   }
-  const HandOver h = read_hand_over(sync, R, r, sync_tag(E), false, polls);
-  if (!h.seen) {  // the commit will not see this row decided, so the call changes nothing
-    if (tid == 0) set_status(status, ZF_DEV_ESYNC);
+  // the rows before this one: their raw blocks are this row's prefix
+  const bool give_up = r > 0 && sync[kSyncGiveUp] != 0u;
+  const HandOver h = read_hand_over(sync, r, tag, false, give_up ? 0u : kSyncPolls);
+  if (!h.seen) {  // the commit sees the mark and changes nothing
+    if (tid == 0)
+      __hip_atomic_store(&sync[r], hand_over_word(tag, err, f) | kAbandoned, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (tid == 0)
-    __hip_atomic_store(&sync[r], ((uint64_t)((sync_tag(E) << 4) | err) << 32 | kDecided) | f,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // the commit takes the same decision from the same words
-  if (h.err || !fits_in_pool(h.total, top, spill_slots)) return;
-  const uint64_t first = top + h.pref;
-  if (has && o.raw) {
-    const uint64_t slot = first + __popc(f & ((1u << j) - 1u));
-    *reinterpret_cast<uint32_t*>(spill + slot * 32u + lane8 * 4) = o.hi;
+  // A call that has already failed writes nothing more; otherwise the slots are written even if
+  // a later row still makes the call fail (they hold nothing yet), within the pool
+  if (!err && !h.err && row >= 0 && fits_in_pool(h.total + __popc(f), top, spill_slots)) {
+    const uint64_t first_slot = top + h.total;
+    if (has && o.raw) {
+      const uint64_t slot = first_slot + __popc(f & ((1u << j) - 1u));
+      *reinterpret_cast<uint32_t*>(spill + slot * 32u + lane8 * 4) = o.hi;
+    }
+    if (tid == 0) row_spill[row] = (uint32_t)first_slot;
   }
-  if (tid == 0) row_spill[row] = (uint32_t)first;
+  if (tid == 0)
+    __hip_atomic_store(&sync[r], hand_over_word(tag, err, f) | kDone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------------ decode
@@ -599,30 +908,57 @@ __global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t
     if (tid == 0) set_status(status, ZF_DEV_EPAGE);
     return;
   }
+  __shared__ uint32_t s_f[64], s_sp[64];
+  if (tid < rows) {
+    s_f[tid] = row_flags[(int64_t)pid * g.T + tid];
+    s_sp[tid] = row_spill[(int64_t)pid * g.T + tid];
+  }
+  __syncthreads();
   const int nb = g.nb();
   const int blocks = 2 * g.H * g.T * nb;
   const int lane8 = tid & 7;
+  const int64_t page0 = (int64_t)pid * g.vals_per_page();
   uint32_t err = 0;
-  for (int m = tid >> 3; m < blocks; m += blockDim.x >> 3) {
-    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
-    if (slot >= rows) continue;
-    const int64_t v0 = (int64_t)pid * g.vals_per_page() + (int64_t)m * kBlock + lane8 * 8;
-    const uint2 smw = *reinterpret_cast<const uint2*>(sm + v0);
-    const uint32_t nibw = *reinterpret_cast<const uint32_t*>(nib + (v0 >> 1));
-    const uint32_t f = row_flags[(int64_t)pid * g.T + slot];
-    const int j = hk * nb + half;
-    uint32_t base_pair = 0u, hi = 0u;
-    if ((f >> j) & 1u) {
-      const uint64_t idx = (uint64_t)row_spill[(int64_t)pid * g.T + slot] + __popc(f & ((1u << j) - 1u));
-      if (idx < spill_slots) hi = *reinterpret_cast<const uint32_t*>(spill + idx * 32u + lane8 * 4);
-      else err = ZF_DEV_ESPILL;
-    } else {
-      base_pair = (uint32_t)base[v0 / kBlock] * 0x00010001u;
+  // blocks m0 + 32 i + tid / 8: every load of a group issued before the first rebuild
+  for (int m0 = 0; m0 < blocks; m0 += kEncChunks * 32) {
+    uint2 smw[kEncChunks];
+    uint32_t nibw[kEncChunks], bp[kEncChunks], hi[kEncChunks];
+#pragma unroll
+    for (int i = 0; i < kEncChunks; ++i) {
+      const int m = m0 + 32 * i + (tid >> 3);
+      if (m < blocks && (m / nb) % g.T < rows) {
+        const int64_t v0 = page0 + (int64_t)m * kBlock + lane8 * 8;
+        smw[i] = *reinterpret_cast<const uint2*>(sm + v0);
+        nibw[i] = *reinterpret_cast<const uint32_t*>(nib + (v0 >> 1));
+        bp[i] = base[v0 / kBlock];
+      }
     }
-    uint32_t pr[4], w[4];
-    rebuild8(smw.x, smw.y, nibw, hi, base_pair, pr);
-    pairs_to_natural(pr, w);
-    *reinterpret_cast<uint4*>(out + v0) = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+    for (int i = 0; i < kEncChunks; ++i) {
+      const int m = m0 + 32 * i + (tid >> 3);
+      const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+      hi[i] = 0u;
+      if (m < blocks && slot < rows) {
+        const uint32_t f = s_f[slot];
+        const int j = hk * nb + half;
+        if ((f >> j) & 1u) {
+          const uint64_t idx = (uint64_t)s_sp[slot] + __popc(f & ((1u << j) - 1u));
+          if (idx < spill_slots) hi[i] = *reinterpret_cast<const uint32_t*>(spill + idx * 32u + lane8 * 4);
+          else err = ZF_DEV_ESPILL;
+          bp[i] = 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kEncChunks; ++i) {
+      const int m = m0 + 32 * i + (tid >> 3);
+      if (m < blocks && (m / nb) % g.T < rows) {
+        uint32_t pr[4], w[4];
+        rebuild8(smw[i].x, smw[i].y, nibw[i], hi[i], bp[i] * 0x00010001u, pr);
+        pairs_to_natural(pr, w);
+        *reinterpret_cast<uint4*>(out + page0 + (int64_t)m * kBlock + lane8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
   }
   if (err) set_status(status, err);
 }
@@ -750,32 +1086,27 @@ static SeqView view(const zf_seqs* q) {
 hipError_t launch_encode(const Geom& g, const zf_cache* c, const zf_seqs* q, const uint16_t* raw,
                          uint32_t* ws, hipStream_t st) {
   SeqView s = view(q);
-  uint32_t* ws_flag = ws;
-  uint32_t* page_count = ws + 64;  // 256-byte header
-  dim3 grid(q->max_pages_per_seq, q->batch);
-  hipLaunchKernelGGL(enc_pack_k, grid, dim3(256), 0, st, g, s, raw, c->sm, c->nib, c->base,
-                     c->row_flags, page_count, c->status);
-  size_t lds = ((size_t)q->batch + 1 + kScanThreads) * sizeof(uint32_t);
-  hipLaunchKernelGGL(enc_scan_k, dim3(1), dim3(kScanThreads), lds, st, g, s, page_count,
-                     c->spill_top, c->spill_top, c->spill_slots, ws_flag, c->status);
-  hipLaunchKernelGGL(enc_spill_k, grid, dim3(256), 0, st, g, s, raw, c->row_flags, c->row_spill,
-                     c->spill, page_count, ws_flag, c->spill_slots);
+  uint32_t* failed = ws;                                       // 256-byte header
+  uint64_t* look = reinterpret_cast<uint64_t*>(ws + 64);       // one word per (sequence, page)
+  hipError_t e = launch_fill_zero(ws, encode_workspace_bytes(q), st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(enc_k, dim3(q->max_pages_per_seq, q->batch), dim3(256), 0, st, g, s, raw, c->sm,
+                     c->nib, c->base, c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots,
+                     look, failed, c->status);
+  hipLaunchKernelGGL(enc_finish_k, dim3(1), dim3(64), 0, st, g, s, look, failed, c->spill_top,
+                     c->spill_slots, c->status);
   return hipGetLastError();
 }
 
 size_t encode_workspace_bytes(const zf_seqs* q) {
-  return 256 + (size_t)q->batch * (size_t)q->max_pages_per_seq * sizeof(uint32_t);
+  return 256 + (size_t)q->batch * (size_t)q->max_pages_per_seq * sizeof(uint64_t);
 }
 
 size_t encode_lds_bytes(int32_t batch) {
   return ((size_t)batch + 1 + kScanThreads) * sizeof(uint32_t);
 }
 
-int append_max_rows() { return kAppendMaxRows; }
-
-static uint32_t g_append_wait_polls = kSyncPolls;
-
-void set_append_wait_polls(uint32_t polls) { g_append_wait_polls = polls; }
+int append_max_rows() { return kAppendChunkedMaxRows; }
 
 hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int32_t n, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t st) {
@@ -784,11 +1115,22 @@ hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int
   if (c->append_sync && rows <= kOneMaxRows) {
     hipLaunchKernelGGL(append_one_k, dim3(rows + 1), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
                        c->base, c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status,
-                       c->append_sync, g_append_wait_polls);
+                       c->append_sync);
+    return hipGetLastError();
+  }
+  if (rows > kAppendMaxRows) {
+    const int nchunks = (rows + kChunkRows - 1) / kChunkRows;
+    hipLaunchKernelGGL(append_pack_k, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
+                       c->base, c->row_flags, c->row_spill);
+    hipLaunchKernelGGL(append_chunk_scan_k, dim3(nchunks), dim3(kScanThreads), 0, st, g, s, n, c->row_spill);
+    hipLaunchKernelGGL(append_chunk_commit_k, dim3(nchunks), dim3(kScanThreads), 0, st, g, s, n, k_new,
+                       v_new, c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots);
+    hipLaunchKernelGGL(append_chunk_finish_k, dim3(1), dim3(kScanThreads), 0, st, g, s, n, c->row_spill,
+                       c->spill_top, c->spill_slots, c->status);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(append_pack_k, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
-                     c->base, c->row_flags);
+                     c->base, c->row_flags, nullptr);
   size_t lds = 2 * (size_t)rows * sizeof(uint32_t);
   hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, n, k_new, v_new,
                      c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);

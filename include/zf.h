@@ -37,7 +37,7 @@
  *   row_spill u32[num_pages][page_size]              slot of the row's first raw block
  *   spill     u8 [spill_slots][32]
  *   spill_top u64 (one counter)   status u32 (sticky device error bits, ZF_DEV_*)
- *   append_sync u64[65] (optional; the one-launch append's hand-over words and epoch)
+ *   append_sync u64[66] (optional; the one-launch append's hand-over words, epoch, test hook)
  * Raw (uncompressed) pages use u16[num_pages][H][2][page_size][D], the same page ids.
  *
  * ---------------------------------------------------------------------------------- errors
@@ -71,12 +71,12 @@ typedef enum {
                            than ZF_NOALLOC_SCRATCH_BYTES                                   */
 } zf_status;
 
-#define ZF_DEV_ESPILL 1u  /* spill pool exhausted: the call wrote no spill, kept spill_top */
+#define ZF_DEV_ESPILL 1u  /* spill pool exhausted: spill_top and the slots below it kept   */
 #define ZF_DEV_EPAGE 2u   /* a page-table entry the call needed is out of range           */
 #define ZF_DEV_ELEN 4u    /* a length is negative or beyond the page table / host bound   */
 #define ZF_DEV_ESYNC 8u   /* one-launch append: a hand-over word did not arrive within the
-                             bounded wait (about 1 s; none is expected): the call changed
-                             no defined state; zero the sync area before the next append */
+                             bounded wait (about 1 s; none is expected) or the give-up hook
+                             was set: the call changed no defined state                   */
 
 typedef struct {
   int32_t num_pages, page_size, num_kv_heads, head_dim;
@@ -93,7 +93,10 @@ typedef struct {
                             up, or NULL: see zf_append_kv_n */
 } zf_cache;
 
-#define ZF_APPEND_SYNC_WORDS 65
+/* append_sync: [0, 64) hand-over words, [64] the epoch (calls so far), [65] a test hook: nonzero
+ * makes the one-launch append's packing workgroups give up instead of waiting for the words of
+ * the rows before theirs, so the call ends with ZF_DEV_ESYNC and changes nothing; zero in use. */
+#define ZF_APPEND_SYNC_WORDS 66
 
 typedef struct {
   int32_t batch, max_pages_per_seq;
@@ -103,43 +106,60 @@ typedef struct {
                                 append: on the grown lengths); sizes grids and workspaces   */
 } zf_seqs;
 
-/* Bytes of one cache's arrays except spill, for sizing a pool. */
+/* Bytes of one cache's arrays except spill, for sizing a pool of pages (the paged KV memory of
+ * page "Open Weights: from files to tokens / second", section "09 / The optimization stack"). */
 size_t zf_cache_bytes(int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
                       int32_t head_dim);
 
-/* Initial compression of a prefilled cache (video summary: "initial compression", which the
- * pages leave out of their timings).  Encodes rows t < seq_lens[b] of every sequence from raw
+/* Initial compression of a prefilled cache (ZipFusion video summary, "Run AI Faster With
+ * Lossless Compressed Memory": the initial compression, which its timings leave out, in the
+ * format of chapter "Twelve Bits and One Addition").  Encodes rows t < seq_lens[b] of every sequence from raw
  * pages into the packed planes, takes spill slots from *spill_top in (sequence, token) order
- * and advances it.  If the pool cannot hold them all: ZF_DEV_ESPILL, no spill written,
- * spill_top unchanged, the planes of the rows unspecified.  Workspace: device memory of
- * zf_encode_workspace_bytes(seqs) bytes, any contents. */
+ * and advances it.  If the pool cannot hold them all: ZF_DEV_ESPILL and spill_top unchanged;
+ * the rows' planes and row_spill and the spill slots from spill_top on (within the pool) are
+ * then unspecified.  One pass over the raw pages (the slots by decoupled look-back over the
+ * pages, which waits only for earlier pages of the grid); ZF_DEV_ESYNC if such a wait ran out
+ * (none is expected; spill_top unchanged, the rest as for ESPILL).  Workspace: device memory
+ * of zf_encode_workspace_bytes(seqs) bytes (8 per page of the page table, plus 256), any
+ * contents.  Three launches: workspace clear, encode, finish. */
 zf_status zf_encode_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* raw_pages,
                        void* workspace, size_t workspace_bytes, zf_stream_t stream);
 size_t zf_encode_workspace_bytes(const zf_seqs* seqs);
 
-/* Decode-step append: encodes one new token per sequence (k_new, v_new u16[batch][H][D])
+/* Decode-step append (page "Open Weights: from files to tokens / second", section "03 / The
+ * inference loop": every decode step adds one token's K and V to the cache; ZipFusion video
+ * summary, "Run AI Faster With Lossless Compressed Memory": the cache stays compressed in GPU
+ * memory, so the new row is encoded as it is written; chapter "Twelve Bits and One Addition"
+ * gives the format).  Encodes one new token per sequence (k_new, v_new u16[batch][H][D])
  * into row seq_lens[b] of its page, spill slots from *spill_top in batch order, then
  * seq_lens[b] += 1 for every b.  All or nothing for defined state: on a device error
  * (ZF_DEV_*) seq_lens, spill_top, the spill slots below spill_top and every row
  * t < seq_lens[b] are left as they were; only the rows at position seq_lens[b] and the spill
  * slots from spill_top on, which hold nothing yet, may have been overwritten.  seqs->max_seq_len bounds the lengths after the append.
- * Supports batch <= 4096.  Launches as zf_append_kv_n with n_new = 1. */
+ * Launches as zf_append_kv_n with n_new = 1 (one launch for batch <= 64 with a sync area). */
 zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_t* k_new,
                        const uint16_t* v_new, zf_stream_t stream);
 
-/* Multi-token append (speculative or chunked decode): encodes n_new tokens per sequence
+/* Multi-token append (speculative or chunked decode; page "Open Weights: from files to
+ * tokens / second", section "03 / The inference loop": the cache grows by the tokens each
+ * forward pass processes, in the format of the ZipFusion video summary, "Run AI Faster With
+ * Lossless Compressed Memory").  Encodes n_new tokens per sequence
  * (k_new, v_new u16[batch][n_new][H][D]) into rows seq_lens[b] .. seq_lens[b] + n_new - 1,
  * spill slots from *spill_top in (sequence, token) order, then seq_lens[b] += n_new for every
  * b.  All or nothing, as zf_append_kv (only slots at positions seq_lens[b] and later may have
  * been overwritten after a device error); seqs->max_seq_len bounds the grown lengths.
- * n_new == 0 does nothing; n_new < 0 is ZF_EINVAL.  Supports batch * n_new <= 4096 (callers
- * split longer chunks).  zf_append_kv is the case n_new == 1.
- * Launches: one when cache->append_sync is set and batch * n_new <= 64, else two.  In the
+ * n_new == 0 does nothing; n_new < 0 is ZF_EINVAL.  Supports batch * n_new <= 2^24 new rows.
+ * zf_append_kv is the case n_new == 1.
+ * Launches: one when cache->append_sync is set and batch * n_new <= 64; two up to 4096 new
+ * rows (pack, then one commit workgroup); four beyond (pack; per chunk of 4096 rows a scan,
+ * then the chunk's slots; a last step that checks the whole call and commits).  In the
  * one-launch form the new rows' workgroups hand their flag words to each other through
- * append_sync, words tagged with an epoch that append_sync[64] counts; the area is zero when
- * the cache is set up, holds the last call's words between calls (only these calls may write
- * it), and appends sharing it must not overlap (appends to one cache are ordered anyway: they
- * advance one spill_top).  Both forms write the same bytes. */
+ * append_sync, words tagged with an epoch that append_sync[64] counts (every call advances it,
+ * also one that fails); each workgroup waits only for lower-numbered ones, so no co-residency
+ * is assumed.  The area is zero when the cache is set up, holds the last call's words between
+ * calls (only these calls may write it; an ESYNC needs no clean-up), and appends sharing it
+ * must not overlap (appends to one cache are ordered anyway: they advance one spill_top).
+ * Both forms write the same bytes. */
 zf_status zf_append_kv_n(const zf_cache* cache, const zf_seqs* seqs, int32_t n_new,
                          const uint16_t* k_new, const uint16_t* v_new, zf_stream_t stream);
 
@@ -179,20 +199,28 @@ int64_t zf_max_sequences(int64_t kv_budget_bytes, int32_t layers, int32_t contex
                          int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
                          double raw_blocks_per_row);
 
-/* Inverse of the codec: writes rows t < seq_lens[b] as raw bf16 pages (lossless: the bits
- * that were encoded). */
+/* Inverse of the codec (ZipFusion video summary, "Run AI Faster With Lossless Compressed
+ * Memory", chapter "Lossless or FP8": the compression loses nothing, so the original values
+ * come back exactly): writes rows t < seq_lens[b] as raw bf16 pages, the bits that were
+ * encoded. */
 zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw_pages_out,
                        zf_stream_t stream);
 
-/* Fused decode attention over the packed cache (video summary: values rebuilt in registers
- * by one integer add; no decompressed copy).  q: bf16 u16[batch][num_q_heads][D]; out: f32
- * [batch][num_q_heads][D]; q head i uses kv head i / (num_q_heads / H).  out =
+/* Fused decode attention over the packed cache (ZipFusion video summary, "Run AI Faster With
+ * Lossless Compressed Memory": values rebuilt in registers by one integer add, no decompressed
+ * copy; page "Open Weights: from files to tokens / second", section "03 / The inference loop":
+ * the decode step's attention over the whole cache).  q: bf16 u16[batch][num_q_heads][D]; out:
+ * f32 [batch][num_q_heads][D]; q head i uses kv head i / (num_q_heads / H).  out =
  * softmax(scale * q K^T) V over the sequence's tokens in logical order; zeros when
- * seq_lens[b] == 0.  Workspace: zf_attention_workspace_bytes(...) bytes of device memory, any
- * contents (it holds per-split partials); calls sharing one workspace must not overlap.
+ * seq_lens[b] == 0.  Arithmetic: scores on the matrix cores in fp32, recomputed in fp64 from
+ * the exact bf16 products wherever a weight may reach 2^-40 of the largest; weights, their
+ * sum and the rescales in fp64; products of a value of 2^4 or more summed in fp64; the rest
+ * of p.V on the matrix cores with each weight split into bf16 parts (three, exact, for 4
+ * query heads per kv head; two, within 2^-17 of it, for 8).  Workspace:
+ * zf_attention_workspace_bytes(...) bytes of device memory, any contents (it holds per-split
+ * partials); calls sharing one workspace must not overlap.
  * Requires D == 128, page_size == 16, num_q_heads == 4 * H or 8 * H (Llama-3.1-8B- and
- * 70B-shaped groups; the 8-head kernel carries each weight as two bf16 parts, within 2^-16
- * of it, where the 4-head one carries it exactly in three), max_seq_len <= 2^20 and
+ * 70B-shaped groups), max_seq_len <= 2^20 and
  * spill_slots < 2^27 (the pool is addressed with 32-bit byte offsets) in this
  * version (ZF_EUNSUPPORTED otherwise).  One kernel launch when max_seq_len fits one split per
  * (sequence, kv head), else two (split attention, split merge). */
@@ -215,18 +243,23 @@ zf_status zf_decode_attention_noalloc(const zf_cache* cache, const zf_seqs* seqs
                                       int32_t num_q_heads, float scale, float* out,
                                       zf_stream_t stream);
 
-/* The same attention kernel reading an uncompressed bf16 cache; same split plan and
- * arithmetic, so its output is bitwise identical to zf_decode_attention on the encoded copy
- * of the same pages.  status: device u32 for ZF_DEV_* bits (may not be NULL). */
+/* The same attention kernel reading an uncompressed bf16 cache: the comparator the ZipFusion
+ * video summary ("Run AI Faster With Lossless Compressed Memory") measures its faster attention
+ * against.  Same split plan and arithmetic, so its output is bitwise identical to
+ * zf_decode_attention on the encoded copy of the same pages.  num_pages bounds the page ids;
+ * status: device u32 for ZF_DEV_* bits (may not be NULL). */
 zf_status zf_decode_attention_raw(const uint16_t* raw_pages, int32_t num_pages,
                                   int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
                                   const zf_seqs* seqs, const uint16_t* q, int32_t num_q_heads,
                                   float scale, float* out, void* workspace,
                                   size_t workspace_bytes, uint32_t* status, zf_stream_t stream);
 
+/* Sizing, outside the method: bytes of the split partials an attention call of this shape
+ * needs (a 256-byte header and, per sequence, kv head and split, the running sums). */
 size_t zf_attention_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                                     int32_t head_dim, int32_t max_seq_len);
-/* Zero-fills a workspace on `stream` (a kernel, no memset node); optional. */
+/* Sizing aid, outside the method: zero-fills a workspace on `stream` (a kernel, no memset
+ * node); optional. */
 zf_status zf_attention_workspace_init(void* workspace, size_t workspace_bytes,
                                       zf_stream_t stream);
 
@@ -246,14 +279,10 @@ zf_status zf_time_next_attention(void* start_event, void* stop_event);
 #define ZF_PROBE_BLOCKS 4096
 zf_status zf_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, zf_stream_t stream);
 
-/* Bound on the one-launch append's packing workgroups' wait for each other's hand-over words,
- * in polls (default 1048576, about 1 s), for appends enqueued after the call; process-wide.
- * 0 makes them give up at once, so every one-launch append then ends with ZF_DEV_ESYNC after
- * the commit has waited out its own bound (about 1 s): it lets tests take that path. */
-void zf_set_append_wait_polls(uint32_t polls);
-
-/* Copies the sticky status word to *host_status (synchronizes `stream`). */
+/* Status, outside the method: copies the sticky status word to *host_status (synchronizes
+ * `stream`); a cache's word or the twin's. */
 zf_status zf_get_status(const uint32_t* status, uint32_t* host_status, zf_stream_t stream);
+/* Status, outside the method: a short text for a return code. */
 const char* zf_status_str(zf_status s);
 
 #ifdef __cplusplus

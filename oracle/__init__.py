@@ -38,10 +38,13 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
-            build()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("ZF_ORACLE_LIB")  # another build of the same source (sanitizers)
+        if not path:
+            newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
+                build()
+            path = _LIB
+        lib = ctypes.CDLL(path)
         for name in ("orc_encode_kv", "orc_append_kv", "orc_append_kv_n", "orc_decode_kv",
                      "orc_compact_spill", "orc_attention"):
             getattr(lib, name).restype = ctypes.c_uint32

@@ -50,6 +50,10 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
+        override = os.environ.get("ZF_SYNTH_LIB")  # another build of the same source (sanitizers)
+        if override:
+            _lib = ctypes.CDLL(override)
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build()
         _lib = ctypes.CDLL(_LIB)

@@ -33,6 +33,36 @@ def test_every_declared_function_is_exported():
         assert hasattr(lib, n), n
 
 
+# what a declaration's comment must name: one of the pages (by title), or that it is an aid
+# outside the method, or (the allocation-free variant) the callers it serves
+PAGES = ("Open Weights: from files to tokens / second",
+         "Run AI Faster With Lossless Compressed Memory")
+OTHER = ("outside the method", "callers that cannot allocate")
+
+
+def governing_comments():
+    """Each declared function with the comment block nearest before its declaration (a function
+    declared right after another, without a comment of its own, shares that one)."""
+    text = open(HEADER).read()
+    body = text[text.index("extern \"C\""):]
+    found = {}
+    for m in re.finditer(r"^(?:[a-z_0-9]+\s+)*[a-z_0-9]+\**\s+\**(zf_[a-z_]+)\s*\(", body, flags=re.M):
+        before = body[:m.start()]
+        c = before.rfind("/*")
+        found[m.group(1)] = re.sub(r"\s*\n\s*\*\s*", " ", before[c:before.index("*/", c)])
+    return found
+
+
+def test_every_declaration_cites_a_page_or_says_why_not():
+    found = governing_comments()
+    assert set(found) == set(declared_functions())
+    for name, comment in found.items():
+        assert any(p in comment for p in PAGES + OTHER), (name, comment[:120])
+    for op in ("zf_encode_kv", "zf_append_kv", "zf_append_kv_n", "zf_decode_kv",
+               "zf_decode_attention", "zf_decode_attention_raw"):
+        assert any(p in found[op] for p in PAGES), op
+
+
 def test_cache_bytes_closed_form():
     P, T, H, D = 10, 16, 8, 128
     vals = P * H * 2 * T * D
@@ -52,7 +82,7 @@ def test_attention_workspace_sizes():
 
 def test_encode_workspace_size():
     s = zf.zf_seqs(4, 10, None, None, 160)
-    assert zf.load().zf_encode_workspace_bytes(ctypes.byref(s)) == 256 + 4 * 10 * 4
+    assert zf.load().zf_encode_workspace_bytes(ctypes.byref(s)) == 256 + 4 * 10 * 8  # a look-back word per page
 
 
 def _cache(**kw):
@@ -121,7 +151,7 @@ def test_append_n_arguments():
     s = zf.zf_seqs(64, 1, 4096, 4096, 16)
     assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), -1, 4096, 4096, None) == zf.ZF_EINVAL
     assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 0, None, None, None) == zf.ZF_OK
-    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 65, 4096, 4096, None) == zf.ZF_EUNSUPPORTED
+    assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), (1 << 18) + 1, 4096, 4096, None) == zf.ZF_EUNSUPPORTED
     assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 64, 4096, 4104, None) == zf.ZF_EINVAL
     assert lib.zf_append_kv_n(ctypes.byref(c), ctypes.byref(s), 64, None, 4096, None) == zf.ZF_EINVAL
 

@@ -5,6 +5,7 @@ slots, spill bytes, spill_top), plus the device-side error rules.
 Codec: ZipFusion video summary ("Run AI Faster With Lossless Compressed Memory", chapter
 "Twelve Bits and One Addition"); lossless, so decode must return the encoded bits exactly.
 """
+import dataclasses
 import numpy as np
 import pytest
 import torch
@@ -142,41 +143,43 @@ def test_one_launch_append_with_changing_batch():
     assert int(host(s.cache.append_sync)[64]) == ones
 
 
-def test_one_launch_append_wait_bound_reports_and_changes_nothing():
-    """A zero wait bound makes the packing workgroups give up before they mark their words
-    decided; the commit, which saw every word's tag but no decided mark, waits out its bound:
-    ZF_DEV_ESYNC and no defined state changed.  After the sync words are zeroed, the same
-    append succeeds and matches the oracle."""
+def test_one_launch_append_give_up_reports_and_changes_nothing():
+    """The cache's give-up hook makes every packing workgroup that has rows before it give up
+    instead of waiting for their words: it marks its word abandoned, the commit sees the mark,
+    and the call ends with ZF_DEV_ESYNC, no defined state changed and the epoch advanced.  With
+    the hook cleared the same append succeeds (no clean-up of the sync words) and matches the
+    oracle."""
     w = SMALL
     inst = synth.make(w)
+    assert w.batch >= 2  # a workgroup with a row before it
     s = Setup(inst)
     orc = oracle_cache(inst, s.cache.spill_slots)
     rows = valid_rows(inst)
     names = ("sm", "nib", "base", "row_flags", "row_spill")
     before = {n: host(getattr(s.cache, n)).copy() for n in names}
     top = int(host(s.cache.spill_top)[0])
+    epoch = int(host(s.cache.append_sync)[zf.ZF_SYNC_EPOCH])
     k, v = synth.tokens(w, inst.seq_lens)
-    zf.zf_set_append_wait_polls(0)
-    try:
-        zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
-        torch.cuda.synchronize()
-    finally:
-        zf.zf_set_append_wait_polls(1 << 20)  # the default
+    s.cache.append_sync[zf.ZF_SYNC_GIVE_UP] = 1
+    zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
+    torch.cuda.synchronize()
+    s.cache.append_sync[zf.ZF_SYNC_GIVE_UP] = 0
     assert s.status() & zf.ZF_DEV_ESYNC
+    assert int(host(s.cache.append_sync)[zf.ZF_SYNC_EPOCH]) == epoch + 1
     assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
     assert int(host(s.cache.spill_top)[0]) == top
     for n in names:
         a, b = host(getattr(s.cache, n)), before[n]
         m = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
         assert np.array_equal(a[m], b[m]), n
-    s.cache.append_sync.zero_()
     s.cache.status.zero_()
     lens = inst.seq_lens.copy()
     zf.zf_append_kv(s.cache, s.seqs, dev(k), dev(v))
     assert orc.append(lens, inst.page_table, k, v) == oracle.OK
     torch.cuda.synchronize()
     assert s.status() == 0
-    compare_packed(s.cache, orc, valid_rows(inst, lens), "append after a timed-out one")
+    assert int(host(s.cache.append_sync)[zf.ZF_SYNC_EPOCH]) == epoch + 2
+    compare_packed(s.cache, orc, valid_rows(inst, lens), "append after a given-up one")
 
 
 def test_one_launch_append_bad_page_changes_nothing():
@@ -240,6 +243,39 @@ def test_append_spill_exhaustion_changes_no_defined_state():
     torch.cuda.synchronize()
     assert s2.status() == 0
     compare_packed(s2.cache, orc2, valid_rows(inst, lens), "append after a failed one")
+
+
+@pytest.mark.parametrize("form", ["one", "two"])
+def test_append_partly_fitting_pool_changes_no_defined_state(form):
+    """Room for a few of the new raw blocks but not all: ZF_DEV_ESPILL, lengths, spill_top and
+    every defined row and slot kept; rows whose slots fitted may have written them (slots from
+    spill_top on hold nothing yet), never past the pool's end (guard slots behind a smaller
+    spill_slots stay zero)."""
+    w = SMALL
+    inst = synth.make(w)
+    orc = oracle_cache(inst, 1 << 20)
+    need, room, guard = orc.spill_top, 3, 64
+    s = Setup(inst, spill_slots=need + room + guard, one_launch_append=(form == "one"))
+    c = dataclasses.replace(s.cache, spill_slots=need + room)
+    assert s.status() == 0 and int(host(s.cache.spill_top)[0]) == need
+    rows = valid_rows(inst)
+    names = ("sm", "nib", "base", "row_flags", "row_spill")
+    before = {n: host(getattr(s.cache, n)).copy() for n in names}
+    spill_before = host(s.cache.spill)[:need].copy()
+    k, v = synth.tokens(w, inst.seq_lens)
+    k[:, :, 0] = 0  # every new row gets a raw block: batch > room
+    assert w.batch > room
+    zf.zf_append_kv(c, s.seqs, dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert s.status() & zf.ZF_DEV_ESPILL
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == need
+    assert np.array_equal(host(s.cache.spill)[:need], spill_before)
+    assert not host(s.cache.spill)[need + room:].any()
+    for n in names:
+        a, b = host(getattr(s.cache, n)), before[n]
+        m = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
+        assert np.array_equal(a[m], b[m]), n
 
 
 @pytest.mark.parametrize("form", ["one", "two"])
@@ -314,11 +350,80 @@ def test_append_n_spill_exhaustion_changes_no_defined_state():
     assert s.status() & zf.ZF_DEV_ESPILL
     assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
     assert int(host(s.cache.spill_top)[0]) == need
-    assert np.array_equal(host(s.cache.spill), spill_before)
+    # the defined slots are kept (those from spill_top on hold nothing yet)
+    assert np.array_equal(host(s.cache.spill)[:need], spill_before[:need])
     for n in names:
         a, b = host(getattr(s.cache, n)), before[n]
         m = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
         assert np.array_equal(a[m], b[m]), n
+
+
+# More new rows than one commit workgroup holds (the chunked form): a batch of 32 ragged
+# sequences takes 2048 tokens each in one call (65 536 rows), then 600 more (19 200 rows).
+LONG_APPEND = synth.WORKLOADS[1].replace(name="chunked_append_b32", ctx_min=100, ctx_max=700,
+                                         extra_tokens=2650, seed=31)
+
+
+def test_append_n_chunked_bitexact():
+    w = LONG_APPEND
+    log(f"chunked append parity: workload {w.name}")
+    inst = synth.make(w)
+    s = Setup(inst)
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    lens = inst.seq_lens.copy()
+    for n in (2048, 600):
+        assert w.batch * n > 4096
+        k, v = _chunk_tokens(w, lens, n)
+        zf.zf_append_kv_n(s.cache, s.seqs, dev(k), dev(v))
+        assert orc.append_n(lens, inst.page_table, k, v) == oracle.OK
+        torch.cuda.synchronize()
+        assert s.status() == 0
+        assert np.array_equal(host(s.seqs.seq_lens), lens)
+        compare_packed(s.cache, orc, valid_rows(inst, lens), f"{w.name} ({w.batch} x {n} rows)")
+        log(f"  {w.batch * n} rows: bit-exact, spill_top {orc.spill_top}")
+
+
+@pytest.mark.parametrize("fault", ["spill", "length", "page"])
+def test_append_n_chunked_errors_change_no_defined_state(fault):
+    """The chunked form fails whole: a pool with room for a few raw blocks only (ZF_DEV_ESPILL),
+    one sequence whose new rows pass its page table's end (ZF_DEV_ELEN), or one new row on an
+    out-of-range page id (ZF_DEV_EPAGE).  Lengths, spill_top, every defined row and slot, and
+    the memory past the pool's end stay as they were."""
+    w = LONG_APPEND.replace(batch=8, extra_tokens=700, seed=32)
+    n = 600  # 4800 rows
+    inst = synth.make(w)
+    orc = oracle_cache(inst, 1 << 24)
+    need, guard = orc.spill_top, 64
+    room = 3 if fault == "spill" else 8 * n * 32
+    s = Setup(inst, spill_slots=need + room + guard)
+    c = dataclasses.replace(s.cache, spill_slots=need + room)
+    rows = valid_rows(inst)
+    names = ("sm", "nib", "base", "row_flags", "row_spill")
+    before = {m: host(getattr(s.cache, m)).copy() for m in names}
+    spill_before = host(s.cache.spill)[:need].copy()
+    k, v = _chunk_tokens(w, inst.seq_lens, n)
+    seqs = s.seqs
+    if fault == "spill":
+        k[:, :, :, 0] = 0  # every new row gets a raw block
+    elif fault == "length":
+        seqs = zf.Seqs(s.seqs.page_table, s.seqs.seq_lens, int(inst.seq_lens.max()) + n - 1)
+    else:
+        pt = inst.page_table.copy()
+        b = 5
+        pt[b, (int(inst.seq_lens[b]) + n - 1) // w.page_size] = inst.num_pages + 7
+        seqs = zf.Seqs(dev(pt), s.seqs.seq_lens, s.seqs.max_seq_len)
+    zf.zf_append_kv_n(c, seqs, dev(k), dev(v))
+    torch.cuda.synchronize()
+    want = {"spill": zf.ZF_DEV_ESPILL, "length": zf.ZF_DEV_ELEN, "page": zf.ZF_DEV_EPAGE}[fault]
+    assert s.status() & want
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == need
+    assert np.array_equal(host(s.cache.spill)[:need], spill_before)
+    assert not host(s.cache.spill)[need + room:].any()
+    for m in names:
+        a, b_ = host(getattr(s.cache, m)), before[m]
+        msk = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
+        assert np.array_equal(a[msk], b_[msk]), m
 
 
 # other geometries of the format: head_dim 64 (16 blocks per row), head_dim 256 with 4 kv heads
@@ -346,12 +451,19 @@ def test_other_geometries_encode_append_decode(w):
 
 
 def test_encode_spill_exhaustion_keeps_pool():
+    """One slot short: ZF_DEV_ESPILL and spill_top kept.  The slots inside the pool may hold
+    the pass's nibbles (they are unspecified after a failed encode); memory past the pool's
+    end (guard slots behind a smaller spill_slots) stays untouched."""
     inst = synth.make(SMALL)
     orc = oracle_cache(inst, 1 << 20)
-    s = Setup(inst, spill_slots=orc.spill_top - 1)
+    n, guard = orc.spill_top - 1, 64
+    s = Setup(inst, spill_slots=n + guard, encode=False)
+    short = dataclasses.replace(s.cache, spill_slots=n)
+    zf.zf_encode_kv(short, s.seqs, s.raw, zf.encode_workspace(s.seqs))
+    torch.cuda.synchronize()
     assert s.status() & zf.ZF_DEV_ESPILL
     assert int(host(s.cache.spill_top)[0]) == 0
-    assert not host(s.cache.spill).any()
+    assert not host(s.cache.spill)[n:].any()
     # exactly enough slots: succeeds and fills the pool
     s2 = Setup(inst, spill_slots=orc.spill_top)
     assert s2.status() == 0
