@@ -652,7 +652,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   if (s >= nsplit) return;
 
   // q in fp64, pair order, for the exact-score path: [head][quarter][pair] = (lo, hi) dims
-  __shared__ double2 s_q64[G][4][16];
+  // (rows of 17 pairs: the four quarters read in one instruction fall in different banks)
+  __shared__ double2 s_q64[G][4][17];
   if (tid < G * 64) {
     const int i = tid >> 6, qq = (tid >> 4) & 3, k = tid & 15;
     const int dlo = 32 * qq + 8 * (k >> 2) + (k & 3);

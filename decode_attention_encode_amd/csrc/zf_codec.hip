@@ -51,7 +51,6 @@ constexpr uint64_t kLbAggregate = (uint64_t)1 << 62;
 constexpr uint64_t kLbInclusive = (uint64_t)2 << 62;
 constexpr uint64_t kLbValue = ((uint64_t)1 << 62) - 1u;
 constexpr uint32_t kLbPolls = 1u << 22;  // bound on one look-back wait (~ seconds; none is expected)
-constexpr int kEncChunks = 16;           // 16-byte loads in flight per thread
 
 // Pages of sequence b that hold tokens (0 for an invalid length).
 __device__ __forceinline__ int pages_of(const SeqView& s, const Geom& g, int b) {
@@ -108,6 +107,13 @@ __device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* l
   }
 }
 
+// Encode of one (sequence, logical page): 4 lanes per 64-value block, 16 values each (two
+// 16-byte loads).  The first kEncSweeps sweeps of 256 chunks (a whole page of 512 blocks)
+// keep their raw blocks' spill nibbles in registers until the page's slots are known; a larger
+// page's later sweeps read their raw blocks again for them.
+constexpr int kEncSweeps = 8;
+constexpr int kEncUnroll = 4;
+
 __global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* __restrict__ raw,
                                              uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
                                              uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags,
@@ -134,61 +140,73 @@ __global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* 
 
   const int nb = g.nb();
   const int blocks = 2 * g.H * g.T * nb;
-  const int64_t page_vals = g.vals_per_page();
-  const int lane8 = tid & 7;
-  const int64_t page0 = (int64_t)(rows > 0 ? pid : 0) * page_vals;
-  // Classify blocks m0 + 32 i + tid / 8 (i < kEncChunks): all loads first, then per block the
-  // exponent window over its 8 lanes, the planes and the row flag bits.  Returns the raw
-  // blocks' spill nibbles (hiw[i]) and which chunks are raw (the mask).
-  auto classify = [&](int m0, uint32_t (&hiw)[kEncChunks]) -> uint32_t {
-    uint32_t w[kEncChunks][4];
+  const int chunks = blocks * 4;  // 16 values each; chunk k: block k / 4, quarter k % 4
+  const int64_t page0 = (int64_t)(rows > 0 ? pid : 0) * g.vals_per_page();
+  auto live = [&](int k) { return k < chunks && ((k >> 2) / nb) % g.T < rows; };
+  // Classify chunks k0 + 256 u (u < kEncUnroll): loads first, then per chunk its 16 exponents,
+  // the block's window over its 4 lanes (uniform over them), the planes and the row flag bit.
+  // hio[u]: the chunk's spill nibbles (raw blocks); the return value: which chunks are raw.
+  auto classify = [&](int k0, uint2 (&hio)[kEncUnroll]) -> uint32_t {
+    uint4 lo[kEncUnroll], hi[kEncUnroll];
 #pragma unroll
-    for (int i = 0; i < kEncChunks; ++i) {
-      const int m = m0 + 32 * i + (tid >> 3);
-      if (m < blocks && (m / nb) % g.T < rows) {
-        const uint4 in = *reinterpret_cast<const uint4*>(raw + page0 + (int64_t)m * kBlock + lane8 * 8);
-        w[i][0] = in.x;
-        w[i][1] = in.y;
-        w[i][2] = in.z;
-        w[i][3] = in.w;
+    for (int u = 0; u < kEncUnroll; ++u) {
+      const int k = k0 + 256 * u;
+      if (live(k)) {
+        const uint4* src = reinterpret_cast<const uint4*>(raw + page0 + (int64_t)(k >> 2) * kBlock + (k & 3) * 16);
+        lo[u] = src[0];
+        hi[u] = src[1];
       }
     }
     uint32_t raw_mask = 0u;
 #pragma unroll
-    for (int i = 0; i < kEncChunks; ++i) {
-      const int m = m0 + 32 * i + (tid >> 3);
-      const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
-      hiw[i] = 0u;
-      if (m < blocks && slot < rows) {  // uniform over the 8 lanes of the block
-        Window win = window8(w[i]);
+    for (int u = 0; u < kEncUnroll; ++u) {
+      const int k = k0 + 256 * u, m = k >> 2, qtr = k & 3;
+      hio[u] = make_uint2(0u, 0u);
+      if (!live(k)) continue;  // uniform over the 4 lanes of the block
+      const uint32_t w0[4] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w};
+      const uint32_t w1[4] = {hi[u].x, hi[u].y, hi[u].z, hi[u].w};
+      Window a = window8(w0);
+      const Window c = window8(w1);
+      a.emin = min(a.emin, c.emin);
+      a.emax = max(a.emax, c.emax);
+      a.special |= c.special;
 #pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-          win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
-          win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
-          win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
-        }
-        const uint32_t raw_blk = win.special | (uint32_t)(win.emax - win.emin > 15u);
-        const uint32_t bexp = raw_blk ? 0u : win.emin;
-        uint32_t smw[2], nibw;
-        pack8(w[i], bexp, raw_blk, smw, nibw, hiw[i]);
-        const int64_t v0 = page0 + (int64_t)m * kBlock + lane8 * 8;
-        *reinterpret_cast<uint2*>(sm + v0) = make_uint2(smw[0], smw[1]);
-        *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = nibw;
-        raw_mask |= raw_blk << i;
-        if (lane8 == 0) {
-          base[v0 / kBlock] = (uint8_t)bexp;
-          if (raw_blk) atomicOr(&s_flags[slot], 1u << (hk * nb + half));
+      for (int o = 1; o < 4; o <<= 1) {
+        a.emin = min(a.emin, (uint32_t)__shfl_xor((int)a.emin, o, 4));
+        a.emax = max(a.emax, (uint32_t)__shfl_xor((int)a.emax, o, 4));
+        a.special |= (uint32_t)__shfl_xor((int)a.special, o, 4);
+      }
+      const uint32_t raw_blk = a.special | (uint32_t)(a.emax - a.emin > 15u);
+      const uint32_t bexp = raw_blk ? 0u : a.emin;
+      uint32_t sm0[2], sm1[2], n0, n1;
+      pack8(w0, bexp, raw_blk, sm0, n0, hio[u].x);
+      pack8(w1, bexp, raw_blk, sm1, n1, hio[u].y);
+      const int64_t v0 = page0 + (int64_t)m * kBlock + qtr * 16;
+      *reinterpret_cast<uint4*>(sm + v0) = make_uint4(sm0[0], sm0[1], sm1[0], sm1[1]);
+      *reinterpret_cast<uint2*>(nib + (v0 >> 1)) = make_uint2(n0, n1);
+      raw_mask |= raw_blk << u;
+      if (qtr == 0) {
+        base[v0 / kBlock] = (uint8_t)bexp;
+        if (raw_blk) {
+          const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+          atomicOr(&s_flags[slot], 1u << (hk * nb + half));
         }
       }
     }
     return raw_mask;
   };
-  constexpr int kGroup = kEncChunks * 32;  // blocks per group of sweeps
-  uint32_t hiw0[kEncChunks];
-  const uint32_t mask0 = classify(0, hiw0);  // the first group's spill nibbles stay in registers
-  for (int m0 = kGroup; m0 < blocks; m0 += kGroup) {  // pages of more than 512 blocks
-    uint32_t hiw[kEncChunks];
-    classify(m0, hiw);
+  uint2 hik[kEncSweeps];
+  uint32_t rawm = 0u;
+#pragma unroll
+  for (int gi = 0; gi < kEncSweeps / kEncUnroll; ++gi) {
+    uint2 h[kEncUnroll];
+    rawm |= classify(tid + 256 * kEncUnroll * gi, h) << (kEncUnroll * gi);
+#pragma unroll
+    for (int u = 0; u < kEncUnroll; ++u) hik[kEncUnroll * gi + u] = h[u];
+  }
+  for (int k0 = tid + 256 * kEncSweeps; k0 < chunks; k0 += 256 * kEncUnroll) {  // larger pages
+    uint2 h[kEncUnroll];
+    classify(k0, h);
   }
   __syncthreads();
 
@@ -218,7 +236,7 @@ __global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* 
   }
   __syncthreads();
 
-  // spill slots: the first group's from registers, any later group's from the raw input again
+  // spill slots: 8 bytes per chunk of a raw block
   const uint64_t top = *spill_top;
   auto slot_of = [&](int m) -> uint64_t {
     const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
@@ -226,23 +244,29 @@ __global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* 
     return top + s_first[slot] + __popc(s_flags[slot] & ((1u << j) - 1u));
   };
 #pragma unroll
-  for (int i = 0; i < kEncChunks; ++i) {
-    if (!((mask0 >> i) & 1u)) continue;
-    const uint64_t idx = slot_of(32 * i + (tid >> 3));
+  for (int i = 0; i < kEncSweeps; ++i) {
+    if (!((rawm >> i) & 1u)) continue;
+    const int k = tid + 256 * i;
+    const uint64_t idx = slot_of(k >> 2);
     if (idx < spill_slots)  // a pool too small for the call: slots past its end are skipped
-      *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hiw0[i];
+      *reinterpret_cast<uint2*>(spill + idx * 32u + (k & 3) * 8) = hik[i];
   }
-  for (int m = kGroup + (tid >> 3); m < blocks; m += 32) {
-    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+  for (int k = tid + 256 * kEncSweeps; k < chunks; k += 256) {  // larger pages
+    const int m = k >> 2, half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
     if (slot >= rows || !((s_flags[slot] >> (hk * nb + half)) & 1u)) continue;
     const uint64_t idx = slot_of(m);
     if (idx >= spill_slots) continue;
-    const uint4 in = *reinterpret_cast<const uint4*>(raw + page0 + (int64_t)m * kBlock + lane8 * 8);
-    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    uint32_t hi = 0u;
+    const uint4* src = reinterpret_cast<const uint4*>(raw + page0 + (int64_t)m * kBlock + (k & 3) * 16);
+    uint32_t hv[2];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
-    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint4 in = src[h2];
+      const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+      hv[h2] = 0u;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) hv[h2] |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
+    }
+    *reinterpret_cast<uint2*>(spill + idx * 32u + (k & 3) * 8) = make_uint2(hv[0], hv[1]);
   }
 }
 
@@ -889,6 +913,13 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
 
 // ------------------------------------------------------------------------------ decode
 
+// One workgroup per (sequence, logical page).  The page's row flags, spill indices and block
+// bases are staged in LDS first; then each lane rebuilds 16 values (a quarter of a block) per
+// step from one 16-byte sm load, one 8-byte nibble load and, for a raw block, one 8-byte spill
+// load, and writes 32 bytes.  Four steps per lane are unrolled so their loads fly together.
+constexpr int kDecUnroll = 4;
+constexpr int kMaxPageBlocks = 32 * 64;  // 32 blocks per row, 64 rows per page at most
+
 __global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t* __restrict__ sm,
                                                 const uint8_t* __restrict__ nib, const uint8_t* __restrict__ base,
                                                 const uint32_t* __restrict__ row_flags,
@@ -908,56 +939,59 @@ __global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t
     if (tid == 0) set_status(status, ZF_DEV_EPAGE);
     return;
   }
+  const int nb = g.nb();
+  const int blocks = 2 * g.H * g.T * nb;
   __shared__ uint32_t s_f[64], s_sp[64];
+  __shared__ uint8_t s_base[kMaxPageBlocks];
   if (tid < rows) {
     s_f[tid] = row_flags[(int64_t)pid * g.T + tid];
     s_sp[tid] = row_spill[(int64_t)pid * g.T + tid];
   }
+  const uint8_t* bsrc = base + (int64_t)pid * blocks;
+  for (int m = tid; m < blocks; m += 256) s_base[m] = bsrc[m];
   __syncthreads();
-  const int nb = g.nb();
-  const int blocks = 2 * g.H * g.T * nb;
-  const int lane8 = tid & 7;
   const int64_t page0 = (int64_t)pid * g.vals_per_page();
+  const int chunks = blocks * 4;  // 16 values each
   uint32_t err = 0;
-  // blocks m0 + 32 i + tid / 8: every load of a group issued before the first rebuild
-  for (int m0 = 0; m0 < blocks; m0 += kEncChunks * 32) {
-    uint2 smw[kEncChunks];
-    uint32_t nibw[kEncChunks], bp[kEncChunks], hi[kEncChunks];
+  for (int k0 = tid; k0 < chunks; k0 += 256 * kDecUnroll) {
+    uint4 smw[kDecUnroll];
+    uint2 nibw[kDecUnroll], hiw[kDecUnroll];
+    uint32_t bp[kDecUnroll];
+    bool live[kDecUnroll];
 #pragma unroll
-    for (int i = 0; i < kEncChunks; ++i) {
-      const int m = m0 + 32 * i + (tid >> 3);
-      if (m < blocks && (m / nb) % g.T < rows) {
-        const int64_t v0 = page0 + (int64_t)m * kBlock + lane8 * 8;
-        smw[i] = *reinterpret_cast<const uint2*>(sm + v0);
-        nibw[i] = *reinterpret_cast<const uint32_t*>(nib + (v0 >> 1));
-        bp[i] = base[v0 / kBlock];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kEncChunks; ++i) {
-      const int m = m0 + 32 * i + (tid >> 3);
-      const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
-      hi[i] = 0u;
-      if (m < blocks && slot < rows) {
-        const uint32_t f = s_f[slot];
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int k = k0 + 256 * u, m = k >> 2, qtr = k & 3;
+      live[u] = k < chunks && (m / nb) % g.T < rows;
+      hiw[u] = make_uint2(0u, 0u);
+      bp[u] = 0u;
+      if (live[u]) {
+        const int64_t v0 = page0 + (int64_t)m * kBlock + qtr * 16;
+        smw[u] = *reinterpret_cast<const uint4*>(sm + v0);
+        nibw[u] = *reinterpret_cast<const uint2*>(nib + (v0 >> 1));
+        const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
         const int j = hk * nb + half;
+        const uint32_t f = s_f[slot];
         if ((f >> j) & 1u) {
           const uint64_t idx = (uint64_t)s_sp[slot] + __popc(f & ((1u << j) - 1u));
-          if (idx < spill_slots) hi[i] = *reinterpret_cast<const uint32_t*>(spill + idx * 32u + lane8 * 4);
+          if (idx < spill_slots) hiw[u] = *reinterpret_cast<const uint2*>(spill + idx * 32u + qtr * 8);
           else err = ZF_DEV_ESPILL;
-          bp[i] = 0u;
+        } else {
+          bp[u] = (uint32_t)s_base[m] * 0x00010001u;
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kEncChunks; ++i) {
-      const int m = m0 + 32 * i + (tid >> 3);
-      if (m < blocks && (m / nb) % g.T < rows) {
-        uint32_t pr[4], w[4];
-        rebuild8(smw[i].x, smw[i].y, nibw[i], hi[i], bp[i] * 0x00010001u, pr);
-        pairs_to_natural(pr, w);
-        *reinterpret_cast<uint4*>(out + page0 + (int64_t)m * kBlock + lane8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+    for (int u = 0; u < kDecUnroll; ++u) {
+      if (!live[u]) continue;
+      const int k = k0 + 256 * u, m = k >> 2, qtr = k & 3;
+      uint32_t pr[4], w0[4], w1[4];
+      rebuild8(smw[u].x, smw[u].y, nibw[u].x, hiw[u].x, bp[u], pr);
+      pairs_to_natural(pr, w0);
+      rebuild8(smw[u].z, smw[u].w, nibw[u].y, hiw[u].y, bp[u], pr);
+      pairs_to_natural(pr, w1);
+      uint4* dst = reinterpret_cast<uint4*>(out + page0 + (int64_t)m * kBlock + qtr * 16);
+      dst[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+      dst[1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
     }
   }
   if (err) set_status(status, err);
