@@ -75,6 +75,10 @@ def parse():
                                                        "CAL_WRITE_DIR"),
                     help="only summarize rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (of this "
                          "bench and of --calibrate-copy) into OUT (JSON) and exit")
+    ap.add_argument("--codec", action="store_true",
+                    help="only time full-cache encode and decode (the batch-32 layer and the "
+                         "4 x 131072-token cache) and a prefill written as chunked appends, one "
+                         "JSON line each, and exit")
     ap.add_argument("--per-config", default="",
                     help="only time the attention call on these workloads (e.g. 1,2,3,4: the "
                          "parity configurations; d1, d2, d8: their diffuse-softmax forms), one "
@@ -111,6 +115,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "launches": 3}))
+        return
+    if args.codec:
+        for wi in (1, 4):
+            print(json.dumps(full_cache_codec(torch, zf, synth, wi, dev)), flush=True)
+        print(json.dumps(prefill_chunks(torch, zf, synth, dev)), flush=True)
         return
     if args.per_config:
         for key in args.per_config.split(","):
@@ -256,7 +265,9 @@ def main():
     if args.extras:
         extra.update(extras(torch, zf, inst, layers, raw, q_dev[NS - 1], ws, out, scale,
                             attn_bytes.mean(), row_bytes))
+        extra.update(full_cache_codec(torch, zf, synth, 1, dev))
         extra.update(full_cache_codec(torch, zf, synth, 4, dev))
+        extra.update(prefill_chunks(torch, zf, synth, dev))
         if not args.no_cpu_baseline:
             extra["oracle_single_thread"] = oracle_ops(w, inst, lens0, ks, vs, qs)
 
@@ -649,6 +660,63 @@ def pmc_summary(out, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
         res["hbm_bytes_per_launch"] = attn["hbm_read_bytes_per_dispatch"] + attn["hbm_write_bytes_per_dispatch"]
     json.dump(res, open(out, "w"), indent=1)
     print(json.dumps(res, indent=1))
+
+
+def prefill_chunks(torch, zf, synth, dev, n=512, chunks=4):
+    """A prefill written as multi-token appends: 32 sequences take `chunks` chunks of `n`
+    tokens each (16 384 rows per call, the chunked form) into an empty cache, each call timed
+    with HIP events; rows/s against the full-cache encode of the same rows."""
+    w = synth.WORKLOADS[1].replace(name="prefill_b32", ctx_min=n * chunks, ctx_max=n * chunks,
+                                   extra_tokens=0, seed=71)
+    inst = synth.make(w)
+    B, H, D, T = w.batch, w.num_kv_heads, w.head_dim, w.page_size
+    to = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    # the tokens of each chunk, [B][n][H][D], from the same pages the encode reads
+    pages = inst.raw_pages
+    kv = []
+    for c in range(chunks):
+        t = np.arange(c * n, (c + 1) * n)
+        pg = inst.page_table[:, t // T]                       # [B][n]
+        x = pages[pg, :, :, (t % T)[None, :], :]              # [B][n][H][2][D]
+        kv.append((to(np.ascontiguousarray(x[:, :, :, 0])), to(np.ascontiguousarray(x[:, :, :, 1]))))
+    rows = B * n * chunks
+    stream = torch.cuda.current_stream()
+
+    def run(timed):
+        cache = zf.PackedCache.empty(inst.num_pages, T, H, D, rows * 2 * H * (D // 64), device=dev)
+        seqs = zf.Seqs(to(inst.page_table), torch.zeros(B, dtype=torch.int32, device=dev), n * chunks)
+        ev = []
+        for k, v in kv:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            zf.zf_append_kv_n(cache, seqs, k, v)
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        assert zf.zf_get_status(cache.status) == 0
+        return cache, seqs, [a.elapsed_time(b) / 1e3 for a, b in ev]
+    run(False)
+    cache, seqs, ts = run(True)
+    # the same rows by one full-cache encode
+    raw = to(inst.raw_pages)
+    c2 = zf.PackedCache.empty(inst.num_pages, T, H, D, cache.spill_slots, device=dev)
+    ws = zf.encode_workspace(seqs)
+    zf.zf_encode_kv(c2, seqs, raw, ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c2.spill_top.zero_()
+    a.record(stream)
+    zf.zf_encode_kv(c2, seqs, raw, ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    t_enc = a.elapsed_time(b) / 1e3
+    same = all(torch.equal(getattr(cache, f), getattr(c2, f)) for f in ("sm", "nib", "base", "row_flags"))
+    return {"prefill_chunk_tokens_per_seq": n, "prefill_chunk_rows": B * n,
+            "prefill_chunk_us": [round(t * 1e6, 1) for t in ts],
+            "prefill_chunked_rows_per_s": round(rows / sum(ts), 1),
+            "prefill_encode_rows_per_s": round(rows / t_enc, 1),
+            "prefill_chunked_vs_encode_time": round(sum(ts) / t_enc, 3),
+            "prefill_chunked_planes_equal_encode": bool(same)}
 
 
 def fp32_scale(head_dim: int) -> float:

@@ -84,9 +84,11 @@ constexpr double kSigBits = 40.0;
 constexpr int kFlushPages = 4;
 // The exact-path test takes the largest score that the waves of the workgroup had seen
 // kShareLag steps earlier as a lower bound of the final maximum (it depends on the data only,
-// not on timing, so results stay bitwise repeatable).  A wave waits when it gets more than
-// kShareLag steps ahead of the slowest one; ring slots are reused after kShareRing steps.
-constexpr int kShareLag = 3;
+// not on timing, so results stay bitwise repeatable), and on the first step the largest of
+// the waves' first pages, which they exchange before any of them tests its own.  A wave waits
+// when it gets more than kShareLag steps ahead of the slowest one; ring slots are reused after
+// kShareRing steps.
+constexpr int kShareLag = 1;
 constexpr int kShareRing = 8;  // > 2 * kShareLag: no slot is rewritten while it may be read
 constexpr uint32_t kDone = 0x7FFFFFFFu;  // progress of a wave that has finished its pages
 constexpr int kOrderMaxBatch = 256;  // longest-first group order up to this batch (LDS scratch)
@@ -156,6 +158,9 @@ __device__ __forceinline__ uint32_t lds_load_u32(uint32_t addr) {
 }
 __device__ __forceinline__ void lds_max_f64(uint32_t addr, double v) {
   asm volatile("ds_max_f64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_add_u32(uint32_t addr, uint32_t v) {
+  asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 __device__ __forceinline__ double lds_load_f64(uint32_t addr) {
   double v;
@@ -669,6 +674,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   // lane n holds the page id of page n < nmine
   const int p_end = min(npages, (s + 1) * a.pps);
   const int nmine = p_first < p_end ? (p_end - p_first + kWaves - 1) / kWaves : 0;
+  const uint32_t nact = (uint32_t)max(0, min(kWaves, p_end - s * a.pps));  // waves with pages
   int32_t my_pid = 0;
   uint32_t err = 0;
   if (lane < nmine) {
@@ -683,6 +689,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
   __shared__ double s_gmax[kShareRing][G];  // per step: max over the waves' running maxima
   if (tid < kShareRing * G) s_gmax[tid / G][tid % G] = -INFINITY;
+  __shared__ double s_first_max[G];  // max over the waves' first pages
+  __shared__ uint32_t s_first_count;  // waves that have added their first page to it
+  if (tid < G) s_first_max[tid] = -INFINITY;
+  if (tid == 0) s_first_count = 0u;
   if (lane == 0) s_prog[wave] = nmine > 0 ? 0u : kDone;
   __syncthreads();
 
@@ -722,6 +732,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   auto slot_of = [&](int n) -> uint32_t { return ring + (uint32_t)(n & 1) * kSlotBytes; };
   auto meta_of = [&](int n) -> uint32_t { return meta_ring + (uint32_t)(n & (kMetaRing - 1)) * kMetaBytes; };
 
+  const uint32_t first_max_addr = (uint32_t)(uintptr_t)&s_first_max[head];
+  const uint32_t first_count_addr = (uint32_t)(uintptr_t)&s_first_count;
   auto compute = [&](const int n, const typename Loader::Page& pg) {
     const int ntok = ntok_at(n);
     uint32_t kp[16];
@@ -738,6 +750,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       for (int i = 0; i < 4; ++i) sc[i] = qd + 4 * i < ntok ? sc[i] : -INFINITY;
     }
     const float pm32 = rows_max(max_f32(max3_f32(sc[0], sc[1], sc[2]), sc[3]));
+    if (n == 0) {
+      // every wave with pages adds its first page's maximum, then waits for the others (they
+      // all start together, so the wait is short) and takes the largest as its lower bound
+      if (lane < 16 && part == 0) lds_max_f64(first_max_addr, (double)pm32);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the maximum lands before the count
+      if (lane == 0) lds_add_u32(first_count_addr, 1u);
+      while (lds_load_u32(first_count_addr) < nact) __builtin_amdgcn_s_sleep(1);
+      shared32 = max_f32(shared32, (float)lds_load_f64(first_max_addr));
+    }
     // A score is significant unless it lies more than kSigBits / c2 below a lower bound of the
     // final maximum (the wave's running maximum, this page's, and the workgroup's of a few steps
     // ago): only then is its weight sure to stay under 2^-kSigBits of the largest one.  The
@@ -1028,7 +1049,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
           __builtin_amdgcn_s_sleep(1);
           prog = lds_load_u32(prog_base + 4 * (lane & (kWaves - 1)));
         }
-        shared32 = (float)lds_load_f64(gmax_at(n - lag));
+        shared32 = max_f32(shared32, (float)lds_load_f64(gmax_at(n - lag)));
       }
       if ((uint32_t)n + 1 > __builtin_amdgcn_readlane(prog, wave ^ 4)) __builtin_amdgcn_s_setprio(0);
       else __builtin_amdgcn_s_setprio(2);
