@@ -616,13 +616,14 @@ def oracle_ops(w, inst, lens0, ks, vs, qs):
 
 
 def _pmc_rows(d: str):
-    """(kernel name, counter, value) of every dispatch in the rocprofv3 counter CSVs under d."""
+    """(kernel name and grid size, counter, value) of every dispatch in the rocprofv3 counter
+    CSVs under d."""
     import csv
     import glob
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+            rows.append((f'{r["Kernel_Name"]}|{r["Grid_Size"]}', r["Counter_Name"], float(r["Counter_Value"])))
     return rows
 
 
@@ -642,7 +643,9 @@ def pmc_summary(out, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     ff, wf = n / (cal_f * 1024), n / (cal_w * 1024)
     kernels = {}
     for name in sorted({k for k, _, _ in fetch} | {k for k, _, _ in write}):
-        short = name.split("(")[0]
+        short = name.split("(")[0] + " grid " + name.rsplit("|", 1)[1]
+        if short.startswith("void "):
+            short = short[5:]
         if not short.startswith("zf::"):
             continue
         f, nf = _per_dispatch(fetch, "FETCH_SIZE", lambda k: k == name)
@@ -655,7 +658,8 @@ def pmc_summary(out, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
            "calibration": {"copy_bytes_read": n, "copy_bytes_written": n, "FETCH_SIZE_KiB": cal_f,
                            "WRITE_SIZE_KiB": cal_w, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
            "kernels": kernels}
-    attn = next((v for k, v in kernels.items() if k.startswith("zf::attn_k<zf::PackedLoader")), None)
+    attn = max((v for k, v in kernels.items() if k.startswith("zf::attn_k<zf::PackedLoader")),
+               key=lambda v: v["dispatches"], default=None)
     if attn and attn["hbm_read_bytes_per_dispatch"] is not None and attn["hbm_write_bytes_per_dispatch"] is not None:
         res["hbm_bytes_per_launch"] = attn["hbm_read_bytes_per_dispatch"] + attn["hbm_write_bytes_per_dispatch"]
     json.dump(res, open(out, "w"), indent=1)

@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kScanThreads) void append_chunk_scan_k(Geom g, SeqV
 __device__ uint64_t chunks_before(const Geom& g, const SeqView& s, int n, int c,
                                   const uint32_t* row_spill) {
   uint64_t part = 0;
-  for (int k = threadIdx.x; k < c; k += kScanThreads) {
+  for (int k = threadIdx.x; k < c; k += blockDim.x) {
     uint32_t e;
     const int r = k * kChunkRows;
     const int64_t row = append_row(g, s, r / n, r % n, n, &e);
@@ -668,46 +668,68 @@ __device__ uint64_t chunks_before(const Geom& g, const SeqView& s, int n, int c,
   return r;
 }
 
-__global__ __launch_bounds__(kScanThreads) void append_chunk_commit_k(
+// kCommitRows rows of one chunk per workgroup: their final row_spill entries (but a chunk's
+// first row's) and their raw blocks' spill slots.
+constexpr int kCommitRows = 16;
+static_assert(kChunkRows % kCommitRows == 0, "a commit workgroup stays inside one chunk");
+
+__global__ __launch_bounds__(256) void append_chunk_commit_k(
     Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint32_t* __restrict__ row_flags, uint32_t* row_spill, uint8_t* spill,
     const uint64_t* spill_top, uint64_t spill_slots) {
-  __shared__ uint32_t s_flags[kChunkRows], s_first[kChunkRows];
-  const int R = s.B * n, c = blockIdx.x, r0 = c * kChunkRows, tid = threadIdx.x;
-  const int rows = min(kChunkRows, R - r0);
+  __shared__ uint32_t s_flags[kCommitRows], s_first[kCommitRows];
+  const int R = s.B * n, r0 = blockIdx.x * kCommitRows, tid = threadIdx.x;
+  const int c = r0 / kChunkRows, rows = min(kCommitRows, R - r0);
   const uint64_t before = *spill_top + chunks_before(g, s, n, c, row_spill);
-  for (int i = tid; i < rows; i += kScanThreads) {
-    const int r = r0 + i;
+  if (tid < rows) {
+    const int r = r0 + tid;
     uint32_t e;
     const int64_t row = append_row(g, s, r / n, r % n, n, &e);
     uint32_t f = 0u, local = 0u;
+    const bool first = r % kChunkRows == 0;  // its entry holds the chunk's total
     if (row >= 0) {
       f = row_flags[row];
-      local = i == 0 ? 0u : row_spill[row];
+      local = first ? 0u : row_spill[row];
     }
-    s_flags[i] = f;
-    s_first[i] = local;
-    if (row >= 0 && i > 0) row_spill[row] = (uint32_t)(before + local);
+    s_flags[tid] = f;
+    s_first[tid] = local;
+    if (row >= 0 && !first) row_spill[row] = (uint32_t)(before + local);
   }
   __syncthreads();
-  // spill slots of the raw blocks: 8 lanes per block, blocks walked in (row, block) order
+  // spill slots of the raw blocks: 8 lanes per block, two blocks per step so that their loads
+  // fly together
   const int nb = g.nb(), D = g.D, H = g.H;
   const uint32_t rb = 2u * H * nb, nblk = (uint32_t)rows * rb;
   const int lane8 = tid & 7;
-  for (uint32_t m = tid >> 3; m < nblk; m += kScanThreads >> 3) {
-    const uint32_t i = m / rb, j = m - i * rb;
-    const uint32_t f = s_flags[i];
-    if (!((f >> j) & 1u)) continue;
-    const uint64_t idx = before + s_first[i] + __popc(f & ((1u << j) - 1u));
-    if (idx >= spill_slots) continue;  // the call fails in the last step
-    const uint32_t hk = j / nb, half = j - hk * nb, h = hk >> 1, kv = hk & 1;
-    const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)(r0 + i) * H + h) * D +
-                                                     half * kBlock + lane8 * 8);
-    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    uint32_t hi = 0u;
+  for (uint32_t m0 = tid >> 3; m0 < nblk; m0 += 2 * (256 >> 3)) {
+    uint4 in[2];
+    uint64_t idx[2];
+    bool take[2];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
-    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t m = m0 + u * (256 >> 3);
+      take[u] = false;
+      if (m >= nblk) continue;
+      const uint32_t i = m / rb, j = m - i * rb;
+      const uint32_t f = s_flags[i];
+      idx[u] = before + s_first[i] + __popc(f & ((1u << j) - 1u));
+      // (a slot past the pool: the call fails in the last step)
+      take[u] = ((f >> j) & 1u) && idx[u] < spill_slots;
+      if (take[u]) {
+        const uint32_t hk = j / nb, half = j - hk * nb, h = hk >> 1, kv = hk & 1;
+        in[u] = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)(r0 + i) * H + h) * D +
+                                                half * kBlock + lane8 * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!take[u]) continue;
+      const uint32_t w[4] = {in[u].x, in[u].y, in[u].z, in[u].w};
+      uint32_t hi = 0u;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
+      *reinterpret_cast<uint32_t*>(spill + idx[u] * 32u + lane8 * 4) = hi;
+    }
   }
 }
 
@@ -1157,7 +1179,8 @@ hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int
     hipLaunchKernelGGL(append_pack_k, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
                        c->base, c->row_flags, c->row_spill);
     hipLaunchKernelGGL(append_chunk_scan_k, dim3(nchunks), dim3(kScanThreads), 0, st, g, s, n, c->row_spill);
-    hipLaunchKernelGGL(append_chunk_commit_k, dim3(nchunks), dim3(kScanThreads), 0, st, g, s, n, k_new,
+    hipLaunchKernelGGL(append_chunk_commit_k, dim3((rows + kCommitRows - 1) / kCommitRows), dim3(256), 0, st,
+                       g, s, n, k_new,
                        v_new, c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots);
     hipLaunchKernelGGL(append_chunk_finish_k, dim3(1), dim3(kScanThreads), 0, st, g, s, n, c->row_spill,
                        c->spill_top, c->spill_slots, c->status);
