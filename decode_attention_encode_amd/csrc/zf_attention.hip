@@ -25,8 +25,8 @@
 //   pairs.  The hi row goes to fp64 every page, mid and lo stay in the MFMA accumulators.
 //   Softmax: running max in fp64, raised (with an fp64 rescale) only when a page exceeds it.
 //   Precise path: every score whose weight may reach 2^-40 of the final maximum is recomputed
-//   in fp64 from the exact bf16 products and weighted with an fp64 exp; the weight sums carry
-//   those fp64 weights.  An output that one large value dominates must be right to ~1e-9
+//   in fp64 from the exact bf16 products (on the fp64 matrix cores, v_mfma_f64_4x4x4_4b) and
+//   weighted with an fp64 exp; the weight sums carry those fp64 weights.  An output that one large value dominates must be right to ~1e-9
 //   before its one rounding (the 1e-3 bar is an fp32 ulp at 2^14), and the matrix cores' fp32
 //   scores are only good to ~1e-6 of a weight.
 //   Large values: a lane's 8 values of a V row holding a magnitude >= 2^4 leave the p.V MFMA
@@ -772,68 +772,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
     double sd[4], pm;
     const bool exact = __any(big);
     if (exact) {
-      // exact fp64 scores for the heads that hold a significant score: lane (t, qd) sums its 32
-      // dims of token krow(t) for each of them, the four quarters are added, and each lane then
-      // fetches its own (token, head) entries.  Heads without one keep their fp32 scores.
+      // exact fp64 scores on the matrix cores (v_mfma_f64_4x4x4_4b: four independent 4x4x4
+      // blocks per wave).  Block b = t >> 2 takes tokens b + 4r (r = 0..3) against 4 query
+      // heads, k = the quarter qd: lane (t, qd) feeds A[r = t & 3][k = qd] = its own K value
+      // (token krow(t) = b + 4 (t & 3)) and B[k = qd][j = t & 3] = query head j (+ 4 for the second
+      // group of G = 8) at the same dim, and receives D[r = qd][j = t & 3]: the score of token
+      // (t >> 2) + 4 qd, head t & 3.  Each step covers one dim of every quarter; the products
+      // of two bf16 values are exact in fp64, so only the fp64 sums round.
       const uint64_t bm = __ballot(big);  // bit 16 qd + t: head t / kParts
       const uint32_t cols = (uint32_t)(bm | (bm >> 16) | (bm >> 32) | (bm >> 48)) & 0xFFFFu;
-      // K in fp64 four dims at a time, shared by every head that needs it; per head and group
-      // of four dims the four q reads go out together; two FMA chains per head (G = 4)
-      constexpr int kChains = G == 4 ? 2 : 1;
-      uint32_t hm = 0;  // heads with a significant score (wave-uniform)
+      constexpr int kGroups = G / 4;  // groups of 4 query heads (one MFMA chain set each)
+      bool need[kGroups];  // wave-uniform: the group holds a significant score
 #pragma unroll
-      for (int i = 0; i < G; ++i) hm |= ((cols >> (kParts * i)) & kColMask) ? 1u << i : 0u;
-      double acc2[G][kChains];
+      for (int g = 0; g < kGroups; ++g) need[g] = (cols >> (16 / kGroups) * g) & (0xFFFFu >> (16 - 16 / kGroups));
+      double dsum[kGroups];
 #pragma unroll
-      for (int i = 0; i < G; ++i)
+      for (int g = 0; g < kGroups; ++g) {
+        dsum[g] = 0.0;
+        if (!need[g]) continue;
+        double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;  // four chains: dims lo / hi of even / odd pairs
+        const double2* qrow = &s_q64[4 * g + (t & 3)][qd][0];
 #pragma unroll
-        for (int c = 0; c < kChains; ++c) acc2[i][c] = 0.0;
-#pragma unroll
-      for (int k0 = 0; k0 < 16; k0 += 4) {
-        double kl[4], kh[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          kl[u] = (double)__uint_as_float(kp[k0 + u] << 16);
-          kh[u] = (double)__uint_as_float(kp[k0 + u] & 0xFFFF0000u);
+        for (int n = 0; n < 16; n += 2) {
+          const double2 qa = qrow[n], qb2 = qrow[n + 1];
+          d0 = __builtin_amdgcn_mfma_f64_4x4x4f64((double)__uint_as_float(kp[n] << 16), qa.x, d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f64_4x4x4f64((double)__uint_as_float(kp[n] & 0xFFFF0000u), qa.y, d1, 0, 0, 0);
+          d2 = __builtin_amdgcn_mfma_f64_4x4x4f64((double)__uint_as_float(kp[n + 1] << 16), qb2.x, d2, 0, 0, 0);
+          d3 = __builtin_amdgcn_mfma_f64_4x4x4f64((double)__uint_as_float(kp[n + 1] & 0xFFFF0000u), qb2.y, d3, 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-          if ((hm >> i) & 1u) {  // wave-uniform
-            double2 qq[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) qq[u] = s_q64[i][qd][k0 + u];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              acc2[i][0] = fma(qq[u].x, kl[u], acc2[i][0]);
-              acc2[i][kChains - 1] = fma(qq[u].y, kh[u], acc2[i][kChains - 1]);
-            }
-          }
-        }
+        dsum[g] = (d0 + d1) + (d2 + d3);
       }
-      double pd[G];
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        pd[i] = 0.0;
-        if ((hm >> i) & 1u) pd[i] = rows_sum_d(kChains == 2 ? acc2[i][0] + acc2[i][kChains - 1] : acc2[i][0]);
-      }
-      // lane (t', qd') offers heads qd' (and qd' + 4) of token krow(t'); lane (t, qd) reads
-      // token qd + 4i = krow(4qd + i), head t / kParts
-      const double offer = qd == 0 ? pd[0] : qd == 1 ? pd[1] : qd == 2 ? pd[2] : pd[3];
-      double offer2 = 0.0;
-      if constexpr (G == 8) offer2 = qd == 0 ? pd[4] : qd == 1 ? pd[5] : qd == 2 ? pd[6] : pd[7];
-      // (the shift is rebuilt from an opaque copy of t on every page: hoisted out of the loop,
-      // it would hold a register for the whole kernel)
-      int tq = t;
-      asm volatile("" : "+v"(tq));
-      const bool mine = (cols >> (tq & ~(kParts - 1))) & kColMask;
+      // lane (t, qd) reads token qd + 4i, head `head`: the D entry of lane (4 qd + (head & 3), i)
+      // of group head >> 2.  Heads of a group without a significant score keep their fp32 ones.
+      const bool mine = need[kGroups == 1 ? 0 : head >> 2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        double x = __shfl(offer, (head & 3) * 16 + 4 * qd + i, 64);
+        const int src = 16 * i + 4 * qd + (head & 3);
+        double x = __shfl(dsum[0], src, 64);
         if constexpr (G == 8) {
-          const double x2 = __shfl(offer2, (head & 3) * 16 + 4 * qd + i, 64);
+          const double x2 = __shfl(dsum[1], src, 64);
           x = head >= 4 ? x2 : x;
         }
-        // tokens past the end stay out; heads without a significant score keep the fp32 one
+        // tokens past the end stay out
         sd[i] = sc[i] == -INFINITY ? -INFINITY : mine ? x : (double)sc[i];
       }
       pm = rows_max_d(max_f64(max_f64(sd[0], sd[1]), max_f64(sd[2], sd[3])));
