@@ -109,17 +109,20 @@ __device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* l
 
 // Encode of one (sequence, logical page): 4 lanes per 64-value block, 16 values each (two
 // 16-byte loads).  The first kEncSweeps sweeps of 256 chunks (a whole page of 512 blocks)
-// keep their raw blocks' spill nibbles in registers until the page's slots are known; a larger
+// keep their raw blocks' spill nibbles in LDS until the page's slots are known; a larger
 // page's later sweeps read their raw blocks again for them.
 constexpr int kEncSweeps = 8;
-constexpr int kEncUnroll = 4;
+constexpr int kEncUnroll = 2;
+// The encode is bound by how many loads are in flight, so by how many workgroups fit a CU: the
+// raw blocks' spill nibbles wait for their slots in LDS rather than in VGPRs, and the register
+// budget is held to 6 waves per SIMD (80 VGPRs, no spills; 8 waves spill and run slower).
+constexpr int kEncWavesPerSimd = 6;
 
-__global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* __restrict__ raw,
-                                             uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
-                                             uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags,
-                                             uint32_t* __restrict__ row_spill, uint8_t* __restrict__ spill,
-                                             const uint64_t* spill_top, uint64_t spill_slots,
-                                             uint64_t* look, uint32_t* failed, uint32_t* status) {
+__global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
+    Geom g, SeqView s, const uint16_t* __restrict__ raw, uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
+    uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags, uint32_t* __restrict__ row_spill,
+    uint8_t* __restrict__ spill, const uint64_t* spill_top, uint64_t spill_slots, uint64_t* look, uint32_t* failed,
+    uint32_t* status) {
   const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int32_t L;
   int rows = rows_in_page(s, g, b, p, &L);
@@ -195,14 +198,14 @@ __global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* 
     }
     return raw_mask;
   };
-  uint2 hik[kEncSweeps];
+  __shared__ uint2 s_hik[kEncSweeps][256];  // LDS, not registers: more workgroups per CU
   uint32_t rawm = 0u;
 #pragma unroll
   for (int gi = 0; gi < kEncSweeps / kEncUnroll; ++gi) {
     uint2 h[kEncUnroll];
     rawm |= classify(tid + 256 * kEncUnroll * gi, h) << (kEncUnroll * gi);
 #pragma unroll
-    for (int u = 0; u < kEncUnroll; ++u) hik[kEncUnroll * gi + u] = h[u];
+    for (int u = 0; u < kEncUnroll; ++u) s_hik[kEncUnroll * gi + u][tid] = h[u];
   }
   for (int k0 = tid + 256 * kEncSweeps; k0 < chunks; k0 += 256 * kEncUnroll) {  // larger pages
     uint2 h[kEncUnroll];
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(256) void enc_k(Geom g, SeqView s, const uint16_t* 
     const int k = tid + 256 * i;
     const uint64_t idx = slot_of(k >> 2);
     if (idx < spill_slots)  // a pool too small for the call: slots past its end are skipped
-      *reinterpret_cast<uint2*>(spill + idx * 32u + (k & 3) * 8) = hik[i];
+      *reinterpret_cast<uint2*>(spill + idx * 32u + (k & 3) * 8) = s_hik[i][tid];
   }
   for (int k = tid + 256 * kEncSweeps; k < chunks; k += 256) {  // larger pages
     const int m = k >> 2, half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
