@@ -533,7 +533,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   static_assert(G == 4 || G == 8, "4 or 8 query heads per kv head");
   constexpr int kParts = 16 / G;           // score columns (and p.V rows) per head
   constexpr int kHeadsPerLane = G / 4;     // p.V output heads per lane
-  constexpr uint32_t kColMask = (1u << kParts) - 1u;
   // The job: a (sequence b, split s, kv head h).  Workgroup ids go round-robin over the 8
   // XCDs; in the plain order each XCD takes a contiguous run of jobs (split fastest, then kv
   // head, then sequence), so the kv heads of a sequence share one L2 for the page metadata and

@@ -70,10 +70,14 @@ __device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* l
                               uint32_t* failed) {
   const int lane = threadIdx.x & 63;
   uint64_t sum = 0;
+  uint32_t ran_out = 0u;
   int pb = b, hi = p - 1;  // next page to look at: (pb, hi)
   while (true) {
     while (hi < 0) {  // on to the previous sequence's last page
-      if (--pb < 0) return sum;
+      if (--pb < 0) {
+        if (__any(ran_out)) *failed = 1u;  // in every lane
+        return sum;
+      }
       hi = pages_of(s, g, pb) - 1;
     }
     const int q = hi - lane;
@@ -85,7 +89,7 @@ __device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* l
         w = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((w >> 62) != 0u) break;
         if (++n == kLbPolls) {
-          *failed = 1u;
+          ran_out = 1u;
           w = kLbAggregate;
           break;
         }
@@ -102,8 +106,11 @@ __device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* l
       hi -= 64;
       continue;
     }
-    if (hi - k >= 0) return sum;  // lane k holds an inclusive count: everything before is in it
-    hi = -1;                      // the window passed the sequence's first page
+    if (hi - k >= 0) {  // lane k holds an inclusive count: everything before is in it
+      if (__any(ran_out)) *failed = 1u;
+      return sum;
+    }
+    hi = -1;  // the window passed the sequence's first page
   }
 }
 
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan_k(Geom g, SeqView s,
 // up waiting marks its word abandoned instead, and the commit then changes nothing
 // (ZF_DEV_ESYNC).  Each word carries its data itself, so no fence orders it after other stores.
 constexpr int kAppendThreads = 1024;
-constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS (beyond: the chunked form)
+constexpr int kAppendMaxRows = 4096;  // two u32 per row in LDS (beyond: the grouped form)
 constexpr int kAppendChunkedMaxRows = 1 << 24;  // new rows of one call
 constexpr int kOneMaxRows = 64;       // new rows of a one-launch append (sync words 0 .. 63; 64: epoch)
 constexpr uint32_t kSyncPolls = 1u << 20;  // bound on each wait for the words (about 1 s)
@@ -468,13 +475,16 @@ struct NewBlock {
 };
 
 // New row r is u16 [H][D] of K and of V; block j covers half j % nb of head j / nb / 2, K or V
-// by (j / nb) & 1, the order of the row's flag bits.
-__device__ __forceinline__ NewBlock classify_new(const Geom& g, int r, int j, int lane8,
-                                                 const uint16_t* __restrict__ k_new,
-                                                 const uint16_t* __restrict__ v_new) {
+// by (j / nb) & 1, the order of the row's flag bits.  load_new: this lane's 8 values of it.
+__device__ __forceinline__ uint4 load_new(const Geom& g, int r, int j, int lane8, const uint16_t* __restrict__ k_new,
+                                          const uint16_t* __restrict__ v_new) {
   const int nb = g.nb(), half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
-  const uint4 in = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)r * g.H + h) * g.D +
-                                                   half * kBlock + lane8 * 8);
+  return *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)r * g.H + h) * g.D + half * kBlock +
+                                         lane8 * 8);
+}
+
+// The block's window over its 8 lanes, then this lane's planes.
+__device__ __forceinline__ NewBlock classify_loaded(const uint4 in) {
   const uint32_t w[4] = {in.x, in.y, in.z, in.w};
   Window win = window8(w);
 #pragma unroll
@@ -491,6 +501,12 @@ __device__ __forceinline__ NewBlock classify_new(const Geom& g, int r, int j, in
   o.sm0 = smw[0];
   o.sm1 = smw[1];
   return o;
+}
+
+__device__ __forceinline__ NewBlock classify_new(const Geom& g, int r, int j, int lane8,
+                                                 const uint16_t* __restrict__ k_new,
+                                                 const uint16_t* __restrict__ v_new) {
+  return classify_loaded(load_new(g, r, j, lane8, k_new, v_new));
 }
 
 __device__ __forceinline__ void store_new(const Geom& g, int64_t row, int j, int lane8, const NewBlock& o,
@@ -514,24 +530,57 @@ __device__ __forceinline__ uint32_t row_flag_word(bool has, int j, int lane8, ui
   return s_f;
 }
 
-// count_out: the chunked form also leaves the row's raw count in its row_spill entry (the new
-// row's, which holds nothing yet) for the chunk scan.
+// Grouped form of the append (below): rows per group, and the flags of a group's look-back word.
+constexpr int kGroupRows = 16;
+constexpr uint32_t kGlAggregate = 1u << 30;
+constexpr uint32_t kGlInclusive = 2u << 30;
+constexpr uint32_t kGlValue = (1u << 30) - 1u;  // raw blocks of a call: <= 2^24 rows x 32 < 2^30
+
+// kPackRows new rows per workgroup (block j of each on threads 8j .. 8j + 7), their loads issued
+// together.  words: the grouped form's look-back words (the row_spill entries of each group's
+// first row, which hold nothing yet), cleared here.
+constexpr int kPackRows = 4;
+
 __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, uint8_t* sm,
                                                      uint8_t* nib, uint8_t* base, uint32_t* row_flags,
-                                                     uint32_t* count_out) {
-  const int r = blockIdx.x, b = r / n, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
-  uint32_t err;
-  const int64_t row = append_row(g, s, b, r - b * n, n, &err);
-  if (row < 0) return;  // reported by append_commit_k
+                                                     uint32_t* words) {
+  const int R = s.B * n, r0 = blockIdx.x * kPackRows, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
   const bool has = j < g.blocks_per_row();
-  NewBlock o{};
-  if (has) o = classify_new(g, r, j, lane8, k_new, v_new);
-  const uint32_t f = row_flag_word(has, j, lane8, o.raw);
-  if (has) store_new(g, row, j, lane8, o, sm, nib, base);
-  if (tid == 0) {
-    row_flags[row] = f;
-    if (count_out) count_out[row] = __popc(f);
+  __shared__ uint32_t s_f[kPackRows];
+  if (tid < kPackRows) s_f[tid] = 0u;
+  int64_t row[kPackRows];
+  uint4 in[kPackRows];
+#pragma unroll
+  for (int i = 0; i < kPackRows; ++i) {
+    const int r = r0 + i;
+    row[i] = -1;  // past the last row, or a position the call cannot take (append_commit_k or
+                  // append_group_finish_k reports it)
+    if (r < R) {
+      uint32_t err;
+      row[i] = append_row(g, s, r / n, r % n, n, &err);
+      // the new values do not depend on where they go: their loads fly with the lookups
+      if (has) in[i] = load_new(g, r, j, lane8, k_new, v_new);
+    }
+  }
+  __syncthreads();  // s_f cleared
+  NewBlock o[kPackRows];
+#pragma unroll
+  for (int i = 0; i < kPackRows; ++i) {
+    if (has && row[i] >= 0) {
+      o[i] = classify_loaded(in[i]);
+      if (lane8 == 0 && o[i].raw) atomicOr(&s_f[i], 1u << j);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPackRows; ++i) {
+    if (has && row[i] >= 0) store_new(g, row[i], j, lane8, o[i], sm, nib, base);
+    if (tid == i && row[i] >= 0) {
+      const uint32_t f = s_f[i];
+      row_flags[row[i]] = f;
+      if (words && (r0 + i) % kGroupRows == 0) words[row[i]] = 0u;
+    }
   }
 }
 
@@ -612,95 +661,110 @@ __global__ __launch_bounds__(kAppendThreads) void append_commit_k(Geom g, SeqVie
   if (tid == 0) *spill_top = top + total;
 }
 
-// ------------------------------------------------------------------ append: chunked form
+// ------------------------------------------------------------------ append: grouped form
 // For more new rows than one commit workgroup holds (prefill written in chunks, long
-// speculative runs), four launches and no workspace: the pack kernel above leaves each row's raw
-// count in its (not yet defined) row_spill entry; append_chunk_scan_k turns the counts of each
-// chunk of kChunkRows rows into row-local exclusive prefixes there, the chunk's total in its
-// first row's entry; append_chunk_commit_k adds the totals of the chunks before its own and
-// writes the chunk's final row_spill entries (all but the first row's, which the other chunks
-// still read) and spill slots; append_chunk_finish_k checks the whole call (lengths, page ids,
-// room in the pool) and only then writes the first rows' entries and advances seq_lens and
-// spill_top.  Until that last step only slots that hold nothing yet are written (rows at
-// positions seq_lens[b] and later, spill slots from spill_top on within the pool), so a failed
-// call changes no defined state.  Rows with an invalid position are skipped by every step (the
-// call then fails in the last).
-constexpr int kChunkItems = 4;
-constexpr int kChunkRows = kScanThreads * kChunkItems;
+// speculative runs), three launches and no workspace.  The rows are taken in groups of
+// kGroupRows in row order; each group's first row's row_spill entry (which holds nothing yet)
+// serves as the group's look-back word: append_pack_k clears it, append_group_commit_k
+// publishes the group's raw count there, takes the count of every earlier group by decoupled
+// look-back, publishes the inclusive count, and writes the group's other row_spill entries and
+// its spill slots; append_group_finish_k checks the whole call (lengths, page ids, every group's
+// word complete, room in the pool) and only then writes the first rows' entries and advances
+// seq_lens and spill_top.  Until that last step only slots that hold nothing yet are written
+// (rows at positions seq_lens[b] and later, spill slots from spill_top on within the pool), so
+// a failed call changes no defined state.  A group whose first row has an invalid position has
+// no word: the groups after it count it as an inclusive 0 (their prefixes are then wrong, and
+// the call fails in the last step).
 
-__global__ __launch_bounds__(kScanThreads) void append_chunk_scan_k(Geom g, SeqView s, int n,
-                                                                    uint32_t* row_spill) {
-  __shared__ uint32_t s_tmp[kScanThreads];
-  const int R = s.B * n, r0 = blockIdx.x * kChunkRows, tid = threadIdx.x;
-  int64_t row[kChunkItems];
-  uint32_t cnt[kChunkItems], mine = 0;
-#pragma unroll
-  for (int i = 0; i < kChunkItems; ++i) {
-    const int r = r0 + tid * kChunkItems + i;
-    uint32_t e;
-    row[i] = r < R ? append_row(g, s, r / n, r % n, n, &e) : -1;
-    cnt[i] = row[i] >= 0 ? row_spill[row[i]] : 0u;
-    mine += cnt[i];
-  }
-  uint32_t total;
-  uint32_t ex = block_exclusive_scan(mine, s_tmp, &total);
-#pragma unroll
-  for (int i = 0; i < kChunkItems; ++i) {
-    if (row[i] >= 0) row_spill[row[i]] = (tid == 0 && i == 0) ? total : ex;
-    ex += cnt[i];
-  }
-}
-
-// Raw blocks of the chunks before chunk c (every thread gets the sum).
-__device__ uint64_t chunks_before(const Geom& g, const SeqView& s, int n, int c,
-                                  const uint32_t* row_spill) {
-  uint64_t part = 0;
-  for (int k = threadIdx.x; k < c; k += blockDim.x) {
-    uint32_t e;
-    const int r = k * kChunkRows;
-    const int64_t row = append_row(g, s, r / n, r % n, n, &e);
-    if (row >= 0) part += row_spill[row];
-  }
-  __shared__ unsigned long long s_sum;
-  if (threadIdx.x == 0) s_sum = 0ull;
-  __syncthreads();
-  atomicAdd(&s_sum, (unsigned long long)part);
-  __syncthreads();
-  const uint64_t r = s_sum;
-  __syncthreads();
-  return r;
-}
-
-// kCommitRows rows of one chunk per workgroup: their final row_spill entries (but a chunk's
-// first row's) and their raw blocks' spill slots.
-constexpr int kCommitRows = 16;
-static_assert(kChunkRows % kCommitRows == 0, "a commit workgroup stays inside one chunk");
-
-__global__ __launch_bounds__(256) void append_chunk_commit_k(
-    Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const uint32_t* __restrict__ row_flags, uint32_t* row_spill, uint8_t* spill,
-    const uint64_t* spill_top, uint64_t spill_slots) {
-  __shared__ uint32_t s_flags[kCommitRows], s_first[kCommitRows];
-  const int R = s.B * n, r0 = blockIdx.x * kCommitRows, tid = threadIdx.x;
-  const int c = r0 / kChunkRows, rows = min(kCommitRows, R - r0);
-  const uint64_t before = *spill_top + chunks_before(g, s, n, c, row_spill);
-  if (tid < rows) {
-    const int r = r0 + tid;
-    uint32_t e;
-    const int64_t row = append_row(g, s, r / n, r % n, n, &e);
-    uint32_t f = 0u, local = 0u;
-    const bool first = r % kChunkRows == 0;  // its entry holds the chunk's total
-    if (row >= 0) {
-      f = row_flags[row];
-      local = first ? 0u : row_spill[row];
+// Raw blocks of every group before group G (called by one wave; the result in every lane).
+// Lane l looks at group G - 1 - l; the walk stops at the nearest group with an inclusive count.
+// Every group waited for comes earlier in the grid, so it has been dispatched and publishes
+// without waiting for this one.  *failed is set if a wait ran out (the sum is then incomplete).
+__device__ uint32_t group_look_back(const Geom& g, const SeqView& s, int n, const uint32_t* row_spill, int G,
+                                    uint32_t* failed) {
+  const int lane = threadIdx.x & 63;
+  uint32_t sum = 0, ran_out = 0u;
+  for (int hi = G - 1; hi >= 0; hi -= 64) {
+    const int q = hi - lane;
+    uint32_t w = kGlInclusive;  // before group 0, or a group without a word: a stop with 0
+    if (q >= 0) {
+      uint32_t e;
+      const int r = q * kGroupRows;
+      const int64_t row = append_row(g, s, r / n, r % n, n, &e);
+      if (row >= 0) {
+        for (uint32_t k = 0;; ++k) {
+          w = __hip_atomic_load(&row_spill[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((w >> 30) != 0u) break;
+          if (k + 1 == kLbPolls) {
+            ran_out = 1u;
+            w = kGlAggregate;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
     }
-    s_flags[tid] = f;
-    s_first[tid] = local;
-    if (row >= 0 && !first) row_spill[row] = (uint32_t)(before + local);
+    const uint64_t stop = __ballot((w >> 30) == 2u);
+    const int k = stop ? __builtin_ctzll(stop) : 63;
+    uint32_t v = lane <= k ? (w & kGlValue) : 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
+    sum += v;
+    if (stop) break;
+  }
+  if (__any(ran_out)) *failed = 1u;  // in every lane
+  return sum;
+}
+
+// One group per workgroup: its look-back, its rows' row_spill entries (but the first row's)
+// and its raw blocks' spill slots.
+__global__ __launch_bounds__(256) void append_group_commit_k(
+    Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint32_t* __restrict__ row_flags, uint32_t* row_spill, uint8_t* spill, const uint64_t* spill_top,
+    uint64_t spill_slots, uint32_t* status) {
+  __shared__ uint32_t s_flags[kGroupRows], s_first[kGroupRows];
+  __shared__ uint64_t s_base;
+  const int R = s.B * n, G = blockIdx.x, r0 = G * kGroupRows, tid = threadIdx.x;
+  const int rows = min(kGroupRows, R - r0);
+  uint32_t e0;
+  const int64_t row0 = append_row(g, s, r0 / n, r0 % n, n, &e0);
+  if (row0 < 0) return;  // no word: the call fails in the last step
+  if (tid < 64) {
+    const int r = r0 + tid;
+    int64_t row = -1;
+    uint32_t f = 0u;
+    if (tid < rows) {
+      uint32_t e;
+      row = append_row(g, s, r / n, r % n, n, &e);
+      if (row >= 0) f = row_flags[row];
+    }
+    const uint32_t c = __popc(f);
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < kGroupRows; o <<= 1) {
+      const uint32_t up = (uint32_t)__shfl_up((int)incl, o, 64);
+      if (tid >= o) incl += up;
+    }
+    const uint32_t total = (uint32_t)__shfl((int)incl, kGroupRows - 1, 64);
+    if (tid == 0) __hip_atomic_store(&row_spill[row0], kGlAggregate | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t failed = 0u;
+    const uint32_t before = group_look_back(g, s, n, row_spill, G, &failed);
+    if (tid == 0) {
+      // a wait that ran out leaves the word at its aggregate: the last step then fails the call
+      if (!failed) __hip_atomic_store(&row_spill[row0], kGlInclusive | (before + total), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_base = *spill_top + before;
+    }
+    const uint32_t ex = incl - c;
+    if (tid < kGroupRows) {
+      s_flags[tid] = f;
+      s_first[tid] = ex;
+    }
+    if (tid > 0 && row >= 0) row_spill[row] = (uint32_t)(*spill_top + before + ex);
   }
   __syncthreads();
   // spill slots of the raw blocks: 8 lanes per block, two blocks per step so that their loads
   // fly together
+  const uint64_t base = s_base;
   const int nb = g.nb(), D = g.D, H = g.H;
   const uint32_t rb = 2u * H * nb, nblk = (uint32_t)rows * rb;
   const int lane8 = tid & 7;
@@ -715,7 +779,7 @@ __global__ __launch_bounds__(256) void append_chunk_commit_k(
       if (m >= nblk) continue;
       const uint32_t i = m / rb, j = m - i * rb;
       const uint32_t f = s_flags[i];
-      idx[u] = before + s_first[i] + __popc(f & ((1u << j) - 1u));
+      idx[u] = base + s_first[i] + __popc(f & ((1u << j) - 1u));
       // (a slot past the pool: the call fails in the last step)
       take[u] = ((f >> j) & 1u) && idx[u] < spill_slots;
       if (take[u]) {
@@ -734,20 +798,20 @@ __global__ __launch_bounds__(256) void append_chunk_commit_k(
       *reinterpret_cast<uint32_t*>(spill + idx[u] * 32u + lane8 * 4) = hi;
     }
   }
+  (void)status;
 }
 
-// The last step of the chunked form (one workgroup): every sequence's length and the page ids
-// of its new rows, then room in the pool; on success the first rows' row_spill entries,
-// seq_lens and spill_top.
-__global__ __launch_bounds__(kScanThreads) void append_chunk_finish_k(Geom g, SeqView s, int n,
+// The last step of the grouped form (one workgroup): every sequence's length and the page ids
+// of its new rows, every group's word complete, then room in the pool; on success the first
+// rows' row_spill entries, seq_lens and spill_top.
+__global__ __launch_bounds__(kScanThreads) void append_group_finish_k(Geom g, SeqView s, int n,
                                                                       uint32_t* row_spill, uint64_t* spill_top,
                                                                       uint64_t spill_slots, uint32_t* status) {
-  __shared__ uint32_t s_err;
-  __shared__ unsigned long long s_total;
-  const int tid = threadIdx.x, R = s.B * n, nchunks = (R + kChunkRows - 1) / kChunkRows;
+  __shared__ uint32_t s_err, s_total;
+  const int tid = threadIdx.x, R = s.B * n, ngroups = (R + kGroupRows - 1) / kGroupRows;
   if (tid == 0) {
     s_err = 0u;
-    s_total = 0ull;
+    s_total = 0u;
   }
   __syncthreads();
   // 32 threads per sequence check the page ids of its new rows
@@ -764,15 +828,18 @@ __global__ __launch_bounds__(kScanThreads) void append_chunk_finish_k(Geom g, Se
       if (pid < 0 || pid >= g.P) err |= ZF_DEV_EPAGE;
     }
   }
-  if (err) atomicOr(&s_err, err);
-  uint64_t part = 0;
-  for (int k = tid; k < nchunks; k += kScanThreads) {
+  // every group's word inclusive (a look-back that ran out left one at its aggregate); the last
+  // group's value is the call's total
+  for (int G = tid; G < ngroups; G += kScanThreads) {
     uint32_t e;
-    const int r = k * kChunkRows;
+    const int r = G * kGroupRows;
     const int64_t row = append_row(g, s, r / n, r % n, n, &e);
-    if (row >= 0) part += row_spill[row];
+    if (row < 0) continue;  // reported above
+    const uint32_t w = row_spill[row];
+    if ((w >> 30) != 2u) err |= ZF_DEV_ESYNC;
+    if (G == ngroups - 1) s_total = w & kGlValue;
   }
-  atomicAdd(&s_total, (unsigned long long)part);
+  if (err) atomicOr(&s_err, err);
   __syncthreads();
   const uint64_t top = *spill_top, total = s_total;
   if (s_err) {
@@ -783,23 +850,26 @@ __global__ __launch_bounds__(kScanThreads) void append_chunk_finish_k(Geom g, Se
     if (tid == 0) set_status(status, ZF_DEV_ESPILL);
     return;
   }
-  // first rows: the exclusive prefixes of the chunk totals, kScanThreads chunks at a time
-  __shared__ uint32_t s_scan[kScanThreads];
-  uint64_t carry = 0;  // the same in every thread
-  for (int c0 = 0; c0 < nchunks; c0 += kScanThreads) {
-    const int c = c0 + tid;
+  // first rows: a group's exclusive prefix is the inclusive count of the group before it; each
+  // pass reads its groups' words before any of them is rewritten, and carries the last one on
+  __shared__ uint32_t s_incl[kScanThreads], s_prev;
+  if (tid == 0) s_prev = 0u;
+  for (int G0 = 0; G0 < ngroups; G0 += kScanThreads) {
+    const int G = G0 + tid;
     int64_t row = -1;
-    uint32_t tot = 0u;
-    if (c < nchunks) {
+    uint32_t incl = 0u;
+    if (G < ngroups) {
       uint32_t e;
-      const int r = c * kChunkRows;
+      const int r = G * kGroupRows;
       row = append_row(g, s, r / n, r % n, n, &e);
-      tot = row_spill[row];
+      incl = row_spill[row] & kGlValue;
     }
-    uint32_t sum;
-    const uint32_t ex = block_exclusive_scan(tot, s_scan, &sum);
-    if (row >= 0) row_spill[row] = (uint32_t)(top + carry + ex);
-    carry += sum;
+    s_incl[tid] = incl;
+    __syncthreads();
+    const uint32_t ex = tid == 0 ? s_prev : s_incl[tid - 1];
+    __syncthreads();  // every thread has its prefix before s_prev moves on
+    if (row >= 0) row_spill[row] = (uint32_t)(top + ex);
+    if (tid == kScanThreads - 1) s_prev = incl;
   }
   __syncthreads();  // every length was read above
   for (int b = tid; b < s.B; b += kScanThreads) s.lens[b] += n;
@@ -1178,19 +1248,17 @@ hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int
     return hipGetLastError();
   }
   if (rows > kAppendMaxRows) {
-    const int nchunks = (rows + kChunkRows - 1) / kChunkRows;
-    hipLaunchKernelGGL(append_pack_k, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
-                       c->base, c->row_flags, c->row_spill);
-    hipLaunchKernelGGL(append_chunk_scan_k, dim3(nchunks), dim3(kScanThreads), 0, st, g, s, n, c->row_spill);
-    hipLaunchKernelGGL(append_chunk_commit_k, dim3((rows + kCommitRows - 1) / kCommitRows), dim3(256), 0, st,
-                       g, s, n, k_new,
-                       v_new, c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots);
-    hipLaunchKernelGGL(append_chunk_finish_k, dim3(1), dim3(kScanThreads), 0, st, g, s, n, c->row_spill,
+    const int ngroups = (rows + kGroupRows - 1) / kGroupRows;
+    hipLaunchKernelGGL(append_pack_k, dim3((rows + kPackRows - 1) / kPackRows), dim3(256), 0, st, g, s, n, k_new,
+                       v_new, c->sm, c->nib, c->base, c->row_flags, c->row_spill);
+    hipLaunchKernelGGL(append_group_commit_k, dim3(ngroups), dim3(256), 0, st, g, s, n, k_new, v_new, c->row_flags,
+                       c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
+    hipLaunchKernelGGL(append_group_finish_k, dim3(1), dim3(kScanThreads), 0, st, g, s, n, c->row_spill,
                        c->spill_top, c->spill_slots, c->status);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(append_pack_k, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
-                     c->base, c->row_flags, nullptr);
+  hipLaunchKernelGGL(append_pack_k, dim3((rows + kPackRows - 1) / kPackRows), dim3(256), 0, st, g, s, n, k_new,
+                     v_new, c->sm, c->nib, c->base, c->row_flags, nullptr);
   size_t lds = 2 * (size_t)rows * sizeof(uint32_t);
   hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, n, k_new, v_new,
                      c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);

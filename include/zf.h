@@ -151,8 +151,9 @@ zf_status zf_append_kv(const zf_cache* cache, const zf_seqs* seqs, const uint16_
  * n_new == 0 does nothing; n_new < 0 is ZF_EINVAL.  Supports batch * n_new <= 2^24 new rows.
  * zf_append_kv is the case n_new == 1.
  * Launches: one when cache->append_sync is set and batch * n_new <= 64; two up to 4096 new
- * rows (pack, then one commit workgroup); four beyond (pack; per chunk of 4096 rows a scan,
- * then the chunk's slots; a last step that checks the whole call and commits).  In the
+ * rows (pack, then one commit workgroup); three beyond (pack; per group of 16 rows a look-back
+ * over the earlier groups and the group's slots; a last step that checks the whole call and
+ * commits).  In the
  * one-launch form the new rows' workgroups hand their flag words to each other through
  * append_sync, words tagged with an epoch that append_sync[64] counts (every call advances it,
  * also one that fails); each workgroup waits only for lower-numbered ones, so no co-residency
