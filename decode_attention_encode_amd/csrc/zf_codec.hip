@@ -446,27 +446,42 @@ constexpr int kSyncGiveUp = kOneMaxRows + 1; // sync word: nonzero makes waiting
                                              // workgroups give up at once (forces ZF_DEV_ESYNC)
 constexpr uint64_t kTagMod = (1u << 27) - 1u;
 
-// Row of new token j of sequence b (n per sequence) whose length was read as L, or -1 (with the
-// error bit) when the sequence cannot take them.
-__device__ __forceinline__ int64_t append_row_at(const Geom& g, const SeqView& s, int b, int j, int n,
-                                                 int32_t L, uint32_t* err) {
+// Where new token j of sequence b (n per sequence) goes when its length was read as L: its
+// page and slot, and row = pid * T + slot; row -1 (with the error bit) when the sequence cannot
+// take them.
+struct NewPos {
+  int64_t row;
+  int32_t pid, slot;
+};
+
+__device__ __forceinline__ NewPos append_pos_at(const Geom& g, const SeqView& s, int b, int j, int n, int32_t L,
+                                                uint32_t* err) {
   if (L < 0 || (int64_t)L + n > (int64_t)s.maxp * g.T || (int64_t)L + n > s.max_seq_len) {
     *err = ZF_DEV_ELEN;
-    return -1;
+    return NewPos{-1, 0, 0};
   }
-  const int32_t t = L + j;
-  const int32_t pid = s.pt[(int64_t)b * s.maxp + t / g.T];
+  const int32_t t = L + j, p = t / g.T, slot = t - p * g.T;
+  const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
   if (pid < 0 || pid >= g.P) {
     *err = ZF_DEV_EPAGE;
-    return -1;
+    return NewPos{-1, 0, 0};
   }
   *err = 0;
-  return (int64_t)pid * g.T + t % g.T;
+  return NewPos{(int64_t)pid * g.T + slot, pid, slot};
+}
+
+__device__ __forceinline__ int64_t append_row_at(const Geom& g, const SeqView& s, int b, int j, int n,
+                                                 int32_t L, uint32_t* err) {
+  return append_pos_at(g, s, b, j, n, L, err).row;
+}
+
+__device__ __forceinline__ NewPos append_pos(const Geom& g, const SeqView& s, int b, int j, int n, uint32_t* err) {
+  return append_pos_at(g, s, b, j, n, s.lens[b], err);
 }
 
 __device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, int b, int j, int n,
                                               uint32_t* err) {
-  return append_row_at(g, s, b, j, n, s.lens[b], err);
+  return append_pos(g, s, b, j, n, err).row;
 }
 
 // Block j of a new row, classified and packed in registers (8 lanes, 8 values each).
@@ -509,11 +524,11 @@ __device__ __forceinline__ NewBlock classify_new(const Geom& g, int r, int j, in
   return classify_loaded(load_new(g, r, j, lane8, k_new, v_new));
 }
 
-__device__ __forceinline__ void store_new(const Geom& g, int64_t row, int j, int lane8, const NewBlock& o,
+__device__ __forceinline__ void store_new(const Geom& g, const NewPos& at, int j, int lane8, const NewBlock& o,
                                           uint8_t* sm, uint8_t* nib, uint8_t* base) {
   const int nb = g.nb(), half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
-  const int64_t pid = row / g.T, slot = row % g.T;
-  const int64_t v0 = ((pid * g.H + h) * 2 + kv) * g.T * g.D + slot * g.D + half * kBlock + lane8 * 8;
+  const int64_t v0 = (((int64_t)at.pid * g.H + h) * 2 + kv) * g.T * g.D + (int64_t)at.slot * g.D + half * kBlock +
+                     lane8 * 8;
   *reinterpret_cast<uint2*>(sm + v0) = make_uint2(o.sm0, o.sm1);
   *reinterpret_cast<uint32_t*>(nib + (v0 >> 1)) = o.nib;
   if (lane8 == 0) base[v0 / kBlock] = (uint8_t)o.bexp;
@@ -549,19 +564,27 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, c
   const bool has = j < g.blocks_per_row();
   __shared__ uint32_t s_f[kPackRows];
   if (tid < kPackRows) s_f[tid] = 0u;
-  int64_t row[kPackRows];
+  // the new values do not depend on where they go: all their loads go out before the lookups
+  // of the rows' pages (dependent scalar round trips)
   uint4 in[kPackRows];
+#pragma unroll
+  for (int i = 0; i < kPackRows; ++i)
+    if (has && r0 + i < R) in[i] = load_new(g, r0 + i, j, lane8, k_new, v_new);
+  int32_t L[kPackRows];  // the lengths first, then the page-table entries they lead to
+#pragma unroll
+  for (int i = 0; i < kPackRows; ++i) L[i] = r0 + i < R ? s.lens[(r0 + i) / n] : 0;
+  NewPos at[kPackRows];
+  int64_t row[kPackRows];
 #pragma unroll
   for (int i = 0; i < kPackRows; ++i) {
     const int r = r0 + i;
-    row[i] = -1;  // past the last row, or a position the call cannot take (append_commit_k or
-                  // append_group_finish_k reports it)
+    at[i] = NewPos{-1, 0, 0};  // past the last row, or a position the call cannot take
+                               // (append_commit_k or append_group_finish_k reports it)
     if (r < R) {
       uint32_t err;
-      row[i] = append_row(g, s, r / n, r % n, n, &err);
-      // the new values do not depend on where they go: their loads fly with the lookups
-      if (has) in[i] = load_new(g, r, j, lane8, k_new, v_new);
+      at[i] = append_pos_at(g, s, r / n, r % n, n, L[i], &err);
     }
+    row[i] = at[i].row;
   }
   __syncthreads();  // s_f cleared
   NewBlock o[kPackRows];
@@ -575,7 +598,7 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, c
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kPackRows; ++i) {
-    if (has && row[i] >= 0) store_new(g, row[i], j, lane8, o[i], sm, nib, base);
+    if (has && row[i] >= 0) store_new(g, at[i], j, lane8, o[i], sm, nib, base);
     if (tid == i && row[i] >= 0) {
       const uint32_t f = s_f[i];
       row_flags[row[i]] = f;
@@ -967,7 +990,8 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
   const uint64_t top = *spill_top;
   const int b = r / n;
   uint32_t err;
-  const int64_t row = append_row(g, s, b, r - b * n, n, &err);
+  const NewPos at = append_pos(g, s, b, r - b * n, n, &err);
+  const int64_t row = at.row;
   const bool has = j < g.blocks_per_row();
   NewBlock o{};
   if (has) o = classify_new(g, r, j, lane8, k_new, v_new);
@@ -980,7 +1004,7 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
     __hip_atomic_store(&sync[r], hand_over_word(t, err, f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (row >= 0) {
-    if (has) store_new(g, row, j, lane8, o, sm, nib, base);
+    if (has) store_new(g, at, j, lane8, o, sm, nib, base);
     if (tid == 0) row_flags[row] = f;
   }
   // the rows before this one: their raw blocks are this row's prefix
