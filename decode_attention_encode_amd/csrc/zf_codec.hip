@@ -552,10 +552,10 @@ constexpr uint32_t kGlInclusive = 2u << 30;
 constexpr uint32_t kGlValue = (1u << 30) - 1u;  // raw blocks of a call: <= 2^24 rows x 32 < 2^30
 
 // kPackRows new rows per workgroup (block j of each on threads 8j .. 8j + 7), their loads issued
-// together.  words: the grouped form's look-back words (the row_spill entries of each group's
-// first row, which hold nothing yet), cleared here.
-constexpr int kPackRows = 4;
-
+// together: 4 for the grouped form's many rows, 1 for the two-launch form's few, where the
+// workgroups' number sets the latency.  words: the grouped form's look-back words (the
+// row_spill entries of each group's first row, which hold nothing yet), cleared here.
+template <int kPackRows>
 __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, uint8_t* sm,
                                                      uint8_t* nib, uint8_t* base, uint32_t* row_flags,
@@ -1273,16 +1273,16 @@ hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int
   }
   if (rows > kAppendMaxRows) {
     const int ngroups = (rows + kGroupRows - 1) / kGroupRows;
-    hipLaunchKernelGGL(append_pack_k, dim3((rows + kPackRows - 1) / kPackRows), dim3(256), 0, st, g, s, n, k_new,
-                       v_new, c->sm, c->nib, c->base, c->row_flags, c->row_spill);
+    hipLaunchKernelGGL(append_pack_k<4>, dim3((rows + 3) / 4), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
+                       c->base, c->row_flags, c->row_spill);
     hipLaunchKernelGGL(append_group_commit_k, dim3(ngroups), dim3(256), 0, st, g, s, n, k_new, v_new, c->row_flags,
                        c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
     hipLaunchKernelGGL(append_group_finish_k, dim3(1), dim3(kScanThreads), 0, st, g, s, n, c->row_spill,
                        c->spill_top, c->spill_slots, c->status);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(append_pack_k, dim3((rows + kPackRows - 1) / kPackRows), dim3(256), 0, st, g, s, n, k_new,
-                     v_new, c->sm, c->nib, c->base, c->row_flags, nullptr);
+  hipLaunchKernelGGL(append_pack_k<1>, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib, c->base,
+                     c->row_flags, nullptr);
   size_t lds = 2 * (size_t)rows * sizeof(uint32_t);
   hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, n, k_new, v_new,
                      c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
