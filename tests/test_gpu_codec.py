@@ -358,20 +358,26 @@ def test_append_n_spill_exhaustion_changes_no_defined_state():
         assert np.array_equal(a[m], b[m]), n
 
 
-# More new rows than one commit workgroup holds (the chunked form): a batch of 32 ragged
+# More new rows than one commit workgroup holds (the grouped form): a batch of 32 ragged
 # sequences takes 2048 tokens each in one call (65 536 rows), then 600 more (19 200 rows).
 LONG_APPEND = synth.WORKLOADS[1].replace(name="chunked_append_b32", ctx_min=100, ctx_max=700,
                                          extra_tokens=2650, seed=31)
 
 
-def test_append_n_chunked_bitexact():
-    w = LONG_APPEND
+# and a batch of 7 taking 997 tokens, then 1021: 6979 and 7147 rows, neither a multiple of the
+# 16-row groups nor of the pack kernel's 4 rows, groups straddling sequences
+ODD_APPEND = LONG_APPEND.replace(name="chunked_append_b7_odd", batch=7, extra_tokens=2100, seed=33)
+
+
+@pytest.mark.parametrize("w,ns", [(LONG_APPEND, (2048, 600)), (ODD_APPEND, (997, 1021))],
+                         ids=["b32", "b7_odd"])
+def test_append_n_chunked_bitexact(w, ns):
     log(f"chunked append parity: workload {w.name}")
     inst = synth.make(w)
     s = Setup(inst)
     orc = oracle_cache(inst, s.cache.spill_slots)
     lens = inst.seq_lens.copy()
-    for n in (2048, 600):
+    for n in ns:
         assert w.batch * n > 4096
         k, v = _chunk_tokens(w, lens, n)
         zf.zf_append_kv_n(s.cache, s.seqs, dev(k), dev(v))
@@ -385,7 +391,7 @@ def test_append_n_chunked_bitexact():
 
 @pytest.mark.parametrize("fault", ["spill", "length", "page"])
 def test_append_n_chunked_errors_change_no_defined_state(fault):
-    """The chunked form fails whole: a pool with room for a few raw blocks only (ZF_DEV_ESPILL),
+    """The grouped form fails whole: a pool with room for a few raw blocks only (ZF_DEV_ESPILL),
     one sequence whose new rows pass its page table's end (ZF_DEV_ELEN), or one new row on an
     out-of-range page id (ZF_DEV_EPAGE).  Lengths, spill_top, every defined row and slot, and
     the memory past the pool's end stay as they were."""
