@@ -551,30 +551,39 @@ constexpr uint32_t kGlAggregate = 1u << 30;
 constexpr uint32_t kGlInclusive = 2u << 30;
 constexpr uint32_t kGlValue = (1u << 30) - 1u;  // raw blocks of a call: <= 2^24 rows x 32 < 2^30
 
-// kPackRows new rows per workgroup (block j of each on threads 8j .. 8j + 7), their loads issued
-// together: 4 for the grouped form's many rows, 1 for the two-launch form's few, where the
-// workgroups' number sets the latency.  words: the grouped form's look-back words (the
+// kPackRows new rows per workgroup, two at a time: 4 lanes per 64-value block, 16 values each
+// (two 16-byte loads), so a row takes at most 128 lanes (32 blocks).  Every row's loads go out
+// together, before the lookups of the rows' pages (dependent scalar round trips): the new
+// values do not depend on where they go.  words: the grouped form's look-back words (the
 // row_spill entries of each group's first row, which hold nothing yet), cleared here.
 template <int kPackRows>
 __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, uint8_t* sm,
                                                      uint8_t* nib, uint8_t* base, uint32_t* row_flags,
                                                      uint32_t* words) {
-  const int R = s.B * n, r0 = blockIdx.x * kPackRows, tid = threadIdx.x, j = tid >> 3, lane8 = tid & 7;
+  static_assert(kPackRows % 2 == 0, "two rows per pass");
+  constexpr int kPasses = kPackRows / 2;
+  const int R = s.B * n, r0 = blockIdx.x * kPackRows, tid = threadIdx.x;
+  const int second = tid >> 7, j = (tid >> 2) & 31, qtr = tid & 3;  // row 2p + second of pass p
+  const int nb = g.nb(), half = j % nb, hk = j / nb, h = hk >> 1, kv = hk & 1;
   const bool has = j < g.blocks_per_row();
   __shared__ uint32_t s_f[kPackRows];
   if (tid < kPackRows) s_f[tid] = 0u;
-  // the new values do not depend on where they go: all their loads go out before the lookups
-  // of the rows' pages (dependent scalar round trips)
-  uint4 in[kPackRows];
+  uint4 lo[kPasses], hi[kPasses];
 #pragma unroll
-  for (int i = 0; i < kPackRows; ++i)
-    if (has && r0 + i < R) in[i] = load_new(g, r0 + i, j, lane8, k_new, v_new);
+  for (int p = 0; p < kPasses; ++p) {
+    const int r = r0 + 2 * p + second;
+    if (has && r < R) {
+      const uint4* src = reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)r * g.H + h) * g.D +
+                                                        half * kBlock + qtr * 16);
+      lo[p] = src[0];
+      hi[p] = src[1];
+    }
+  }
   int32_t L[kPackRows];  // the lengths first, then the page-table entries they lead to
 #pragma unroll
   for (int i = 0; i < kPackRows; ++i) L[i] = r0 + i < R ? s.lens[(r0 + i) / n] : 0;
   NewPos at[kPackRows];
-  int64_t row[kPackRows];
 #pragma unroll
   for (int i = 0; i < kPackRows; ++i) {
     const int r = r0 + i;
@@ -584,25 +593,53 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, c
       uint32_t err;
       at[i] = append_pos_at(g, s, r / n, r % n, n, L[i], &err);
     }
-    row[i] = at[i].row;
   }
   __syncthreads();  // s_f cleared
-  NewBlock o[kPackRows];
+  uint32_t sm4[kPasses][4], nib2[kPasses][2], bexp[kPasses];
 #pragma unroll
-  for (int i = 0; i < kPackRows; ++i) {
-    if (has && row[i] >= 0) {
-      o[i] = classify_loaded(in[i]);
-      if (lane8 == 0 && o[i].raw) atomicOr(&s_f[i], 1u << j);
+  for (int p = 0; p < kPasses; ++p) {
+    const NewPos a = second ? at[2 * p + 1] : at[2 * p];
+    if (!has || a.row < 0) continue;  // uniform over the block's 4 lanes
+    const uint32_t w0[4] = {lo[p].x, lo[p].y, lo[p].z, lo[p].w};
+    const uint32_t w1[4] = {hi[p].x, hi[p].y, hi[p].z, hi[p].w};
+    Window wa = window8(w0);
+    const Window wb = window8(w1);
+    wa.emin = min(wa.emin, wb.emin);
+    wa.emax = max(wa.emax, wb.emax);
+    wa.special |= wb.special;
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) {
+      wa.emin = min(wa.emin, (uint32_t)__shfl_xor((int)wa.emin, o, 4));
+      wa.emax = max(wa.emax, (uint32_t)__shfl_xor((int)wa.emax, o, 4));
+      wa.special |= (uint32_t)__shfl_xor((int)wa.special, o, 4);
     }
+    const uint32_t raw = wa.special | (uint32_t)(wa.emax - wa.emin > 15u);
+    bexp[p] = raw ? 0u : wa.emin;
+    uint32_t s0[2], s1[2], hio;
+    pack8(w0, bexp[p], raw, s0, nib2[p][0], hio);
+    pack8(w1, bexp[p], raw, s1, nib2[p][1], hio);
+    sm4[p][0] = s0[0];
+    sm4[p][1] = s0[1];
+    sm4[p][2] = s1[0];
+    sm4[p][3] = s1[1];
+    if (qtr == 0 && raw) atomicOr(&s_f[2 * p + second], 1u << j);
   }
   __syncthreads();
 #pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const NewPos a = second ? at[2 * p + 1] : at[2 * p];
+    if (!has || a.row < 0) continue;
+    const int64_t v0 = (((int64_t)a.pid * g.H + h) * 2 + kv) * g.T * g.D + (int64_t)a.slot * g.D + half * kBlock +
+                       qtr * 16;
+    *reinterpret_cast<uint4*>(sm + v0) = make_uint4(sm4[p][0], sm4[p][1], sm4[p][2], sm4[p][3]);
+    *reinterpret_cast<uint2*>(nib + (v0 >> 1)) = make_uint2(nib2[p][0], nib2[p][1]);
+    if (qtr == 0) base[v0 / kBlock] = (uint8_t)bexp[p];
+  }
+#pragma unroll
   for (int i = 0; i < kPackRows; ++i) {
-    if (has && row[i] >= 0) store_new(g, at[i], j, lane8, o[i], sm, nib, base);
-    if (tid == i && row[i] >= 0) {
-      const uint32_t f = s_f[i];
-      row_flags[row[i]] = f;
-      if (words && (r0 + i) % kGroupRows == 0) words[row[i]] = 0u;
+    if (tid == i && at[i].row >= 0) {
+      row_flags[at[i].row] = s_f[i];
+      if (words && (r0 + i) % kGroupRows == 0) words[at[i].row] = 0u;
     }
   }
 }
@@ -1281,8 +1318,8 @@ hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int
                        c->spill_top, c->spill_slots, c->status);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(append_pack_k<1>, dim3(rows), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib, c->base,
-                     c->row_flags, nullptr);
+  hipLaunchKernelGGL(append_pack_k<2>, dim3((rows + 1) / 2), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
+                     c->base, c->row_flags, nullptr);
   size_t lds = 2 * (size_t)rows * sizeof(uint32_t);
   hipLaunchKernelGGL(append_commit_k, dim3(1), dim3(kAppendThreads), lds, st, g, s, n, k_new, v_new,
                      c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
