@@ -777,11 +777,16 @@ __device__ uint32_t group_look_back(const Geom& g, const SeqView& s, int n, cons
 }
 
 // One group per workgroup: its look-back, its rows' row_spill entries (but the first row's)
-// and its raw blocks' spill slots.
+// and its raw blocks' spill slots.  Wave 0 reads the rows' flag words and then walks the
+// look-back; meanwhile waves 1..3 load the new values of the raw blocks (their slots need the
+// prefix, their nibbles do not), 8 lanes per block, every load out at once.
+constexpr int kCommitItems = 22;  // blocks per 8-lane group of waves 1..3: 24 groups x 22 >= 16 x 32
+
 __global__ __launch_bounds__(256) void append_group_commit_k(
     Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint32_t* __restrict__ row_flags, uint32_t* row_spill, uint8_t* spill, const uint64_t* spill_top,
     uint64_t spill_slots, uint32_t* status) {
+  static_assert(24 * kCommitItems >= kGroupRows * 32, "waves 1..3 cover a group's blocks");
   __shared__ uint32_t s_flags[kGroupRows], s_first[kGroupRows];
   __shared__ uint64_t s_base;
   const int R = s.B * n, G = blockIdx.x, r0 = G * kGroupRows, tid = threadIdx.x;
@@ -789,15 +794,34 @@ __global__ __launch_bounds__(256) void append_group_commit_k(
   uint32_t e0;
   const int64_t row0 = append_row(g, s, r0 / n, r0 % n, n, &e0);
   if (row0 < 0) return;  // no word: the call fails in the last step
-  if (tid < 64) {
+  int64_t row = -1;
+  uint32_t f = 0u;
+  if (tid < rows) {
+    uint32_t e;
     const int r = r0 + tid;
-    int64_t row = -1;
-    uint32_t f = 0u;
-    if (tid < rows) {
-      uint32_t e;
-      row = append_row(g, s, r / n, r % n, n, &e);
-      if (row >= 0) f = row_flags[row];
+    row = append_row(g, s, r / n, r % n, n, &e);
+    if (row >= 0) f = row_flags[row];
+  }
+  if (tid < kGroupRows) s_flags[tid] = f;
+  __syncthreads();
+  const int nb = g.nb(), D = g.D, H = g.H;
+  const uint32_t rb = 2u * H * nb, nblk = (uint32_t)rows * rb;
+  const int lane8 = tid & 7, grp = (tid - 64) >> 3;  // waves 1..3: 24 groups of 8 lanes
+  uint4 in[kCommitItems];
+  uint32_t take = 0u;  // bit u: item u is a raw block's piece
+  if (tid >= 64) {
+#pragma unroll
+    for (int u = 0; u < kCommitItems; ++u) {
+      const uint32_t m = (uint32_t)grp + 24u * u;
+      if (m >= nblk) continue;
+      const uint32_t i = m / rb, j = m - i * rb;
+      if (!((s_flags[i] >> j) & 1u)) continue;
+      take |= 1u << u;
+      const uint32_t hk = j / nb, half = j - hk * nb, h = hk >> 1, kv = hk & 1;
+      in[u] = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)(r0 + i) * H + h) * D + half * kBlock +
+                                              lane8 * 8);
     }
+  } else {
     const uint32_t c = __popc(f);
     uint32_t incl = c;
 #pragma unroll
@@ -815,48 +839,23 @@ __global__ __launch_bounds__(256) void append_group_commit_k(
       s_base = *spill_top + before;
     }
     const uint32_t ex = incl - c;
-    if (tid < kGroupRows) {
-      s_flags[tid] = f;
-      s_first[tid] = ex;
-    }
+    if (tid < kGroupRows) s_first[tid] = ex;
     if (tid > 0 && row >= 0) row_spill[row] = (uint32_t)(*spill_top + before + ex);
   }
   __syncthreads();
-  // spill slots of the raw blocks: 8 lanes per block, two blocks per step so that their loads
-  // fly together
+  if (tid < 64) return;
   const uint64_t base = s_base;
-  const int nb = g.nb(), D = g.D, H = g.H;
-  const uint32_t rb = 2u * H * nb, nblk = (uint32_t)rows * rb;
-  const int lane8 = tid & 7;
-  for (uint32_t m0 = tid >> 3; m0 < nblk; m0 += 2 * (256 >> 3)) {
-    uint4 in[2];
-    uint64_t idx[2];
-    bool take[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t m = m0 + u * (256 >> 3);
-      take[u] = false;
-      if (m >= nblk) continue;
-      const uint32_t i = m / rb, j = m - i * rb;
-      const uint32_t f = s_flags[i];
-      idx[u] = base + s_first[i] + __popc(f & ((1u << j) - 1u));
-      // (a slot past the pool: the call fails in the last step)
-      take[u] = ((f >> j) & 1u) && idx[u] < spill_slots;
-      if (take[u]) {
-        const uint32_t hk = j / nb, half = j - hk * nb, h = hk >> 1, kv = hk & 1;
-        in[u] = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + ((int64_t)(r0 + i) * H + h) * D +
-                                                half * kBlock + lane8 * 8);
-      }
-    }
+  for (int u = 0; u < kCommitItems; ++u) {
+    if (!((take >> u) & 1u)) continue;
+    const uint32_t m = (uint32_t)grp + 24u * u, i = m / rb, j = m - i * rb;
+    const uint64_t idx = base + s_first[i] + __popc(s_flags[i] & ((1u << j) - 1u));
+    if (idx >= spill_slots) continue;  // a slot past the pool: the call fails in the last step
+    const uint32_t w[4] = {in[u].x, in[u].y, in[u].z, in[u].w};
+    uint32_t hi = 0u;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!take[u]) continue;
-      const uint32_t w[4] = {in[u].x, in[u].y, in[u].z, in[u].w};
-      uint32_t hi = 0u;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
-      *reinterpret_cast<uint32_t*>(spill + idx[u] * 32u + lane8 * 4) = hi;
-    }
+    for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
+    *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
   }
   (void)status;
 }
