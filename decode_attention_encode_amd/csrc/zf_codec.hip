@@ -1021,6 +1021,11 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
     commit_one(s, n, spill_top, spill_slots, status, sync);
     return;
   }
+  const bool has = j < g.blocks_per_row();
+  // the new values do not depend on where they go: their loads go out before the lookups
+  // (unconditionally, from block 0 on lanes past the row's blocks: a load inside a branch is
+  // waited for at the branch's end)
+  const uint4 in = load_new(g, r, has ? j : 0, lane8, k_new, v_new);
   const uint64_t E = sync[kSyncEpoch];
   const uint32_t tag = sync_tag(E);
   const uint64_t top = *spill_top;
@@ -1028,9 +1033,8 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
   uint32_t err;
   const NewPos at = append_pos(g, s, b, r - b * n, n, &err);
   const int64_t row = at.row;
-  const bool has = j < g.blocks_per_row();
   NewBlock o{};
-  if (has) o = classify_new(g, r, j, lane8, k_new, v_new);
+  if (has) o = classify_loaded(in);
   const uint32_t f = row_flag_word(has, j, lane8, o.raw);
   if (tid == 0) {
     // the word is built from the epoch, the length (through err and row) and spill_top as
