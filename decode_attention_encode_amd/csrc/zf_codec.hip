@@ -785,7 +785,7 @@ constexpr int kCommitItems = 22;  // blocks per 8-lane group of waves 1..3: 24 g
 __global__ __launch_bounds__(256) void append_group_commit_k(
     Geom g, SeqView s, int n, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint32_t* __restrict__ row_flags, uint32_t* row_spill, uint8_t* spill, const uint64_t* spill_top,
-    uint64_t spill_slots, uint32_t* status) {
+    uint64_t spill_slots, const uint64_t* sync) {
   static_assert(24 * kCommitItems >= kGroupRows * 32, "waves 1..3 cover a group's blocks");
   __shared__ uint32_t s_flags[kGroupRows], s_first[kGroupRows];
   __shared__ uint64_t s_base;
@@ -831,8 +831,10 @@ __global__ __launch_bounds__(256) void append_group_commit_k(
     }
     const uint32_t total = (uint32_t)__shfl((int)incl, kGroupRows - 1, 64);
     if (tid == 0) __hip_atomic_store(&row_spill[row0], kGlAggregate | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t failed = 0u;
-    const uint32_t before = group_look_back(g, s, n, row_spill, G, &failed);
+    // the cache's give-up hook (a test of the failure path): every group with groups before it
+    // acts as if its wait had run out
+    uint32_t failed = G > 0 && sync && sync[kSyncGiveUp] != 0u ? 1u : 0u;
+    const uint32_t before = failed ? 0u : group_look_back(g, s, n, row_spill, G, &failed);
     if (tid == 0) {
       // a wait that ran out leaves the word at its aggregate: the last step then fails the call
       if (!failed) __hip_atomic_store(&row_spill[row0], kGlInclusive | (before + total), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -857,7 +859,6 @@ __global__ __launch_bounds__(256) void append_group_commit_k(
     for (int v = 0; v < 8; ++v) hi |= (exp_of(w[v >> 1] >> (16 * (v & 1))) >> 4) << (4 * v);
     *reinterpret_cast<uint32_t*>(spill + idx * 32u + lane8 * 4) = hi;
   }
-  (void)status;
 }
 
 // The last step of the grouped form (one workgroup): every sequence's length and the page ids
@@ -1316,7 +1317,7 @@ hipError_t launch_append(const Geom& g, const zf_cache* c, const zf_seqs* q, int
     hipLaunchKernelGGL(append_pack_k<4>, dim3((rows + 3) / 4), dim3(256), 0, st, g, s, n, k_new, v_new, c->sm, c->nib,
                        c->base, c->row_flags, c->row_spill);
     hipLaunchKernelGGL(append_group_commit_k, dim3(ngroups), dim3(256), 0, st, g, s, n, k_new, v_new, c->row_flags,
-                       c->row_spill, c->spill, c->spill_top, c->spill_slots, c->status);
+                       c->row_spill, c->spill, c->spill_top, c->spill_slots, c->append_sync);
     hipLaunchKernelGGL(append_group_finish_k, dim3(1), dim3(kScanThreads), 0, st, g, s, n, c->row_spill,
                        c->spill_top, c->spill_slots, c->status);
     return hipGetLastError();

@@ -95,7 +95,8 @@ typedef struct {
 
 /* append_sync: [0, 64) hand-over words, [64] the epoch (calls so far), [65] a test hook: nonzero
  * makes the one-launch append's packing workgroups give up instead of waiting for the words of
- * the rows before theirs, so the call ends with ZF_DEV_ESYNC and changes nothing; zero in use. */
+ * the rows before theirs (and the grouped multi-token form's groups instead of walking their
+ * look-back), so the call ends with ZF_DEV_ESYNC and changes nothing; zero in use. */
 #define ZF_APPEND_SYNC_WORDS 66
 
 typedef struct {

@@ -432,6 +432,45 @@ def test_append_n_chunked_errors_change_no_defined_state(fault):
         assert np.array_equal(a[msk], b_[msk]), m
 
 
+def test_append_n_grouped_give_up_reports_and_changes_nothing():
+    """The cache's give-up hook makes every group of the grouped form (more than 4096 new rows)
+    that has groups before it skip its look-back as if the wait had run out: its word stays at
+    its aggregate, the last step sees it and the call ends with ZF_DEV_ESYNC, lengths, spill_top
+    and every defined row and slot unchanged.  With the hook cleared the same call succeeds and
+    matches the oracle bit for bit."""
+    w = LONG_APPEND.replace(name="grouped_give_up_b8", batch=8, extra_tokens=700, seed=34)
+    n = 600  # 4800 rows
+    inst = synth.make(w)
+    s = Setup(inst)
+    orc = oracle_cache(inst, s.cache.spill_slots)
+    need = orc.spill_top
+    rows = valid_rows(inst)
+    names = ("sm", "nib", "base", "row_flags", "row_spill")
+    before = {m: host(getattr(s.cache, m)).copy() for m in names}
+    spill_before = host(s.cache.spill)[:need].copy()
+    k, v = _chunk_tokens(w, inst.seq_lens, n)
+    s.cache.append_sync[zf.ZF_SYNC_GIVE_UP] = 1
+    zf.zf_append_kv_n(s.cache, s.seqs, dev(k), dev(v))
+    torch.cuda.synchronize()
+    s.cache.append_sync[zf.ZF_SYNC_GIVE_UP] = 0
+    assert s.status() & zf.ZF_DEV_ESYNC
+    assert np.array_equal(host(s.seqs.seq_lens), inst.seq_lens)
+    assert int(host(s.cache.spill_top)[0]) == need
+    assert np.array_equal(host(s.cache.spill)[:need], spill_before)
+    for m in names:
+        a, b_ = host(getattr(s.cache, m)), before[m]
+        msk = np.broadcast_to(rows[:, None, None, :, None], a.shape) if a.ndim == 5 else rows
+        assert np.array_equal(a[msk], b_[msk]), m
+    s.cache.status.zero_()
+    lens = inst.seq_lens.copy()
+    zf.zf_append_kv_n(s.cache, s.seqs, dev(k), dev(v))
+    assert orc.append_n(lens, inst.page_table, k, v) == oracle.OK
+    torch.cuda.synchronize()
+    assert s.status() == 0
+    assert np.array_equal(host(s.seqs.seq_lens), lens)
+    compare_packed(s.cache, orc, valid_rows(inst, lens), "grouped append after a given-up one")
+
+
 # other geometries of the format: head_dim 64 (16 blocks per row), head_dim 256 with 4 kv heads
 # (32 blocks per row, every flag bit), 2 kv heads
 GEOMS = [SMALL.replace(name="small_d64", head_dim=64, seed=51),
