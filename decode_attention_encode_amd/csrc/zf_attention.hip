@@ -655,8 +655,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   const int nsplit = max(1, (npages + a.pps - 1) / a.pps);
   if (s >= nsplit) return;
 
-  // q in fp64, pair order, for the exact-score path: [head][quarter][pair] = (lo, hi) dims
-  // (rows of 17 pairs: the four quarters read in one instruction fall in different banks)
+  // q in fp64, pair order, the B operand of the exact-score MFMA: [head][quarter][pair] =
+  // (lo, hi) dims (rows of 17 pairs: the 16 (head, quarter) rows that one read instruction
+  // touches fall in different banks)
   __shared__ double2 s_q64[G][4][17];
   if (tid < G * 64) {
     const int i = tid >> 6, qq = (tid >> 4) & 3, k = tid & 15;
