@@ -51,6 +51,10 @@ constexpr uint64_t kLbAggregate = (uint64_t)1 << 62;
 constexpr uint64_t kLbInclusive = (uint64_t)2 << 62;
 constexpr uint64_t kLbValue = ((uint64_t)1 << 62) - 1u;
 constexpr uint32_t kLbPolls = 1u << 22;  // bound on one look-back wait (~ seconds; none is expected)
+// Pause between polls of a look-back word (units of 64 clocks): the words are read through the
+// coherence point shared by all XCDs, and thousands of workgroups polling it back to back slow
+// everyone's other traffic (encode: 302 us at 1, 288 us at 32, no better beyond)
+constexpr int kLbSleep = 32;
 
 // Pages of sequence b that hold tokens (0 for an invalid length).
 __device__ __forceinline__ int pages_of(const SeqView& s, const Geom& g, int b) {
@@ -93,7 +97,7 @@ __device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* l
           w = kLbAggregate;
           break;
         }
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(kLbSleep);
       }
     }
     const uint64_t stop = __ballot((w >> 62) == 2u);
