@@ -156,7 +156,7 @@ def main():
     layers = []
     for _ in range(NL):  # one packed cache per layer (same data), own lengths
         cache = zf.PackedCache.empty(inst.num_pages, T, H, D, spill_slots, device=dev)
-        seqs = zf.Seqs(pt_dev, to(lens0.copy()), max_len)
+        seqs = zf.Seqs(pt_dev, to(lens0.copy()), max_len, page_hint(torch, B, H, inst.page_table.shape[1], dev))
         zf.zf_encode_kv(cache, seqs, raw, zf.encode_workspace(seqs))
         layers.append((cache, seqs))
     torch.cuda.synchronize()
@@ -480,7 +480,8 @@ def per_config(torch, zf, synth, key, dev):
     for _ in range(NL):
         cache = zf.PackedCache.empty(inst.num_pages, T, H, D, int(inst.seq_lens.sum()) * 2 * H * (D // 64),
                                      device=dev)
-        seqs = zf.Seqs(to(inst.page_table), to(inst.seq_lens.copy()), int(inst.seq_lens.max()))
+        seqs = zf.Seqs(to(inst.page_table), to(inst.seq_lens.copy()), int(inst.seq_lens.max()),
+                       page_hint(torch, w.batch, H, inst.page_table.shape[1], dev))
         zf.zf_encode_kv(cache, seqs, raw, zf.encode_workspace(seqs))
         layers.append((cache, seqs))
     torch.cuda.synchronize()
@@ -721,6 +722,11 @@ def prefill_chunks(torch, zf, synth, dev, n=512, chunks=4):
             "prefill_encode_rows_per_s": round(rows / t_enc, 1),
             "prefill_chunked_vs_encode_time": round(sum(ts) / t_enc, 3),
             "prefill_chunked_planes_equal_encode": bool(same)}
+
+
+def page_hint(torch, batch: int, num_kv_heads: int, max_pages: int, dev):
+    """Device array for the attention's page-order hint (the encode fills it, appends raise it)."""
+    return torch.zeros((batch, num_kv_heads, max_pages), dtype=torch.int32, device=dev)
 
 
 def fp32_scale(head_dim: int) -> float:

@@ -50,7 +50,7 @@ class zf_cache(ctypes.Structure):
 class zf_seqs(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
-                ("max_seq_len", ctypes.c_int32)]
+                ("max_seq_len", ctypes.c_int32), ("kmax", ctypes.c_void_p)]
 
 
 _lib = None
@@ -165,10 +165,11 @@ class Seqs:
     page_table: torch.Tensor  # int32 [B][max_pages] on the device
     seq_lens: torch.Tensor    # int32 [B] on the device
     max_seq_len: int          # host bound
+    kmax: Optional[torch.Tensor] = None  # uint32 (int32) [B][num_kv_heads][max_pages]: page hint
 
     def c(self) -> zf_seqs:
         B, maxp = self.page_table.shape
-        return zf_seqs(B, maxp, _ptr(self.page_table), _ptr(self.seq_lens), self.max_seq_len)
+        return zf_seqs(B, maxp, _ptr(self.page_table), _ptr(self.seq_lens), self.max_seq_len, _ptr(self.kmax))
 
 
 # ---------------------------------------------------------------------- the C entry points

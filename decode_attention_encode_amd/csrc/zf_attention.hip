@@ -103,6 +103,7 @@ struct AttnArgs {
   int32_t order;   // number the (sequence, split) groups longest sequence first
   const int32_t* pt;
   const int32_t* lens;
+  const uint32_t* kmax;  // [B][H][maxp] largest K exponent field per page, or null
   const uint16_t* q;
   double scale_log2e;
   float scale_log2e_f32;  // the same in fp32
@@ -626,12 +627,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   s = __builtin_amdgcn_readfirstlane(s);
   h = __builtin_amdgcn_readfirstlane(h);
 
-  // this wave's pages: p_first + 8n; lane n reads the page id of page n.  The table row and q
+  // this wave's pages: p_first + 8n; lane n reads the page id (and hint) of page n.  The table row and q
   // are read together with the length, not after it (one memory round trip less before the
   // first page); table entries past the sequence's end are never used.
   const int p_first = s * a.pps + wave;
   int32_t pt_lane = 0;
-  if (p_first + kWaves * lane < a.maxp) pt_lane = a.pt[(int64_t)b * a.maxp + p_first + kWaves * lane];
+  uint32_t km_lane = 0u;  // the page's K-exponent hint
+  if (p_first + kWaves * lane < a.maxp) {
+    pt_lane = a.pt[(int64_t)b * a.maxp + p_first + kWaves * lane];
+    if (a.kmax) km_lane = a.kmax[((int64_t)b * a.H + h) * a.maxp + p_first + kWaves * lane];
+  }
   // B operand of the score MFMA: column t is query head t / kParts (each head kParts times),
   // head_dim 32*qd + 8c + (0,4,1,5,2,6,3,7)[k]
   bf16x8 qb[4];
@@ -684,6 +689,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
       my_pid = -1;  // page skipped: read page 0, count no token
     }
   }
+  // With the hint, the wave takes first its page with the largest K exponent (the lowest such
+  // page on ties): its scores are the likeliest to be near the final maximum, so the running
+  // maximum (and through the first-page exchange, every wave's bound) settles early and fewer
+  // pages need the fp64 scores.  Steps 0 and `first` swap their pages.
+  int first = 0;
+  if (a.kmax) {
+    uint32_t key = lane < nmine && my_pid >= 0 ? (km_lane << 6) | (63u - (uint32_t)lane) : 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) key = max(key, (uint32_t)__shfl_xor((int)key, o, 64));
+    first = __builtin_amdgcn_readfirstlane(key ? 63 - (int)(key & 63u) : 0);
+    if (first > 0) {
+      const int32_t p0 = __builtin_amdgcn_readlane(my_pid, 0), pf = __builtin_amdgcn_readlane(my_pid, first);
+      my_pid = lane == 0 ? pf : (lane == first ? p0 : my_pid);
+    }
+  }
   // pin the q unpacking here: placed after the first page loads, its wait for q would also
   // wait for them
   asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
@@ -727,7 +747,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_k(AttnArgs a, Loader ld) {
   };
   auto ntok_at = [&](int n) -> int {
     if (__builtin_amdgcn_readlane(my_pid, n) < 0) return 0;
-    return min(kT, L - (p_first + kWaves * n) * kT);
+    const int ln = n == 0 ? first : (n == first ? 0 : n);  // the page's place in the sequence
+    return min(kT, L - (p_first + kWaves * ln) * kT);
   };
   auto slot_of = [&](int n) -> uint32_t { return ring + (uint32_t)(n & 1) * kSlotBytes; };
   auto meta_of = [&](int n) -> uint32_t { return meta_ring + (uint32_t)(n & (kMetaRing - 1)) * kMetaBytes; };
@@ -1219,6 +1240,7 @@ static hipError_t launch(const Loader& ld, int32_t num_pages, int32_t H, const z
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   a.pt = q->page_table;
   a.lens = q->seq_lens;
+  a.kmax = q->kmax;
   a.q = qv;
   a.scale_log2e = (double)scale * kLog2e;
   a.scale_log2e_f32 = (float)a.scale_log2e;

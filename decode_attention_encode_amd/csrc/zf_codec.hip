@@ -24,7 +24,13 @@ struct SeqView {
   int32_t B, maxp, max_seq_len;
   const int32_t* pt;
   int32_t* lens;
+  uint32_t* kmax;  // [B][H][maxp] largest K exponent field per (sequence, kv head, page), or null
 };
+
+// The K-exponent hint of (sequence b, kv head h, logical page p).
+__device__ __forceinline__ int64_t kmax_at(const SeqView& s, int H, int b, int h, int p) {
+  return ((int64_t)b * H + h) * s.maxp + p;
+}
 
 // Whether `need` more slots fit in a pool of `slots` whose first `top` are taken (a top beyond
 // the pool, which no call leaves behind, counts as full).
@@ -141,7 +147,10 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
     if (p == 0 && tid == 0) set_status(status, ZF_DEV_ELEN);
     return;  // the sequence counts as empty
   }
-  if (rows == 0) return;  // past the sequence's end: no page, no word
+  if (rows == 0) {  // past the sequence's end: no page, no word, no K
+    if (s.kmax && tid < g.H) s.kmax[kmax_at(s, g.H, b, tid, p)] = 0u;
+    return;
+  }
   const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
   if (pid < 0 || pid >= g.P) {
     if (tid == 0) set_status(status, ZF_DEV_EPAGE);
@@ -149,7 +158,9 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
   }
 
   __shared__ uint32_t s_flags[64], s_first[64];
+  __shared__ uint32_t s_kmax[16];  // per kv head: the largest exponent field of the page's K rows
   if (tid < 64) s_flags[tid] = 0u;
+  if (tid < 16) s_kmax[tid] = 0u;
   __syncthreads();
 
   const int nb = g.nb();
@@ -201,10 +212,9 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
       raw_mask |= raw_blk << u;
       if (qtr == 0) {
         base[v0 / kBlock] = (uint8_t)bexp;
-        if (raw_blk) {
-          const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
-          atomicOr(&s_flags[slot], 1u << (hk * nb + half));
-        }
+        const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+        if (raw_blk) atomicOr(&s_flags[slot], 1u << (hk * nb + half));
+        if (!(hk & 1)) atomicMax(&s_kmax[hk >> 1], a.emax);
       }
     }
     return raw_mask;
@@ -224,6 +234,7 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
   }
   __syncthreads();
 
+  if (s.kmax && tid < g.H) s.kmax[kmax_at(s, g.H, b, tid, p)] = s_kmax[tid];
   // wave 0: row flags, the page's raw count, its prefix by look-back, row_spill
   if (tid < 64) {
     const uint32_t f = tid < rows ? s_flags[tid] : 0u;
@@ -455,23 +466,23 @@ constexpr uint64_t kTagMod = (1u << 27) - 1u;
 // take them.
 struct NewPos {
   int64_t row;
-  int32_t pid, slot;
+  int32_t pid, slot, lp;  // lp: the logical page of the sequence
 };
 
 __device__ __forceinline__ NewPos append_pos_at(const Geom& g, const SeqView& s, int b, int j, int n, int32_t L,
                                                 uint32_t* err) {
   if (L < 0 || (int64_t)L + n > (int64_t)s.maxp * g.T || (int64_t)L + n > s.max_seq_len) {
     *err = ZF_DEV_ELEN;
-    return NewPos{-1, 0, 0};
+    return NewPos{-1, 0, 0, 0};
   }
   const int32_t t = L + j, p = t / g.T, slot = t - p * g.T;
   const int32_t pid = s.pt[(int64_t)b * s.maxp + p];
   if (pid < 0 || pid >= g.P) {
     *err = ZF_DEV_EPAGE;
-    return NewPos{-1, 0, 0};
+    return NewPos{-1, 0, 0, 0};
   }
   *err = 0;
-  return NewPos{(int64_t)pid * g.T + slot, pid, slot};
+  return NewPos{(int64_t)pid * g.T + slot, pid, slot, p};
 }
 
 __device__ __forceinline__ int64_t append_row_at(const Geom& g, const SeqView& s, int b, int j, int n,
@@ -490,7 +501,7 @@ __device__ __forceinline__ int64_t append_row(const Geom& g, const SeqView& s, i
 
 // Block j of a new row, classified and packed in registers (8 lanes, 8 values each).
 struct NewBlock {
-  uint32_t sm0, sm1, nib, hi, bexp, raw;
+  uint32_t sm0, sm1, nib, hi, bexp, raw, emax;
 };
 
 // New row r is u16 [H][D] of K and of V; block j covers half j % nb of head j / nb / 2, K or V
@@ -513,6 +524,7 @@ __device__ __forceinline__ NewBlock classify_loaded(const uint4 in) {
     win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
   }
   NewBlock o;
+  o.emax = win.emax;
   o.raw = win.special | (uint32_t)(win.emax - win.emin > 15u);
   o.bexp = o.raw ? 0u : win.emin;
   uint32_t smw[2];
@@ -591,7 +603,7 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, c
 #pragma unroll
   for (int i = 0; i < kPackRows; ++i) {
     const int r = r0 + i;
-    at[i] = NewPos{-1, 0, 0};  // past the last row, or a position the call cannot take
+    at[i] = NewPos{-1, 0, 0, 0};  // past the last row, or a position the call cannot take
                                // (append_commit_k or append_group_finish_k reports it)
     if (r < R) {
       uint32_t err;
@@ -618,6 +630,7 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, c
       wa.special |= (uint32_t)__shfl_xor((int)wa.special, o, 4);
     }
     const uint32_t raw = wa.special | (uint32_t)(wa.emax - wa.emin > 15u);
+    if (qtr == 0 && !kv && s.kmax) atomicMax(&s.kmax[kmax_at(s, g.H, (r0 + 2 * p + second) / n, h, a.lp)], wa.emax);
     bexp[p] = raw ? 0u : wa.emin;
     uint32_t s0[2], s1[2], hio;
     pack8(w0, bexp[p], raw, s0, nib2[p][0], hio);
@@ -1051,6 +1064,8 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
   if (row >= 0) {
     if (has) store_new(g, at, j, lane8, o, sm, nib, base);
     if (tid == 0) row_flags[row] = f;
+    const int hk = j / g.nb();
+    if (has && lane8 == 0 && !(hk & 1) && s.kmax) atomicMax(&s.kmax[kmax_at(s, g.H, b, hk >> 1, at.lp)], o.emax);
   }
   // the rows before this one: their raw blocks are this row's prefix
   const bool give_up = r > 0 && sync[kSyncGiveUp] != 0u;
@@ -1278,7 +1293,7 @@ __global__ __launch_bounds__(256) void compact_copy_k(CompactWs w, uint8_t* __re
 // ------------------------------------------------------------------------------ host launchers
 
 static SeqView view(const zf_seqs* q) {
-  return SeqView{q->batch, q->max_pages_per_seq, q->max_seq_len, q->page_table, q->seq_lens};
+  return SeqView{q->batch, q->max_pages_per_seq, q->max_seq_len, q->page_table, q->seq_lens, q->kmax};
 }
 
 hipError_t launch_encode(const Geom& g, const zf_cache* c, const zf_seqs* q, const uint16_t* raw,

@@ -105,6 +105,15 @@ typedef struct {
   int32_t* seq_lens;         /* device [batch], tokens present                               */
   int32_t max_seq_len;       /* HOST bound on every seq_lens[b] when the call runs (after an
                                 append: on the grown lengths); sizes grids and workspaces   */
+  uint32_t* kmax;            /* optional device [batch][num_kv_heads][max_pages_per_seq]: per
+                                (sequence, kv head, logical page) the largest bf16 exponent
+                                field among the K values of the page's tokens, 0 for a page
+                                with none.  zf_encode_kv writes every entry; the appends raise
+                                the entries of the pages they write (a call that fails may
+                                leave some raised).  Only a hint: zf_decode_attention takes
+                                each wave's page with the largest entry first, which settles
+                                the running score maximum early; any contents give a correct
+                                result.  NULL: not kept, not used                            */
 } zf_seqs;
 
 /* Bytes of one cache's arrays except spill, for sizing a pool of pages (the paged KV memory of
@@ -218,7 +227,8 @@ zf_status zf_decode_kv(const zf_cache* cache, const zf_seqs* seqs, uint16_t* raw
  * the exact bf16 products wherever a weight may reach 2^-40 of the largest; weights, their
  * sum and the rescales in fp64; products of a value of 2^4 or more summed in fp64; the rest
  * of p.V on the matrix cores with each weight split into bf16 parts (three, exact, for 4
- * query heads per kv head; two, within 2^-17 of it, for 8).  Workspace:
+ * query heads per kv head; two, within 2^-17 of it, for 8).  With seqs->kmax the pages are
+ * visited in another order (the sums are the same up to rounding order).  Workspace:
  * zf_attention_workspace_bytes(...) bytes of device memory, any contents (it holds per-split
  * partials); calls sharing one workspace must not overlap.
  * Requires D == 128, page_size == 16, num_q_heads == 4 * H or 8 * H (Llama-3.1-8B- and

@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the benchmark's
 CPU-baseline leg may import this package; the product path never does.  The arithmetic lives
 in plain C (``zf_oracle.c``: the block codec written from its definition, fp64 attention);
-this module compiles it with gcc and marshals numpy arrays.  It shares no code with the HIP
-library.
+this module compiles it with gcc and marshals numpy arrays; the attention's page-order hint
+(``page_kmax``) is plain numpy here.  It shares no code with the HIP library.
 """
 from __future__ import annotations
 
@@ -188,6 +188,26 @@ class Cache:
                                    ctypes.c_int32(len(lens)), _p(lens), _p(pt),
                                    ctypes.c_int32(pt.shape[1]), _p(out))
         return int(st), out
+
+
+def page_kmax(raw_pages: np.ndarray, seq_lens, page_table) -> np.ndarray:
+    """The attention's page-order hint, from its definition: for each (sequence b, kv head h,
+    logical page p) the largest bf16 exponent field (bits 7..14 of the value) among the K values
+    of the page's tokens t < seq_lens[b]; 0 for a page that holds none.  uint32
+    [B][H][max_pages].  Plain numpy; not part of the pages' method (it only orders the pages
+    the attention visits), so its definition is the whole of it."""
+    P, H, two, T, D = raw_pages.shape
+    pt = np.asarray(page_table, np.int64)
+    B, maxp = pt.shape
+    out = np.zeros((B, H, maxp), np.uint32)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for p in range(min(maxp, -(-L // T))):
+            n = min(T, L - p * T)
+            k = raw_pages[pt[b, p], :, 0, :n, :]            # [H][n][D] bf16 bits
+            e = (k.astype(np.uint32) >> 7) & 0xFF           # exponent fields
+            out[b, :, p] = e.reshape(H, -1).max(axis=1)
+    return out
 
 
 def max_sequences(kv_budget: int, layers: int, context: int, page_size: int, num_kv_heads: int,

@@ -48,7 +48,7 @@ class Setup:
     """One workload resident on the GPU: raw pages, packed cache (GPU-encoded), seqs."""
 
     def __init__(self, inst: synth.Instance, spill_slots: int | None = None, max_seq_len=None,
-                 encode=True, one_launch_append=True):
+                 encode=True, one_launch_append=True, kmax=True):
         self.inst = inst
         w = inst.w
         self.w = w
@@ -59,8 +59,13 @@ class Setup:
                                           w.head_dim, spill_slots,
                                           one_launch_append=one_launch_append)
         cap = inst.page_table.shape[1] * w.page_size
+        # the page-order hint, poisoned: the encode writes every entry
+        hint = None
+        if kmax:
+            B, maxp = inst.page_table.shape
+            hint = torch.full((B, w.num_kv_heads, maxp), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
         self.seqs = zf.Seqs(dev(inst.page_table), dev(inst.seq_lens.copy()),
-                            int(max_seq_len if max_seq_len is not None else cap))
+                            int(max_seq_len if max_seq_len is not None else cap), hint)
         if encode:
             ws = zf.encode_workspace(self.seqs)
             zf.zf_encode_kv(self.cache, self.seqs, self.raw, ws)
@@ -84,6 +89,16 @@ class Setup:
             zf.zf_decode_attention_raw(self.raw, self.seqs, qd, scale, out, ws, self.cache.status)
         torch.cuda.synchronize()
         return out
+
+
+def check_kmax(s: Setup, orc: oracle.Cache, lens, what=""):
+    """The device's page-order hint equals the oracle's, from the oracle cache's decoded pages."""
+    st, raw = orc.decode(lens, s.inst.page_table)
+    assert st == oracle.OK
+    want = oracle.page_kmax(raw, lens, s.inst.page_table)
+    got = host(s.seqs.kmax, np.uint32)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what} kmax: {len(bad)} entries differ, first {bad[:4].tolist()}"
 
 
 def oracle_cache(inst: synth.Instance, spill_slots: int) -> oracle.Cache:

@@ -175,6 +175,40 @@ def test_attention_diffuse_full(key):
     assert torch.equal(out, s.attention(q, packed=False)), "compressed and raw twin differ"
 
 
+@pytest.mark.parametrize("key", ["small", 1, "diffuse8", "split8"])
+@pytest.mark.timeout(600)
+def test_page_hint_only_changes_the_order(key):
+    """The page-order hint (seqs.kmax) decides which page each wave takes first and nothing
+    else: with the exact hint the encode wrote, without a hint, and with an arbitrary one
+    (random, every sequence's last, partly filled page given the largest value so that it
+    comes first) the outputs are within the tolerance of the oracle, and the twin, given the
+    same hint, equals the compressed path bit for bit."""
+    w = workload(key)
+    log(f"attention with and without the page hint: workload {w.name}")
+    inst = synth.make(w)
+    s = Setup(inst)
+    lens = inst.seq_lens.copy()
+    q = synth.query(w, 0)
+    exact = s.seqs.kmax.clone()
+    B, H, maxp = exact.shape
+    rng = np.random.default_rng(17)
+    odd = rng.integers(0, 256, (B, H, maxp)).astype(np.int32)
+    T = w.page_size
+    for b in range(B):
+        if lens[b] > 0:
+            odd[b, :, (lens[b] - 1) // T] = 1000
+    outs = {}
+    for name, hint in (("exact", exact), ("none", None), ("arbitrary", dev(odd))):
+        s.seqs.kmax = hint
+        out = s.attention(q).clone()
+        assert s.status() == 0
+        check(out, inst, lens, q, what=f"{w.name}, {name} hint")
+        assert torch.equal(out, s.attention(q, packed=False)), f"{name} hint: twin differs"
+        outs[name] = out
+    if key == "diffuse8":  # long fp32 sums over hundreds of weights: another order rounds otherwise
+        assert not torch.equal(outs["exact"], outs["none"]), "the hint reordered nothing"
+
+
 @pytest.mark.timeout(600)
 def test_attention_ragged_full():
     w = synth.WORKLOADS[3]

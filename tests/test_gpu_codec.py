@@ -13,7 +13,7 @@ import torch
 import decode_attention_encode_amd as zf
 import oracle
 import synth
-from gpu_util import Setup, compare_packed, dev, host, log, oracle_cache, valid_rows
+from gpu_util import Setup, check_kmax, compare_packed, dev, host, log, oracle_cache, valid_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +34,7 @@ def test_encode_bitexact(key):
     assert s.status() == 0
     orc = oracle_cache(inst, s.cache.spill_slots)
     compare_packed(s.cache, orc, valid_rows(inst), w.name)
+    check_kmax(s, orc, inst.seq_lens, w.name)
     log(f"  raw blocks {orc.spill_top} of {int(inst.seq_lens.sum()) * 32}")
 
 
@@ -69,6 +70,7 @@ def _append_steps(w, steps, check_every=1, one_launch=True):
             assert s.status() == 0
             assert np.array_equal(host(s.seqs.seq_lens), lens)
             compare_packed(s.cache, orc, valid_rows(inst, lens), f"{w.name} step {step}")
+            check_kmax(s, orc, lens, f"{w.name} step {step}")
     return s, inst, lens
 
 
@@ -104,6 +106,7 @@ def test_append_forms_write_the_same_bytes():
     assert one.status() == 0 and two.status() == 0
     for n in ("sm", "nib", "base", "row_flags", "row_spill", "spill", "spill_top"):
         assert np.array_equal(host(getattr(one.cache, n)), host(getattr(two.cache, n))), n
+    assert np.array_equal(host(one.seqs.kmax), host(two.seqs.kmax)), "page hints"
     assert np.array_equal(host(one.seqs.seq_lens), lens)
     assert int(host(one.cache.append_sync)[64]) == 6
 
@@ -332,6 +335,7 @@ def test_append_n_bitexact(key, chunks):
         assert s.status() == 0
         assert np.array_equal(host(s.seqs.seq_lens), lens)
         compare_packed(s.cache, orc, valid_rows(inst, lens), f"{w.name} chunk {i} (n={n})")
+        check_kmax(s, orc, lens, f"{w.name} chunk {i} (n={n})")
 
 
 def test_append_n_spill_exhaustion_changes_no_defined_state():
@@ -386,6 +390,7 @@ def test_append_n_chunked_bitexact(w, ns):
         assert s.status() == 0
         assert np.array_equal(host(s.seqs.seq_lens), lens)
         compare_packed(s.cache, orc, valid_rows(inst, lens), f"{w.name} ({w.batch} x {n} rows)")
+        check_kmax(s, orc, lens, f"{w.name} ({w.batch} x {n} rows)")
         log(f"  {w.batch * n} rows: bit-exact, spill_top {orc.spill_top}")
 
 
