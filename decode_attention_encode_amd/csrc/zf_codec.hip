@@ -135,6 +135,16 @@ constexpr int kEncUnroll = 2;
 // budget is held to 6 waves per SIMD (80 VGPRs, no spills; 8 waves spill and run slower).
 constexpr int kEncWavesPerSimd = 6;
 
+// x / d for x, d < 2^16 by one multiply: with M = floor((2^32 - 1) / d) + 1, x * M / 2^32 exceeds
+// x / d by less than x / 2^32 < 1 / d, which never crosses the next integer (exact when d is a
+// power of two).  The block index math of the encode divides by the blocks per head row and the
+// page size once per chunk; a division there costs a dozen instructions, this one two.
+struct SmallDiv {
+  uint64_t m;
+  __device__ explicit SmallDiv(uint32_t d) : m(0xFFFFFFFFull / d + 1u) {}
+  __device__ uint32_t operator()(uint32_t x) const { return (uint32_t)((x * m) >> 32); }
+};
+
 __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
     Geom g, SeqView s, const uint16_t* __restrict__ raw, uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
     uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags, uint32_t* __restrict__ row_spill,
@@ -167,7 +177,14 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
   const int blocks = 2 * g.H * g.T * nb;
   const int chunks = blocks * 4;  // 16 values each; chunk k: block k / 4, quarter k % 4
   const int64_t page0 = (int64_t)(rows > 0 ? pid : 0) * g.vals_per_page();
-  auto live = [&](int k) { return k < chunks && ((k >> 2) / nb) % g.T < rows; };
+  const SmallDiv div_nb((uint32_t)nb), div_t((uint32_t)g.T);
+  // block m of the page: half m % nb of head row rest = m / nb, which is slot rest % T of
+  // K/V head row hk = rest / T
+  auto slot_of_block = [&](int m) {
+    const int rest = (int)div_nb((uint32_t)m);
+    return rest - (int)div_t((uint32_t)rest) * g.T;
+  };
+  auto live = [&](int k) { return k < chunks && slot_of_block(k >> 2) < rows; };
   // Classify chunks k0 + 256 u (u < kEncUnroll): loads first, then per chunk its 16 exponents,
   // the block's window over its 4 lanes (uniform over them), the planes and the row flag bit.
   // hio[u]: the chunk's spill nibbles (raw blocks); the return value: which chunks are raw.
@@ -194,14 +211,12 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
       const Window c = window8(w1);
       a.emin = min(a.emin, c.emin);
       a.emax = max(a.emax, c.emax);
-      a.special |= c.special;
 #pragma unroll
       for (int o = 1; o < 4; o <<= 1) {
         a.emin = min(a.emin, (uint32_t)__shfl_xor((int)a.emin, o, 4));
         a.emax = max(a.emax, (uint32_t)__shfl_xor((int)a.emax, o, 4));
-        a.special |= (uint32_t)__shfl_xor((int)a.special, o, 4);
       }
-      const uint32_t raw_blk = a.special | (uint32_t)(a.emax - a.emin > 15u);
+      const uint32_t raw_blk = is_raw(a);
       const uint32_t bexp = raw_blk ? 0u : a.emin;
       uint32_t sm0[2], sm1[2], n0, n1;
       pack8(w0, bexp, raw_blk, sm0, n0, hio[u].x);
@@ -212,7 +227,8 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
       raw_mask |= raw_blk << u;
       if (qtr == 0) {
         base[v0 / kBlock] = (uint8_t)bexp;
-        const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+        const int rest = (int)div_nb((uint32_t)m), half = m - rest * nb;
+        const int hk = (int)div_t((uint32_t)rest), slot = rest - hk * g.T;
         if (raw_blk) atomicOr(&s_flags[slot], 1u << (hk * nb + half));
         if (!(hk & 1)) atomicMax(&s_kmax[hk >> 1], a.emax);
       }
@@ -264,7 +280,8 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
   // spill slots: 8 bytes per chunk of a raw block
   const uint64_t top = *spill_top;
   auto slot_of = [&](int m) -> uint64_t {
-    const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+    const int rest = (int)div_nb((uint32_t)m), half = m - rest * nb;
+    const int hk = (int)div_t((uint32_t)rest), slot = rest - hk * g.T;
     const int j = hk * nb + half;
     return top + s_first[slot] + __popc(s_flags[slot] & ((1u << j) - 1u));
   };
@@ -277,7 +294,8 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
       *reinterpret_cast<uint2*>(spill + idx * 32u + (k & 3) * 8) = s_hik[i][tid];
   }
   for (int k = tid + 256 * kEncSweeps; k < chunks; k += 256) {  // larger pages
-    const int m = k >> 2, half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+    const int m = k >> 2, rest = (int)div_nb((uint32_t)m), half = m - rest * nb;
+    const int hk = (int)div_t((uint32_t)rest), slot = rest - hk * g.T;
     if (slot >= rows || !((s_flags[slot] >> (hk * nb + half)) & 1u)) continue;
     const uint64_t idx = slot_of(m);
     if (idx >= spill_slots) continue;
@@ -521,11 +539,10 @@ __device__ __forceinline__ NewBlock classify_loaded(const uint4 in) {
   for (int o = 1; o < 8; o <<= 1) {
     win.emin = min(win.emin, (uint32_t)__shfl_xor((int)win.emin, o, 8));
     win.emax = max(win.emax, (uint32_t)__shfl_xor((int)win.emax, o, 8));
-    win.special |= (uint32_t)__shfl_xor((int)win.special, o, 8);
   }
   NewBlock o;
   o.emax = win.emax;
-  o.raw = win.special | (uint32_t)(win.emax - win.emin > 15u);
+  o.raw = is_raw(win);
   o.bexp = o.raw ? 0u : win.emin;
   uint32_t smw[2];
   pack8(w, o.bexp, o.raw, smw, o.nib, o.hi);
@@ -622,14 +639,12 @@ __global__ __launch_bounds__(256) void append_pack_k(Geom g, SeqView s, int n, c
     const Window wb = window8(w1);
     wa.emin = min(wa.emin, wb.emin);
     wa.emax = max(wa.emax, wb.emax);
-    wa.special |= wb.special;
 #pragma unroll
     for (int o = 1; o < 4; o <<= 1) {
       wa.emin = min(wa.emin, (uint32_t)__shfl_xor((int)wa.emin, o, 4));
       wa.emax = max(wa.emax, (uint32_t)__shfl_xor((int)wa.emax, o, 4));
-      wa.special |= (uint32_t)__shfl_xor((int)wa.special, o, 4);
     }
-    const uint32_t raw = wa.special | (uint32_t)(wa.emax - wa.emin > 15u);
+    const uint32_t raw = is_raw(wa);
     if (qtr == 0 && !kv && s.kmax) atomicMax(&s.kmax[kmax_at(s, g.H, (r0 + 2 * p + second) / n, h, a.lp)], wa.emax);
     bexp[p] = raw ? 0u : wa.emin;
     uint32_t s0[2], s1[2], hio;

@@ -31,40 +31,81 @@ __device__ __forceinline__ uint32_t exp_of(uint32_t h) { return (h >> 7) & 0xFFu
 
 // Per-lane partial window of 8 values held as 4 u32 words (two bf16 each).
 struct Window {
-  uint32_t emin, emax, special;
+  uint32_t emin, emax;
 };
 
+// Two 16-bit lanes at once (v_pk_min_u16, v_pk_max_u16).
+typedef unsigned short zf_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(zf_u16x2, a),
+                                                                __builtin_bit_cast(zf_u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(zf_u16x2, a),
+                                                                __builtin_bit_cast(zf_u16x2, b)));
+}
+
+// The exponent fields of the two values of a word, value 2k's in bits 0..7, value 2k + 1's in
+// bits 16..23.
+__device__ __forceinline__ uint32_t exp_pair(uint32_t w) { return (w >> 7) & 0x00FF00FFu; }
+
+// Both values of a word at once: the minimum and maximum exponent fields of the two 16-bit
+// halves, folded at the end.
 __device__ __forceinline__ Window window8(const uint32_t w[4]) {
-  Window r{255u, 0u, 0u};
+  uint32_t mn = 0x00FF00FFu, mx = 0u;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint32_t e = exp_of(w[k] >> (16 * s));
-      r.emin = min(r.emin, e);
-      r.emax = max(r.emax, e);
-      r.special |= (e == 0u) | (e == 255u);
-    }
+    const uint32_t e = exp_pair(w[k]);
+    mn = pk_min_u16(mn, e);
+    mx = pk_max_u16(mx, e);
   }
+  Window r;
+  r.emin = min(mn & 0xFFFFu, mn >> 16);
+  r.emax = max(mx & 0xFFFFu, mx >> 16);
   return r;
 }
 
+// The raw rule over a block's whole window: a value is special (zero or subnormal: field 0; Inf
+// or NaN: field 255) exactly when the window reaches 0 or 255, so that needs no test per value.
+__device__ __forceinline__ uint32_t is_raw(const Window& w) {
+  return (uint32_t)(w.emin == 0u) | (uint32_t)(w.emax == 255u) | (uint32_t)(w.emax - w.emin > 15u);
+}
+
+// Four words of two 4-bit fields each (bits 0..3 and 16..19: values 2k and 2k + 1) gathered into
+// one word, value v at bits 4v.
+__device__ __forceinline__ uint32_t gather_nibbles(const uint32_t n[4]) {
+  uint32_t y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) y[k] = n[k] | (n[k] >> 12);  // byte 0: value 2k, value 2k + 1 << 4
+  const uint32_t y01 = __builtin_amdgcn_perm(y[1], y[0], 0x0C0C0400u);  // bytes y0.0, y1.0
+  const uint32_t y23 = __builtin_amdgcn_perm(y[3], y[2], 0x04000C0Cu);  // bytes y2.0, y3.0 above
+  return y01 | y23;
+}
+
 // Packs 8 values (4 words, value 2k in the low half of w[k]) into 8 sm bytes (two words)
-// and 8 nibbles (one word, value k at bits 4k).  `base` = 0 for raw blocks.
+// and 8 nibbles (one word, value k at bits 4k); `hi` gets every value's exponent >> 4 the same
+// way (the spill nibbles, used for raw blocks).  `base` = 0 for raw blocks, whose nibbles are
+// then the exponent's low 4 bits; a compressed block's offsets e - base lie in [0, 15], so one
+// subtraction per word serves both (the two halves never borrow from each other).
 __device__ __forceinline__ void pack8(const uint32_t w[4], uint32_t base, uint32_t raw,
                                       uint32_t sm[2], uint32_t& nib, uint32_t& hi) {
-  sm[0] = sm[1] = 0u;
-  nib = 0u;
-  hi = 0u;
+  const uint32_t b2 = (raw ? 0u : base) * 0x00010001u;
+  uint32_t n[4], h[4];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    uint32_t h = (w[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
-    uint32_t e = exp_of(h);
-    uint32_t smb = ((h >> 8) & 0x80u) | (h & 0x7Fu);
-    sm[v >> 2] |= smb << (8 * (v & 3));
-    uint32_t n = raw ? (e & 15u) : (e - base);
-    nib |= n << (4 * v);
-    hi |= (e >> 4) << (4 * v);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t e = exp_pair(w[k]);
+    n[k] = (e - b2) & 0x000F000Fu;
+    h[k] = (e >> 4) & 0x000F000Fu;
+  }
+  nib = gather_nibbles(n);
+  hi = gather_nibbles(h);
+  // sm byte of a value: its low byte (mantissa in bits 0..6) with bit 7 taken from its high
+  // byte (the sign)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t lo = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], 0x06040200u);  // low bytes
+    const uint32_t hb = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], 0x07050301u);  // high bytes
+    sm[j] = (lo & 0x7F7F7F7Fu) | (hb & 0x80808080u);
   }
 }
 
@@ -86,13 +127,6 @@ __device__ __forceinline__ uint32_t bitselect(uint32_t mask, uint32_t a, uint32_
   uint32_t r;
   asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
   return r;
-}
-
-// Two 16-bit lanes at once (v_pk_max_u16).
-typedef unsigned short zf_u16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(zf_u16x2, a),
-                                                                __builtin_bit_cast(zf_u16x2, b)));
 }
 
 __device__ __forceinline__ void rebuild8(uint32_t s0, uint32_t s1, uint32_t nib, uint32_t hi,
