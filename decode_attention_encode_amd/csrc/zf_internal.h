@@ -71,42 +71,37 @@ __device__ __forceinline__ uint32_t is_raw(const Window& w) {
   return (uint32_t)(w.emin == 0u) | (uint32_t)(w.emax == 255u) | (uint32_t)(w.emax - w.emin > 15u);
 }
 
-// Four words of two 4-bit fields each (bits 0..3 and 16..19: values 2k and 2k + 1) gathered into
-// one word, value v at bits 4v.
-__device__ __forceinline__ uint32_t gather_nibbles(const uint32_t n[4]) {
-  uint32_t y[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) y[k] = n[k] | (n[k] >> 12);  // byte 0: value 2k, value 2k + 1 << 4
-  const uint32_t y01 = __builtin_amdgcn_perm(y[1], y[0], 0x0C0C0400u);  // bytes y0.0, y1.0
-  const uint32_t y23 = __builtin_amdgcn_perm(y[3], y[2], 0x04000C0Cu);  // bytes y2.0, y3.0 above
-  return y01 | y23;
+// Two words of four 4-bit fields, one in the low bits of each byte (values 0..3 and 4..7),
+// gathered into one word, value v at bits 4v: byte 0 of x | x >> 4 holds values 0 and 1, byte 2
+// values 2 and 3.
+__device__ __forceinline__ uint32_t gather_nibbles(uint32_t lo4, uint32_t hi4) {
+  return __builtin_amdgcn_perm(hi4 | (hi4 >> 4), lo4 | (lo4 >> 4), 0x06040200u);
 }
 
 // Packs 8 values (4 words, value 2k in the low half of w[k]) into 8 sm bytes (two words)
 // and 8 nibbles (one word, value k at bits 4k); `hi` gets every value's exponent >> 4 the same
 // way (the spill nibbles, used for raw blocks).  `base` = 0 for raw blocks, whose nibbles are
-// then the exponent's low 4 bits; a compressed block's offsets e - base lie in [0, 15], so one
-// subtraction per word serves both (the two halves never borrow from each other).
+// then the exponent's low 4 bits.  Four values at a time, one byte each: the exponent fields
+// (bits 7..14 of a value) shifted down and gathered by a byte permute; a compressed block's
+// offsets e - base lie in [0, 15], so one subtraction per four values serves both (the bytes
+// never borrow from each other).
 __device__ __forceinline__ void pack8(const uint32_t w[4], uint32_t base, uint32_t raw,
                                       uint32_t sm[2], uint32_t& nib, uint32_t& hi) {
-  const uint32_t b2 = (raw ? 0u : base) * 0x00010001u;
-  uint32_t n[4], h[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t e = exp_pair(w[k]);
-    n[k] = (e - b2) & 0x000F000Fu;
-    h[k] = (e >> 4) & 0x000F000Fu;
-  }
-  nib = gather_nibbles(n);
-  hi = gather_nibbles(h);
-  // sm byte of a value: its low byte (mantissa in bits 0..6) with bit 7 taken from its high
-  // byte (the sign)
+  const uint32_t b4 = (raw ? 0u : base) * 0x01010101u;
+  uint32_t n[2], h[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    const uint32_t e = __builtin_amdgcn_perm(w[2 * j + 1] >> 7, w[2 * j] >> 7, 0x06040200u);  // 4 fields
+    n[j] = (e - b4) & 0x0F0F0F0Fu;
+    h[j] = (e >> 4) & 0x0F0F0F0Fu;
+    // sm byte of a value: its low byte (mantissa in bits 0..6) with bit 7 taken from its high
+    // byte (the sign)
     const uint32_t lo = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], 0x06040200u);  // low bytes
     const uint32_t hb = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], 0x07050301u);  // high bytes
     sm[j] = (lo & 0x7F7F7F7Fu) | (hb & 0x80808080u);
   }
+  nib = gather_nibbles(n[0], n[1]);
+  hi = gather_nibbles(h[0], h[1]);
 }
 
 // ---------------------------------------------------------------- rebuild (decode, attention)
