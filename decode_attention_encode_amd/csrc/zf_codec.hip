@@ -13,6 +13,8 @@
 // with Decoupled Look-back", NVIDIA technical report NVR-2016-002): each page publishes its
 // raw count, then takes its prefix from the pages before it, so a raw block's spill nibbles
 // are written from the registers that classified it and the raw input is read once.
+#include <type_traits>
+
 #include "zf_internal.h"
 
 namespace zf {
@@ -46,6 +48,27 @@ __device__ __forceinline__ int rows_in_page(const SeqView& s, const Geom& g, int
   if (L < 0 || (int64_t)L > (int64_t)s.maxp * g.T) return -1;
   int64_t r = (int64_t)L - (int64_t)p * g.T;
   return r <= 0 ? 0 : (r > g.T ? g.T : (int)r);
+}
+
+// Streaming accesses: the codec reads and writes every plane byte once per call, so its loads
+// and stores carry the non-temporal hint (lines are not kept for reuse).  Measured on gfx950, a
+// plain 16-byte copy with the hint on both sides moves ~6.3 TB/s read plus written, without it
+// ~5.4-5.9 TB/s.
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void* p) {
+  const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st_stream16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store((nt_u32x4){a, b, c, d}, reinterpret_cast<nt_u32x4*>(p));
+}
+__device__ __forceinline__ void st_stream8(void* p, uint32_t a, uint32_t b) {
+  __builtin_nontemporal_store((nt_u32x2){a, b}, reinterpret_cast<nt_u32x2*>(p));
 }
 
 // ------------------------------------------------------------------------------ encode
@@ -125,9 +148,11 @@ __device__ uint64_t look_back(const SeqView& s, const Geom& g, const uint64_t* l
 }
 
 // Encode of one (sequence, logical page): 4 lanes per 64-value block, 16 values each (two
-// 16-byte loads).  The first kEncSweeps sweeps of 256 chunks (a whole page of 512 blocks)
-// keep their raw blocks' spill nibbles in LDS until the page's slots are known; a larger
-// page's later sweeps read their raw blocks again for them.
+// 16-byte loads).  The first kEncSweeps sweeps of kEncThreads chunks (a whole page of 512
+// blocks) keep their raw blocks' spill nibbles in LDS until the page's slots are known; a
+// larger page's later sweeps read their raw blocks again for them.  (512 threads with 4 sweeps
+// measured 5 % slower than 256 with 8.)
+constexpr int kEncThreads = 256;
 constexpr int kEncSweeps = 8;
 constexpr int kEncUnroll = 2;
 // The encode is bound by how many loads are in flight, so by how many workgroups fit a CU: the
@@ -145,7 +170,7 @@ struct SmallDiv {
   __device__ uint32_t operator()(uint32_t x) const { return (uint32_t)((x * m) >> 32); }
 };
 
-__global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
+__global__ __launch_bounds__(kEncThreads, kEncWavesPerSimd) void enc_k(
     Geom g, SeqView s, const uint16_t* __restrict__ raw, uint8_t* __restrict__ sm, uint8_t* __restrict__ nib,
     uint8_t* __restrict__ base, uint32_t* __restrict__ row_flags, uint32_t* __restrict__ row_spill,
     uint8_t* __restrict__ spill, const uint64_t* spill_top, uint64_t spill_slots, uint64_t* look, uint32_t* failed,
@@ -185,24 +210,24 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
     return rest - (int)div_t((uint32_t)rest) * g.T;
   };
   auto live = [&](int k) { return k < chunks && slot_of_block(k >> 2) < rows; };
-  // Classify chunks k0 + 256 u (u < kEncUnroll): loads first, then per chunk its 16 exponents,
+  // Classify chunks k0 + kEncThreads u (u < kEncUnroll): loads first, then per chunk its 16 exponents,
   // the block's window over its 4 lanes (uniform over them), the planes and the row flag bit.
   // hio[u]: the chunk's spill nibbles (raw blocks); the return value: which chunks are raw.
   auto classify = [&](int k0, uint2 (&hio)[kEncUnroll]) -> uint32_t {
     uint4 lo[kEncUnroll], hi[kEncUnroll];
 #pragma unroll
     for (int u = 0; u < kEncUnroll; ++u) {
-      const int k = k0 + 256 * u;
+      const int k = k0 + kEncThreads * u;
       if (live(k)) {
         const uint4* src = reinterpret_cast<const uint4*>(raw + page0 + (int64_t)(k >> 2) * kBlock + (k & 3) * 16);
-        lo[u] = src[0];
-        hi[u] = src[1];
+        lo[u] = ld_stream16(src);
+        hi[u] = ld_stream16(src + 1);
       }
     }
     uint32_t raw_mask = 0u;
 #pragma unroll
     for (int u = 0; u < kEncUnroll; ++u) {
-      const int k = k0 + 256 * u, m = k >> 2, qtr = k & 3;
+      const int k = k0 + kEncThreads * u, m = k >> 2, qtr = k & 3;
       hio[u] = make_uint2(0u, 0u);
       if (!live(k)) continue;  // uniform over the 4 lanes of the block
       const uint32_t w0[4] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w};
@@ -222,8 +247,8 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
       pack8(w0, bexp, raw_blk, sm0, n0, hio[u].x);
       pack8(w1, bexp, raw_blk, sm1, n1, hio[u].y);
       const int64_t v0 = page0 + (int64_t)m * kBlock + qtr * 16;
-      *reinterpret_cast<uint4*>(sm + v0) = make_uint4(sm0[0], sm0[1], sm1[0], sm1[1]);
-      *reinterpret_cast<uint2*>(nib + (v0 >> 1)) = make_uint2(n0, n1);
+      st_stream16(sm + v0, sm0[0], sm0[1], sm1[0], sm1[1]);
+      st_stream8(nib + (v0 >> 1), n0, n1);
       raw_mask |= raw_blk << u;
       if (qtr == 0) {
         base[v0 / kBlock] = (uint8_t)bexp;
@@ -235,16 +260,16 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
     }
     return raw_mask;
   };
-  __shared__ uint2 s_hik[kEncSweeps][256];  // LDS, not registers: more workgroups per CU
+  __shared__ uint2 s_hik[kEncSweeps][kEncThreads];  // LDS, not registers: more workgroups per CU
   uint32_t rawm = 0u;
 #pragma unroll
   for (int gi = 0; gi < kEncSweeps / kEncUnroll; ++gi) {
     uint2 h[kEncUnroll];
-    rawm |= classify(tid + 256 * kEncUnroll * gi, h) << (kEncUnroll * gi);
+    rawm |= classify(tid + kEncThreads * kEncUnroll * gi, h) << (kEncUnroll * gi);
 #pragma unroll
     for (int u = 0; u < kEncUnroll; ++u) s_hik[kEncUnroll * gi + u][tid] = h[u];
   }
-  for (int k0 = tid + 256 * kEncSweeps; k0 < chunks; k0 += 256 * kEncUnroll) {  // larger pages
+  for (int k0 = tid + kEncThreads * kEncSweeps; k0 < chunks; k0 += kEncThreads * kEncUnroll) {  // larger pages
     uint2 h[kEncUnroll];
     classify(k0, h);
   }
@@ -288,12 +313,12 @@ __global__ __launch_bounds__(256, kEncWavesPerSimd) void enc_k(
 #pragma unroll
   for (int i = 0; i < kEncSweeps; ++i) {
     if (!((rawm >> i) & 1u)) continue;
-    const int k = tid + 256 * i;
+    const int k = tid + kEncThreads * i;
     const uint64_t idx = slot_of(k >> 2);
     if (idx < spill_slots)  // a pool too small for the call: slots past its end are skipped
       *reinterpret_cast<uint2*>(spill + idx * 32u + (k & 3) * 8) = s_hik[i][tid];
   }
-  for (int k = tid + 256 * kEncSweeps; k < chunks; k += 256) {  // larger pages
+  for (int k = tid + kEncThreads * kEncSweeps; k < chunks; k += kEncThreads) {  // larger pages
     const int m = k >> 2, rest = (int)div_nb((uint32_t)m), half = m - rest * nb;
     const int hk = (int)div_t((uint32_t)rest), slot = rest - hk * g.T;
     if (slot >= rows || !((s_flags[slot] >> (hk * nb + half)) & 1u)) continue;
@@ -1107,14 +1132,19 @@ __global__ __launch_bounds__(256) void append_one_k(Geom g, SeqView s, int n, co
 
 // ------------------------------------------------------------------------------ decode
 
-// One workgroup per (sequence, logical page).  The page's row flags, spill indices and block
-// bases are staged in LDS first; then each lane rebuilds 16 values (a quarter of a block) per
-// step from one 16-byte sm load, one 8-byte nibble load and, for a raw block, one 8-byte spill
-// load, and writes 32 bytes.  Four steps per lane are unrolled so their loads fly together.
+// One workgroup per (sequence, logical page).  Each lane rebuilds 16 values (a quarter of a
+// block) per step from one 16-byte sm load, one 8-byte nibble load and, for a raw block, one
+// 8-byte spill load, and writes 32 bytes; four steps per lane are unrolled so their loads fly
+// together, and 512 lanes cover a 16-token, 8-head page in one such round, so no lane waits
+// for its own stores before loading again (256 lanes in two rounds measured 10 % slower).  The
+// page's row flags, spill indices and block bases go to LDS first, and the planes of the
+// lane's first round, which need none of them, are loaded beside them: the page costs two
+// round trips (metadata and planes, then spill bytes) before its values are written.
 constexpr int kDecUnroll = 4;
+constexpr int kDecThreads = 512;  // with 4 steps per lane, one round covers a 16 x 8 x 128 page
 constexpr int kMaxPageBlocks = 32 * 64;  // 32 blocks per row, 64 rows per page at most
 
-__global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t* __restrict__ sm,
+__global__ __launch_bounds__(kDecThreads) void decode_k(Geom g, SeqView s, const uint8_t* __restrict__ sm,
                                                 const uint8_t* __restrict__ nib, const uint8_t* __restrict__ base,
                                                 const uint32_t* __restrict__ row_flags,
                                                 const uint32_t* __restrict__ row_spill,
@@ -1135,59 +1165,102 @@ __global__ __launch_bounds__(256) void decode_k(Geom g, SeqView s, const uint8_t
   }
   const int nb = g.nb();
   const int blocks = 2 * g.H * g.T * nb;
-  __shared__ uint32_t s_f[64], s_sp[64];
-  __shared__ uint8_t s_base[kMaxPageBlocks];
-  if (tid < rows) {
-    s_f[tid] = row_flags[(int64_t)pid * g.T + tid];
-    s_sp[tid] = row_spill[(int64_t)pid * g.T + tid];
-  }
-  const uint8_t* bsrc = base + (int64_t)pid * blocks;
-  for (int m = tid; m < blocks; m += 256) s_base[m] = bsrc[m];
-  __syncthreads();
   const int64_t page0 = (int64_t)pid * g.vals_per_page();
   const int chunks = blocks * 4;  // 16 values each
-  uint32_t err = 0;
-  for (int k0 = tid; k0 < chunks; k0 += 256 * kDecUnroll) {
-    uint4 smw[kDecUnroll];
-    uint2 nibw[kDecUnroll], hiw[kDecUnroll];
-    uint32_t bp[kDecUnroll];
-    bool live[kDecUnroll];
+  // chunk k: quarter k & 3 of block m = k >> 2, which is half m % nb of head row m / nb, slot
+  // (m / nb) % T of it
+  const SmallDiv div_nb((uint32_t)nb), div_t((uint32_t)g.T);
+  auto slot_of_block = [&](int m) {
+    const int rest = (int)div_nb((uint32_t)m);
+    return rest - (int)div_t((uint32_t)rest) * g.T;
+  };
+  // A full page whose chunks fill whole rounds (every page but a sequence's last, at the usual
+  // geometries) runs without any per-chunk test: with no load or store under a branch, the
+  // compiler's waits count exactly the accesses they need and never wait for stores.
+  const bool full = rows == g.T && chunks % (kDecThreads * kDecUnroll) == 0;
+  auto live_at = [&](int k, auto whole) {
+    if constexpr (decltype(whole)::value) return true;
+    else return k < chunks && slot_of_block(k >> 2) < rows;
+  };
+  // Loads without branches (a chunk outside the page's rows reads chunk 0 instead and drops
+  // it), so that the waits for the metadata below count exactly the loads issued after it.
+  auto load_planes = [&](int k0, uint4 (&smw)[kDecUnroll], uint2 (&nibw)[kDecUnroll], auto whole) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      const int k = k0 + 256 * u, m = k >> 2, qtr = k & 3;
-      live[u] = k < chunks && (m / nb) % g.T < rows;
-      hiw[u] = make_uint2(0u, 0u);
-      bp[u] = 0u;
-      if (live[u]) {
-        const int64_t v0 = page0 + (int64_t)m * kBlock + qtr * 16;
-        smw[u] = *reinterpret_cast<const uint4*>(sm + v0);
-        nibw[u] = *reinterpret_cast<const uint2*>(nib + (v0 >> 1));
-        const int half = m % nb, rest = m / nb, slot = rest % g.T, hk = rest / g.T;
+      const int k = live_at(k0 + kDecThreads * u, whole) ? k0 + kDecThreads * u : 0;
+      const int64_t v0 = page0 + (int64_t)(k >> 2) * kBlock + (k & 3) * 16;
+      smw[u] = ld_stream16(sm + v0);
+      nibw[u] = ld_stream8(nib + (v0 >> 1));
+    }
+  };
+  __shared__ uint32_t s_f[64], s_sp[64];
+  __shared__ __align__(4) uint8_t s_base[kMaxPageBlocks];
+  const bool word_bases = (blocks & 3) == 0;  // the page's bases as 4-byte words
+  const int64_t row0 = (int64_t)pid * g.T + min(tid, rows - 1);
+  const uint32_t f_in = row_flags[row0], sp_in = row_spill[row0];
+  const uint8_t* bsrc = base + (int64_t)pid * blocks;
+  const uint32_t b_in = *(word_bases ? reinterpret_cast<const uint32_t*>(bsrc) + min(tid, blocks / 4 - 1) : &row_flags[row0]);
+  uint4 smw[kDecUnroll];
+  uint2 nibw[kDecUnroll];
+  if (full) load_planes(tid, smw, nibw, std::true_type{});
+  else load_planes(tid, smw, nibw, std::false_type{});
+  if (tid < rows) {
+    s_f[tid] = f_in;
+    s_sp[tid] = sp_in;
+  }
+  if (word_bases) {
+    uint32_t* s_bw = reinterpret_cast<uint32_t*>(s_base);
+    if (tid < blocks / 4) s_bw[tid] = b_in;
+    for (int m = tid + kDecThreads; m < blocks / 4; m += kDecThreads) s_bw[m] = reinterpret_cast<const uint32_t*>(bsrc)[m];
+  } else {
+    for (int m = tid; m < blocks; m += kDecThreads) s_base[m] = bsrc[m];
+  }
+  __syncthreads();
+  uint32_t err = 0;
+  auto rounds = [&](auto whole) {
+    for (int k0 = tid; k0 < chunks; k0 += kDecThreads * kDecUnroll) {
+      if (k0 != tid) load_planes(k0, smw, nibw, whole);
+      // spill loads without branches as well (a block that is not raw reads the page's first sm
+      // bytes and drops them), so the four go out together and are waited for once
+      uint2 hiw[kDecUnroll];
+      uint32_t bp[kDecUnroll];
+      bool spilled[kDecUnroll];
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) {
+        const int k = k0 + kDecThreads * u;
+        const bool live = live_at(k, whole);
+        const int m = live ? k >> 2 : 0, qtr = k & 3;
+        const int rest = (int)div_nb((uint32_t)m), half = m - rest * nb;
+        const int hk = (int)div_t((uint32_t)rest), slot = rest - hk * g.T;
         const int j = hk * nb + half;
         const uint32_t f = s_f[slot];
-        if ((f >> j) & 1u) {
-          const uint64_t idx = (uint64_t)s_sp[slot] + __popc(f & ((1u << j) - 1u));
-          if (idx < spill_slots) hiw[u] = *reinterpret_cast<const uint2*>(spill + idx * 32u + qtr * 8);
-          else err = ZF_DEV_ESPILL;
-        } else {
-          bp[u] = (uint32_t)s_base[m] * 0x00010001u;
-        }
+        const bool raw = live && ((f >> j) & 1u);
+        const uint64_t idx = (uint64_t)s_sp[slot] + __popc(f & ((1u << j) - 1u));
+        spilled[u] = raw && idx < spill_slots;
+        if (raw && !spilled[u]) err = ZF_DEV_ESPILL;
+        hiw[u] = *reinterpret_cast<const uint2*>(spilled[u] ? spill + idx * 32u + qtr * 8 : sm + page0);
+        bp[u] = raw ? 0u : (uint32_t)s_base[m] * 0x00010001u;
+      }
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u)
+        if (!spilled[u]) hiw[u] = make_uint2(0u, 0u);
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) {
+        const int k = k0 + kDecThreads * u, m = k >> 2, qtr = k & 3;
+        if (!live_at(k, whole)) continue;
+        uint32_t pr[4], w0[4], w1[4];
+        rebuild8(smw[u].x, smw[u].y, nibw[u].x, hiw[u].x, bp[u], pr);
+        pairs_to_natural(pr, w0);
+        rebuild8(smw[u].z, smw[u].w, nibw[u].y, hiw[u].y, bp[u], pr);
+        pairs_to_natural(pr, w1);
+        uint16_t* dst = out + page0 + (int64_t)m * kBlock + qtr * 16;
+        st_stream16(dst, w0[0], w0[1], w0[2], w0[3]);
+        st_stream16(dst + 8, w1[0], w1[1], w1[2], w1[3]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      if (!live[u]) continue;
-      const int k = k0 + 256 * u, m = k >> 2, qtr = k & 3;
-      uint32_t pr[4], w0[4], w1[4];
-      rebuild8(smw[u].x, smw[u].y, nibw[u].x, hiw[u].x, bp[u], pr);
-      pairs_to_natural(pr, w0);
-      rebuild8(smw[u].z, smw[u].w, nibw[u].y, hiw[u].y, bp[u], pr);
-      pairs_to_natural(pr, w1);
-      uint4* dst = reinterpret_cast<uint4*>(out + page0 + (int64_t)m * kBlock + qtr * 16);
-      dst[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-      dst[1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-    }
-  }
+  };
+  if (full) rounds(std::true_type{});
+  else rounds(std::false_type{});
   if (err) set_status(status, err);
 }
 
@@ -1318,7 +1391,7 @@ hipError_t launch_encode(const Geom& g, const zf_cache* c, const zf_seqs* q, con
   uint64_t* look = reinterpret_cast<uint64_t*>(ws + 64);       // one word per (sequence, page)
   hipError_t e = launch_fill_zero(ws, encode_workspace_bytes(q), st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(enc_k, dim3(q->max_pages_per_seq, q->batch), dim3(256), 0, st, g, s, raw, c->sm,
+  hipLaunchKernelGGL(enc_k, dim3(q->max_pages_per_seq, q->batch), dim3(kEncThreads), 0, st, g, s, raw, c->sm,
                      c->nib, c->base, c->row_flags, c->row_spill, c->spill, c->spill_top, c->spill_slots,
                      look, failed, c->status);
   hipLaunchKernelGGL(enc_finish_k, dim3(1), dim3(64), 0, st, g, s, look, failed, c->spill_top,
@@ -1408,7 +1481,7 @@ hipError_t launch_decode(const Geom& g, const zf_cache* c, const zf_seqs* q, uin
                          hipStream_t st) {
   SeqView s = view(q);
   dim3 grid(q->max_pages_per_seq, q->batch);
-  hipLaunchKernelGGL(decode_k, grid, dim3(256), 0, st, g, s, c->sm, c->nib, c->base, c->row_flags,
+  hipLaunchKernelGGL(decode_k, grid, dim3(kDecThreads), 0, st, g, s, c->sm, c->nib, c->base, c->row_flags,
                      c->row_spill, c->spill, c->spill_slots, out, c->status);
   return hipGetLastError();
 }
