@@ -29,8 +29,9 @@ EXPORTS = ("zf_cache_bytes", "zf_encode_kv", "zf_encode_workspace_bytes", "zf_ap
            "zf_decode_kv", "zf_decode_attention", "zf_decode_attention_noalloc",
            "zf_decode_attention_raw",
            "zf_attention_workspace_bytes", "zf_attention_workspace_init", "zf_time_next_attention",
-           "zf_stream_read_probe", "zf_get_status", "zf_status_str")
+           "zf_stream_read_probe", "zf_stream_copy_probe", "zf_get_status", "zf_status_str")
 ZF_PROBE_BLOCKS = 4096
+ZF_COPY_PROBE_BLOCKS = 32768
 
 
 class ZfError(RuntimeError):
@@ -88,6 +89,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "zf_attention_workspace_init": (ctypes.c_int, [vp, sz, vp]),
         "zf_time_next_attention": (ctypes.c_int, [vp, vp]),
         "zf_stream_read_probe": (ctypes.c_int, [vp, sz, vp, vp]),
+        "zf_stream_copy_probe": (ctypes.c_int, [vp, vp, sz, vp]),
         "zf_get_status": (ctypes.c_int, [vp, vp, vp]),
         "zf_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -280,6 +282,14 @@ def zf_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> 
     ZF_PROBE_BLOCKS u32 checksums afterwards."""
     _check(load().zf_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                        _stream(stream)), "zf_stream_read_probe")
+
+
+def zf_stream_copy_probe(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Copies all of `src` into `dst` (same byte size) with the library's plain streaming copy."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ZfError(ZF_EINVAL, "zf_stream_copy_probe: src and dst differ in size")
+    _check(load().zf_stream_copy_probe(_ptr(src), _ptr(dst), n, _stream(stream)), "zf_stream_copy_probe")
 
 
 def zf_get_status(status: torch.Tensor, stream=None) -> int:

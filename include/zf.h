@@ -291,6 +291,15 @@ zf_status zf_time_next_attention(void* start_event, void* stop_event);
 #define ZF_PROBE_BLOCKS 4096
 zf_status zf_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, zf_stream_t stream);
 
+/* Measurement aid, outside the method: copies `bytes` of device memory from `src` to `dst`
+ * once, with 16-byte non-temporal loads and stores over up to ZF_COPY_PROBE_BLOCKS
+ * workgroups (a plain stream: the practically achievable HBM read-plus-write rate, context for
+ * the codec kernels', which read one cache form and write the other).  Both 16-byte aligned,
+ * bytes > 0 and a multiple of 16, the two ranges disjoint, else ZF_EINVAL.  Caller-owned
+ * memory; one kernel launch on `stream`. */
+#define ZF_COPY_PROBE_BLOCKS 32768
+zf_status zf_stream_copy_probe(const void* src, void* dst, size_t bytes, zf_stream_t stream);
+
 /* Status, outside the method: copies the sticky status word to *host_status (synchronizes
  * `stream`); a cache's word or the twin's. */
 zf_status zf_get_status(const uint32_t* status, uint32_t* host_status, zf_stream_t stream);

@@ -239,10 +239,22 @@ def test_attention_rejects_spill_pool_beyond_32bit_offsets():
                                    4096, 4096, 0, None) == zf.ZF_EWORKSPACE
 
 
+def test_stream_copy_probe_arguments():
+    lib = zf.load()
+    assert lib.zf_stream_copy_probe(None, 8192, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_copy_probe(4096, None, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_copy_probe(4096, 8192, 0, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_copy_probe(4096, 8192, 4100, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_copy_probe(4104, 8192, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_copy_probe(4096, 8200, 4096, None) == zf.ZF_EINVAL
+    assert lib.zf_stream_copy_probe(4096, 6144, 4096, None) == zf.ZF_EINVAL  # overlap
+
+
 def test_header_constants_match_the_binding():
     """The device status bits and the size of the append sync area are the header's."""
     text = open(HEADER).read()
     defs = {k: int(v.rstrip("u")) for k, v in re.findall(r"#define\s+(ZF_\w+)\s+(\d+u?)", text)}
-    for name in ("ZF_DEV_ESPILL", "ZF_DEV_EPAGE", "ZF_DEV_ELEN", "ZF_DEV_ESYNC", "ZF_APPEND_SYNC_WORDS"):
+    for name in ("ZF_DEV_ESPILL", "ZF_DEV_EPAGE", "ZF_DEV_ELEN", "ZF_DEV_ESYNC", "ZF_APPEND_SYNC_WORDS",
+                 "ZF_PROBE_BLOCKS", "ZF_COPY_PROBE_BLOCKS"):
         assert defs[name] == getattr(zf, name), name
 

@@ -1,5 +1,7 @@
-"""GPU check of the streaming-read probe (zf_stream_read_probe): every workgroup's checksum
-equals the XOR of the words of its share of the buffer, so every byte was read once."""
+"""GPU checks of the measurement probes: the streaming read (zf_stream_read_probe), whose
+every workgroup's checksum equals the XOR of the words of its share of the buffer, so every
+byte was read once; and the streaming copy (zf_stream_copy_probe), whose destination equals its
+source and whose bytes around the destination stay untouched."""
 import numpy as np
 import pytest
 import torch
@@ -28,3 +30,15 @@ def test_stream_read_probe_reads_everything(n16):
         want = np.bitwise_xor.reduce(chunk.reshape(-1)) if chunk.size else np.uint32(0)
         assert got[b] == want, f"block {b}"
     assert (got[blocks:] == 0xFFFFFFFF).all()  # blocks past the grid untouched
+
+
+@pytest.mark.parametrize("n16", [1, 1023, 1024 * 32768 + 7])
+def test_stream_copy_probe_copies_everything(n16):
+    log(f"stream copy probe: {n16 * 16} bytes")
+    g = torch.Generator(device="cuda").manual_seed(n16)
+    src = torch.randint(-2**31, 2**31 - 1, (n16 * 4,), dtype=torch.int32, device="cuda", generator=g)
+    dst = torch.full((n16 * 4 + 8,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    zf.zf_stream_copy_probe(src, dst[4:4 + n16 * 4])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[4:4 + n16 * 4], src)
+    assert (dst[:4] == 0x5A5A5A5A).all() and (dst[-4:] == 0x5A5A5A5A).all()
