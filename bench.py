@@ -334,12 +334,54 @@ def extras(torch, zf, inst, layers, raw, q, ws, out, scale, attn_bytes, row_byte
         d = torch.zeros_like(raw)
         zf.zf_decode_kv(cache, seqs, d)
         twins.append(d)
-    t_pack = timeit(lambda i: zf.zf_decode_attention(layers[i % NL][0], layers[i % NL][1], q, scale, out, ws))
-    t_twin = timeit(lambda i: zf.zf_decode_attention_raw(twins[i % NL], layers[i % NL][1], q, scale, out, ws, status))
+    def timeit_pair(fa, fb, n=30, warm=20):
+        """fa and fb alternately (a, b, a, b, ...) after `warm` untimed rounds, so that both see
+        the same clock and cache state; the mean of each."""
+        for i in range(warm):
+            fa(i)
+            fb(i)
+        torch.cuda.synchronize()
+        ta, tb = [], []
+        for i in range(n):
+            for f, acc in ((fa, ta), (fb, tb)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                f(i)
+                b.record(stream)
+                acc.append((a, b))
+        torch.cuda.synchronize()
+        mean = lambda ev: float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+        return mean(ta), mean(tb)
+
+    t_pack, t_twin = timeit_pair(
+        lambda i: zf.zf_decode_attention(layers[i % NL][0], layers[i % NL][1], q, scale, out, ws),
+        lambda i: zf.zf_decode_attention_raw(twins[i % NL], layers[i % NL][1], q, scale, out, ws, status))
     t_warm = timeit(lambda i: zf.zf_decode_attention(layers[0][0], layers[0][1], q, scale, out, ws))
     res["attention_packed_us"] = round(t_pack * 1e6, 2)
     res["attention_twin_uncompressed_us"] = round(t_twin * 1e6, 2)
     res["speedup_vs_uncompressed_twin"] = round(t_twin / t_pack, 3)
+
+    # the same pair by the kernels' own start and end stamps (no dispatch overhead), alternating
+    def stamped_pair(fa, fb, n=30):
+        ev = []
+        for i in range(n):
+            for f in (fa, fb):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)  # the events exist on the device before the library stamps them
+                b.record(stream)
+                zf.zf_time_next_attention(a, b)
+                f(i)
+                ev.append((a, b))
+        torch.cuda.synchronize()
+        d = [a.elapsed_time(b) / 1e3 for a, b in ev]
+        return float(np.mean(d[0::2])), float(np.mean(d[1::2]))
+
+    k_pack, k_twin = stamped_pair(
+        lambda i: zf.zf_decode_attention(layers[i % NL][0], layers[i % NL][1], q, scale, out, ws),
+        lambda i: zf.zf_decode_attention_raw(twins[i % NL], layers[i % NL][1], q, scale, out, ws, status))
+    res["attention_packed_kernel_us"] = round(k_pack * 1e6, 2)
+    res["attention_twin_kernel_us"] = round(k_twin * 1e6, 2)
+    res["kernel_speedup_vs_uncompressed_twin"] = round(k_twin / k_pack, 3)
     # the unfused alternative: decode the layer's cache to bf16 pages, then the raw kernel
     scratch = torch.empty_like(raw)
 
