@@ -566,8 +566,9 @@ def per_config(torch, zf, synth, key, dev):
         zf.zf_decode_kv(cache, seqs, d)
         twins.append(d)
     del raw
-    tcall, _ = run(lambda i: zf.zf_decode_attention_raw(twins[i % 2], layers[i % 2][1], q, scale, out, ws,
-                                                        status), False)
+    twin = lambda i: zf.zf_decode_attention_raw(twins[i % 2], layers[i % 2][1], q, scale, out, ws, status)
+    tcall, _ = run(twin, False)
+    _, tkern = run(twin, True)
     for cache, _ in layers:
         assert zf.zf_get_status(cache.status) == 0
     # sampled parity against the oracle: 16 (sequence, q head) rows, with their effective token
@@ -596,6 +597,8 @@ def per_config(torch, zf, synth, key, dev):
             "tokens_per_s": round(w.batch / call.mean() * 1e6, 1),
             "twin_call_us_mean": round(float(tcall.mean()), 2),
             "speedup_vs_twin": round(float(tcall.mean() / call.mean()), 3),
+            "twin_kernel_us_mean": round(float(tkern.mean()), 2),
+            "kernel_speedup_vs_twin": round(float(tkern.mean() / kern.mean()), 3),
             "compression_ratio": round((rows * 3112 + 32 * top) / (rows * H * 2 * D * 2), 4),
             "raw_block_fraction": round(top / blocks, 4),
             "raw_blocks_by_cause": raw_causes(inst, rng),
